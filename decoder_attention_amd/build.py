@@ -1,0 +1,92 @@
+"""Build the HIP library libgemma_attn.so in-tree (gfx950).
+
+    python -m decoder_attention_amd.build          # compile every source, link
+    python -m decoder_attention_amd.build --host   # also build the host-logic test binary (g++)
+
+Objects go to decoder_attention_amd/_build/; the shared library is written next
+to this file.  Every call recompiles.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libgemma_attn.so")
+
+HIP_SOURCES = ["prologue.hip", "prefill.hip", "decode.hip", "gemma_attn_api.hip"]
+CXX_SOURCES = ["host_logic.cpp"]
+ARCH = "gfx950"
+
+
+def _hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def _flags() -> list[str]:
+    return [
+        "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+        # packed fp32 arithmetic stays off for every kernel of this library
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, "-I", CSRC,
+    ]
+
+
+def _run(cmd: list[str]) -> None:
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(line for line in r.stderr.splitlines() if "packed-fp32-ops" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    if err.strip():
+        print(err, file=sys.stderr)
+
+
+def build(jobs: int | None = None) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    hipcc = _hipcc()
+    cmds, objs = [], []
+    for src in HIP_SOURCES + CXX_SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        lang = [] if src.endswith(".hip") else ["-x", "c++"]
+        cmds.append([hipcc, *_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(jobs or min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(_run, cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def build_host_test() -> str:
+    """g++ build of the host logic alone (no HIP), for CPU tests."""
+    os.makedirs(BUILD, exist_ok=True)
+    out = os.path.join(BUILD, "libgemma_attn_host.so")
+    _run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-I", INCLUDE, "-I", CSRC,
+          os.path.join(CSRC, "host_logic.cpp"), os.path.join(CSRC, "host_logic_capi.cpp"), "-o", out])
+    return out
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--host", action="store_true")
+    ap.add_argument("-j", type=int, default=None)
+    a = ap.parse_args()
+    print(build(a.j))
+    if a.host:
+        print(build_host_test())
+
+
+if __name__ == "__main__":
+    if shutil.which(_hipcc()) is None and not os.path.exists(_hipcc()):
+        sys.exit("hipcc not found")
+    main()

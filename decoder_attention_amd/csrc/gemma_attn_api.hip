@@ -1,0 +1,157 @@
+// C ABI entry points (include/gemma_attn.h): host-side checks, then launches.
+// Every check runs before the first HIP call, so an error return means nothing
+// was enqueued.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "gemma_attn.h"
+#include "ga_kernels.h"
+#include "host_logic.h"
+
+namespace {
+
+bool dev_ok(const void* p) { return p != nullptr && ga::aligned16(p); }
+
+int hip_rc(hipError_t e) {
+  if (e == hipSuccess) return GA_OK;
+  if (e == hipErrorInvalidValue) return GA_ERR_UNSUPPORTED;
+  return GA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemma_attn_resolve_layer(const gemma_attn_config* cfg, int32_t layer_idx, gemma_attn_layer* out) {
+  return ga::resolve_layer(cfg, layer_idx, out);
+}
+
+const char* gemma_attn_strerror(int code) {
+  switch (code) {
+    case GA_OK: return "ok";
+    case GA_ERR_INVALID_ARG: return "invalid argument";
+    case GA_ERR_UNSUPPORTED: return "unsupported head width or group size";
+    case GA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case GA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown error";
+  }
+}
+
+int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
+                      const void* q_in, const void* k_in, void* q_out, void* k_out,
+                      const float* q_norm_w, const float* k_norm_w, const int32_t* pos0, void* stream) {
+  gemma_attn_layer L;
+  const int rc = ga::resolve_layer(cfg, layer_idx, &L);
+  if (rc != GA_OK) return rc;
+  if (batch < 0 || seq < 0) return GA_ERR_INVALID_ARG;
+  if (static_cast<long long>(batch) * seq > INT_MAX) return GA_ERR_UNSUPPORTED;
+  if (!ga::prologue_dim_supported(L.head_dim)) return GA_ERR_UNSUPPORTED;
+  if (batch == 0 || seq == 0) return GA_OK;
+  if (!dev_ok(q_in) || !dev_ok(q_out)) return GA_ERR_INVALID_ARG;
+  if (k_in && !dev_ok(k_out)) return GA_ERR_INVALID_ARG;
+  if (k_in && !ga::aligned16(k_in)) return GA_ERR_INVALID_ARG;
+  if ((q_norm_w && !ga::aligned16(q_norm_w)) || (k_norm_w && !ga::aligned16(k_norm_w))) return GA_ERR_INVALID_ARG;
+  ga::PrologueArgs a;
+  a.batch = batch;
+  a.seq = seq;
+  a.hq = cfg->num_heads;
+  a.hkv = L.num_kv_heads;
+  a.dim = L.head_dim;
+  a.rotary_dim = L.rotary_dim;
+  a.q_in = q_in;
+  a.k_in = k_in;
+  a.q_out = q_out;
+  a.k_out = k_in ? k_out : nullptr;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.pos0 = pos0;
+  a.theta = L.theta;
+  a.eps = static_cast<float>(cfg->norm_eps);
+  a.offset = static_cast<float>(cfg->norm_weight_offset);
+  return hip_rc(ga::launch_qk_prologue(a, static_cast<hipStream_t>(stream)));
+}
+
+int gemma_attn_prefill(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
+                       const void* q, const void* k, const void* v, void* out, float* lse, void* stream) {
+  gemma_attn_layer L;
+  const int rc = ga::resolve_layer(cfg, layer_idx, &L);
+  if (rc != GA_OK) return rc;
+  if (batch < 0 || seq < 0) return GA_ERR_INVALID_ARG;
+  if (!ga::attn_dim_supported(L.head_dim) || !ga::attn_group_supported(L.group)) return GA_ERR_UNSUPPORTED;
+  if (batch > 65535 || L.num_kv_heads > 65535) return GA_ERR_UNSUPPORTED;
+  if (batch == 0 || seq == 0) return GA_OK;
+  if (!dev_ok(q) || !dev_ok(k) || !dev_ok(out)) return GA_ERR_INVALID_ARG;
+  if (!L.k_eq_v && !dev_ok(v)) return GA_ERR_INVALID_ARG;
+  if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
+  ga::PrefillArgs a;
+  a.batch = batch;
+  a.seq = seq;
+  a.hq = cfg->num_heads;
+  a.hkv = L.num_kv_heads;
+  a.dim = L.head_dim;
+  a.group = L.group;
+  a.window = L.window;
+  a.k_eq_v = L.k_eq_v;
+  a.q = q;
+  a.k = k;
+  a.v = L.k_eq_v ? k : v;
+  a.out = out;
+  a.lse = lse;
+  a.scale = L.scale;
+  a.softcap = L.softcap;
+  return hip_rc(ga::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t gemma_attn_decode_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
+                                        int32_t max_ctx) {
+  gemma_attn_layer L;
+  if (ga::resolve_layer(cfg, layer_idx, &L) != GA_OK) return 0;
+  if (batch < 0 || max_ctx < 1) return 0;
+  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx);
+  return ga::decode_workspace(L, cfg->num_heads, batch, plan).total;
+}
+
+int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t max_ctx,
+                      const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_len,
+                      void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  gemma_attn_layer L;
+  const int rc = ga::resolve_layer(cfg, layer_idx, &L);
+  if (rc != GA_OK) return rc;
+  if (batch < 0 || max_ctx < 1) return GA_ERR_INVALID_ARG;
+  if (!ga::attn_dim_supported(L.head_dim) || !ga::attn_group_supported(L.group)) return GA_ERR_UNSUPPORTED;
+  if (batch > 65535 || L.num_kv_heads > 65535 || cfg->num_heads > 65535) return GA_ERR_UNSUPPORTED;
+  if (batch == 0) return GA_OK;
+  if (!dev_ok(q) || !dev_ok(k_cache) || !dev_ok(out) || ctx_len == nullptr) return GA_ERR_INVALID_ARG;
+  if (!L.k_eq_v && !dev_ok(v_cache)) return GA_ERR_INVALID_ARG;
+  if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
+  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx);
+  const ga::DecodeWorkspace ws = ga::decode_workspace(L, cfg->num_heads, batch, plan);
+  if (workspace == nullptr || !ga::aligned16(workspace) || workspace_bytes < ws.total) return GA_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(workspace);
+  ga::DecodeArgs a;
+  a.batch = batch;
+  a.max_ctx = max_ctx;
+  a.hq = cfg->num_heads;
+  a.hkv = L.num_kv_heads;
+  a.dim = L.head_dim;
+  a.group = L.group;
+  a.window = L.window;
+  a.k_eq_v = L.k_eq_v;
+  a.chunk = plan.chunk;
+  a.n_split = plan.n_split;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = L.k_eq_v ? k_cache : v_cache;
+  a.ctx_len = ctx_len;
+  a.out = out;
+  a.lse = lse;
+  a.ws_o = reinterpret_cast<float*>(wsb + ws.o_off);
+  a.ws_m = reinterpret_cast<float*>(wsb + ws.m_off);
+  a.ws_l = reinterpret_cast<float*>(wsb + ws.l_off);
+  a.scale = L.scale;
+  a.softcap = L.softcap;
+  return hip_rc(ga::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+/*
+ * gemma_attn.h -- C ABI of the Gemma-family decoder attention block on MI355X (gfx950).
+ *
+ * One attention layer of the Gemma family (Gemma, Gemma 2, Gemma 3, Gemma 4):
+ * interleaved sliding-window (local) and causal (global) layers, grouped- and
+ * multi-query KV heads, RMSNorm QK-norm, dual-base and partial rotary position
+ * embedding, keys-as-values global layers, query_pre_attn_scalar scaling and the
+ * tanh attention-logit soft cap.
+ *
+ * Sources: the Gemma model pages ("Gemma", "Gemma 2", "Gemma 3", "Gemma 4") and
+ * their API argument tables, and the "google-gemma-4" architecture summary.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Activations and caches are bf16 (raw 16-bit patterns), row-major and
+ *    contiguous: q [B,S,Hq,D], k and v [B,S,Hkv,D], caches [B,Smax,Hkv,D].
+ *    Norm weights are fp32 [D].  Log-sum-exp outputs are fp32, natural log.
+ *  - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *    allocates nothing, keeps no state between calls and is re-entrant.
+ *    Configuration structs and layer structs are HOST pointers, read during the
+ *    call only.
+ *  - Device pointers must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; nothing in the library synchronizes the host.
+ *  - Every argument check runs on the host before the first HIP call; a call
+ *    that returns an error has enqueued nothing.  GA_ERR_HIP reports a failed
+ *    launch (hipGetLastError after the launch).
+ */
+#ifndef GEMMA_ATTN_H
+#define GEMMA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  GA_OK = 0,
+  GA_ERR_INVALID_ARG = 1, /* a null pointer, a size out of range, an inconsistent config */
+  GA_ERR_UNSUPPORTED = 2, /* valid, but no kernel instantiation (head width, group size) */
+  GA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
+  GA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+};
+
+/*
+ * The attention knobs of a Gemma model, named as in the pages' argument tables
+ * (GemmaModel, Gemma2Model, Gemma3Model, Gemma4Model).
+ */
+typedef struct gemma_attn_config {
+  int32_t num_heads;              /* query heads Hq */
+  int32_t num_kv_heads;           /* KV heads on local layers (Hq % it == 0) */
+  int32_t num_global_kv_heads;    /* KV heads on global layers; 0 = num_kv_heads (Gemma 4 table) */
+  int32_t head_dim;               /* D on local layers */
+  int32_t global_head_dim;        /* D on global layers; 0 = head_dim (Gemma 4 table) */
+  int32_t sliding_window;         /* local attention span W; <= 0: every layer is global */
+  int32_t sliding_window_pattern; /* N >= 1: layer l is global iff (l+1) % N == 0; <= 0: all local */
+  int32_t k_eq_v;                 /* global layers use the processed keys as values (Gemma 4 "K=V") */
+  int32_t norm_weight_offset;     /* QK-norm scales by (offset + w): 1 for Gemma 1-3, 0 for Gemma 4 */
+  int32_t reserved;               /* must be 0 */
+  double rope_theta;              /* rotary base on global layers (all layers when no local base) */
+  double rope_local_theta;        /* rotary base on local layers; <= 0: rope_theta (Gemma 3 dual bases) */
+  double partial_rotary_factor;   /* fraction of each head rotated, in [0, 1] (Gemma 4: 0.25) */
+  double attn_logit_softcapping;  /* tanh cap on scaled logits; <= 0: off (Gemma 2: 50) */
+  double query_pre_attn_scalar;   /* logits scale = this^-1/2; <= 0: the layer's D (Gemma 2/3: 256) */
+  double norm_eps;                /* QK-norm epsilon inside the root (1e-6) */
+} gemma_attn_config;
+
+/* Values one layer resolves to (see gemma_attn_resolve_layer). */
+typedef struct gemma_attn_layer {
+  int32_t is_global;    /* 1: full causal layer; 0: sliding-window layer */
+  int32_t window;       /* W on local layers, 0 on global layers */
+  int32_t num_kv_heads; /* Hkv of this layer */
+  int32_t head_dim;     /* D of this layer */
+  int32_t group;        /* g = Hq / Hkv; query head h reads KV head h / g */
+  int32_t rotary_dim;   /* r = 2*floor(partial_rotary_factor * D / 2): dims [0, r) rotate */
+  int32_t k_eq_v;       /* values are the processed keys on this layer */
+  int32_t reserved;
+  double theta;         /* rotary base of this layer */
+  double scale;         /* query_pre_attn_scalar^-1/2 (or D^-1/2) */
+  double softcap;       /* cap, or 0 when off */
+} gemma_attn_layer;
+
+/*
+ * Resolve layer `layer_idx` of a model (pure host function, no HIP call).
+ * Local/global interleave: "one global layer every N" (Gemma 3 table,
+ * sliding_window_pattern; Gemma 2 introduction: every other layer), read as
+ * local layers first in each period.  Global layers take the global KV-head
+ * count, global head width and keys-as-values flag (Gemma 4 table); local
+ * layers take rope_local_theta (Gemma 3 "Dual RoPE bases").
+ * Returns GA_ERR_INVALID_ARG for a null pointer, a negative layer, or a config
+ * that fails validation (Hq not a multiple of Hkv, a non-positive D, a factor
+ * outside [0, 1], a non-positive theta or eps).
+ */
+int gemma_attn_resolve_layer(const gemma_attn_config* cfg, int32_t layer_idx, gemma_attn_layer* out);
+
+/*
+ * QK-norm + rotary prologue for one layer, in one fused pass over q and k.
+ * Per token s of sequence b and per head vector x (width D of the layer):
+ *   1. if a norm weight w is given: x <- x / sqrt(mean(x^2) + eps) * (w + offset)
+ *      (RMSNorm; Gemma 4 "Plain-weight RMSNorm" uses offset 0);
+ *   2. the first r dims rotate in pairs (i, i + r/2) by the angle
+ *      p * theta^(-2i/r) with p = pos0[b] + s; dims [r, D) pass through
+ *      (Gemma 4 "Zero-pad partial rope"; r from partial_rotary_factor).
+ * q_in [B,S,Hq,D] -> q_out, k_in [B,S,Hkv,D] -> k_out; bf16.  Outputs may alias
+ * their inputs exactly (in place) but must not partially overlap them.
+ * k_in may be NULL (then k_out is ignored): queries only, as in decode.
+ * q_norm_w / k_norm_w: fp32 [D] device arrays, or NULL for no norm on that side.
+ * pos0: device int32 [B] first position of each sequence, or NULL for zeros.
+ * Values are never normed or rotated.  Accumulation is fp32; the angle is
+ * formed and reduced modulo 2*pi in fp64; outputs round to nearest even.
+ */
+int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
+                      const void* q_in, const void* k_in, void* q_out, void* k_out,
+                      const float* q_norm_w, const float* k_norm_w, const int32_t* pos0,
+                      void* stream);
+
+/*
+ * Causal self-attention of one layer over a whole prompt (prefill).
+ * For query head h at position i, against KV head h / g:
+ *   s_ij = (q_i . k_j) * scale;  s_ij <- cap * tanh(s_ij / cap) if cap > 0
+ *   (Gemma 2 "Logit softcapping");  allowed iff j <= i and, on local layers,
+ *   i - j < W (exactly W keys including i: the reading of "local attention
+ *   span");  out_i = softmax_j(s_ij) . v_j;  lse_i = log sum_j exp(s_ij).
+ * q [B,S,Hq,D], k [B,S,Hkv,D], v [B,S,Hkv,D] bf16 (outputs of the prologue for
+ * q and k).  On keys-as-values layers v is ignored (may be NULL) and k serves
+ * as values (Gemma 4 "K=V global MQA").  out [B,S,Hq,D] bf16.
+ * lse: fp32 [B,Hq,S] or NULL.  Supported: D in {64, 256, 512},
+ * g in {1, 2, 4, 8, 16}; anything else returns GA_ERR_UNSUPPORTED.
+ * bf16 MFMA with fp32 accumulation; probabilities are rounded to bf16 before
+ * the value product and the row sum uses the same rounded values.
+ */
+int gemma_attn_prefill(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
+                       const void* q, const void* k, const void* v, void* out, float* lse,
+                       void* stream);
+
+/*
+ * Bytes of device workspace gemma_attn_decode needs for (layer, batch, max_ctx);
+ * 0 when the arguments are invalid.
+ */
+size_t gemma_attn_decode_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
+                                        int32_t max_ctx);
+
+/*
+ * One new token per sequence against a contiguous KV cache (the decode step of
+ * the pages' generate()).  q [B,Hq,D] bf16 is the processed query of the token at
+ * position ctx_len[b] - 1.  k_cache, v_cache [B,max_ctx,Hkv,D] bf16 hold the
+ * processed keys and the values of positions 0..max_ctx-1, the current token
+ * included; v_cache is ignored (may be NULL) on keys-as-values layers.
+ * ctx_len: device int32 [B]; entries are clamped to [0, max_ctx] on the device.
+ * Keys read: rows [max(0, ctx - W), ctx) on local layers, [0, ctx) on global
+ * layers; no other cache row is touched.  ctx = 0 gives out = 0, lse = -inf.
+ * out [B,Hq,D] bf16; lse fp32 [B,Hq] or NULL.
+ * workspace: device buffer of at least gemma_attn_decode_workspace_size() bytes
+ * (split-KV partials; contents on entry are ignored).  Supported: D in
+ * {64, 256, 512}, g in {1, 2, 4, 8, 16}.
+ */
+int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t max_ctx,
+                      const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_len,
+                      void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text of an error code. */
+const char* gemma_attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMMA_ATTN_H */

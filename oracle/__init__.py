@@ -32,6 +32,7 @@ from .gemma_ref import (  # noqa: F401
     rms_norm,
     rotary,
     rotary_inv_freq,
+    round_bf16,
     softcap,
     allowed,
     prologue,

@@ -150,6 +150,29 @@ def rotary(x: np.ndarray, positions: np.ndarray, theta: float, rotary_dim: int) 
     return out
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits, ties to even), returned as fp64.
+
+    The library's activations are bf16, so the processed q and k cross the
+    boundary between the prologue and the attention as bf16; an end-to-end
+    comparison applies this rounding to the oracle's own prologue output.
+    Written from the definition: x = m * 2^(e-7) with e = floor(log2|x|) and m
+    rounded half-to-even.  Normal range only (bf16 shares fp32's exponents).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = (x != 0) & np.isfinite(x)
+    ax = np.abs(x[nz])
+    e = np.floor(np.log2(ax))
+    # log2 can land one off for values a hair below a power of two
+    e = np.where(2.0 ** e > ax, e - 1, e)
+    e = np.where(2.0 ** (e + 1) <= ax, e + 1, e)
+    ulp = 2.0 ** (e - 7)
+    out[nz] = np.sign(x[nz]) * np.rint(ax / ulp) * ulp
+    out[~np.isfinite(x)] = x[~np.isfinite(x)]
+    return out
+
+
 def softcap(s: np.ndarray, cap: float) -> np.ndarray:
     """Gemma 2 attention-logit soft cap: cap * tanh(s / cap); cap <= 0 is off."""
     if cap <= 0:

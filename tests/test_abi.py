@@ -1,0 +1,145 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+matches the C struct layouts, resolves layers exactly like the oracle and
+rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import gemma_ref as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemma_attn.h")
+
+
+@pytest.fixture(scope="module")
+def ga():
+    import decoder_attention_amd as ga
+
+    if not os.path.exists(ga.LIB_PATH):
+        pytest.skip("library not built (python -m decoder_attention_amd.build)")
+    ga.load()
+    return ga
+
+
+def _declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(gemma_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(ga):
+    names = _declared_functions()
+    assert set(names) == {"gemma_attn_resolve_layer", "gemma_qk_prologue", "gemma_attn_prefill",
+                          "gemma_attn_decode_workspace_size", "gemma_attn_decode", "gemma_attn_strerror"}
+    lib = ctypes.CDLL(ga.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "sz.c"
+    src.write_text('#include "gemma_attn.h"\n#include <stdio.h>\n#include <stddef.h>\n'
+                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(gemma_attn_config), sizeof(gemma_attn_layer),'
+                   ' offsetof(gemma_attn_config, rope_theta), offsetof(gemma_attn_config, norm_eps),'
+                   ' offsetof(gemma_attn_layer, softcap)); return 0;}\n')
+    exe = tmp_path / "sz"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    import decoder_attention_amd as ga
+
+    assert got == [ctypes.sizeof(ga.CConfig), ctypes.sizeof(ga.CLayer), ga.CConfig.rope_theta.offset,
+                   ga.CConfig.norm_eps.offset, ga.CLayer.softcap.offset]
+
+
+CFGS = [
+    dict(num_heads=16, num_kv_heads=8, num_global_kv_heads=1, head_dim=256, global_head_dim=512, sliding_window=1024,
+         sliding_window_pattern=6, rope_theta=1e6, rope_local_theta=1e4, partial_rotary_factor=0.25, k_eq_v=True),
+    dict(num_heads=8, num_kv_heads=4, head_dim=256, sliding_window=4096, sliding_window_pattern=2,
+         query_pre_attn_scalar=256.0, attn_logit_softcapping=50.0),
+    dict(num_heads=4, num_kv_heads=1, head_dim=256, sliding_window=512, sliding_window_pattern=6, rope_theta=1e6,
+         rope_local_theta=1e4, norm_weight_offset=1),
+    dict(num_heads=8, num_kv_heads=1, head_dim=256, sliding_window=0),
+    dict(num_heads=6, num_kv_heads=3, head_dim=64, sliding_window=7, sliding_window_pattern=0,
+         partial_rotary_factor=0.3),
+    dict(num_heads=6, num_kv_heads=3, head_dim=96, sliding_window=7, sliding_window_pattern=1,
+         partial_rotary_factor=0.7, query_pre_attn_scalar=10.0),
+]
+
+
+@pytest.mark.parametrize("kw", CFGS)
+def test_resolve_layer_matches_oracle(ga, kw):
+    cfg = R.GemmaAttnConfig(**kw)
+    for layer in range(64):
+        a = ga.resolve_layer(kw, layer)
+        b = R.resolve_layer(cfg, layer)
+        for key in ("is_global", "window", "num_kv_heads", "head_dim", "group", "rotary_dim", "k_eq_v", "theta",
+                    "scale", "softcap"):
+            assert a[key] == b[key], (layer, key, a[key], b[key])
+
+
+BAD = [
+    dict(num_heads=6, num_kv_heads=4, head_dim=64),                        # Hq % Hkv
+    dict(num_heads=8, num_kv_heads=4, head_dim=64, num_global_kv_heads=3),  # Hq % Hkv(global)
+    dict(num_heads=8, num_kv_heads=4, head_dim=0),
+    dict(num_heads=8, num_kv_heads=4, head_dim=64, partial_rotary_factor=1.5),
+    dict(num_heads=8, num_kv_heads=4, head_dim=64, partial_rotary_factor=float("nan")),
+    dict(num_heads=8, num_kv_heads=4, head_dim=64, rope_theta=0.0),
+    dict(num_heads=8, num_kv_heads=4, head_dim=64, norm_eps=0.0),
+    dict(num_heads=8, num_kv_heads=4, head_dim=64, norm_weight_offset=2),
+    dict(num_heads=8, num_kv_heads=4, head_dim=64, attn_logit_softcapping=float("inf")),
+]
+
+
+@pytest.mark.parametrize("kw", BAD)
+def test_invalid_configs_rejected(ga, kw):
+    with pytest.raises(ga.GemmaAttnError) as e:
+        ga.resolve_layer(kw, 0)
+    assert e.value.code == ga.GA_ERR_INVALID_ARG
+
+
+def test_argument_errors_before_any_launch(ga):
+    """Every check runs on the host; none of these calls reaches HIP."""
+    lib = ga.load()
+    good = ga.Config(num_heads=8, num_kv_heads=4, head_dim=256).to_c()
+    ref = ctypes.byref
+    fake = ctypes.c_void_p(1 << 20)        # 16-byte aligned, never dereferenced
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.gemma_attn_prefill(ref(good), -1, 1, 8, fake, fake, fake, fake, None, None) == ga.GA_ERR_INVALID_ARG
+    assert lib.gemma_attn_prefill(ref(good), 0, -1, 8, fake, fake, fake, fake, None, None) == ga.GA_ERR_INVALID_ARG
+    assert lib.gemma_attn_prefill(ref(good), 0, 1, 8, None, fake, fake, fake, None, None) == ga.GA_ERR_INVALID_ARG
+    assert lib.gemma_attn_prefill(ref(good), 0, 1, 8, odd, fake, fake, fake, None, None) == ga.GA_ERR_INVALID_ARG
+    assert lib.gemma_attn_prefill(ref(good), 0, 1, 8, fake, fake, None, fake, None, None) == ga.GA_ERR_INVALID_ARG
+    assert lib.gemma_attn_prefill(ref(good), 0, 0, 8, None, None, None, None, None, None) == ga.GA_OK
+    unsup = ga.Config(num_heads=8, num_kv_heads=4, head_dim=128).to_c()
+    assert lib.gemma_attn_prefill(ref(unsup), 0, 1, 8, fake, fake, fake, fake, None, None) == ga.GA_ERR_UNSUPPORTED
+    g32 = ga.Config(num_heads=32, num_kv_heads=1, head_dim=256).to_c()
+    assert lib.gemma_attn_prefill(ref(g32), 0, 1, 8, fake, fake, fake, fake, None, None) == ga.GA_ERR_UNSUPPORTED
+    pro = ga.Config(num_heads=8, num_kv_heads=4, head_dim=96).to_c()
+    assert lib.gemma_qk_prologue(ref(pro), 0, 1, 8, fake, fake, fake, fake, None, None, None, None) == ga.GA_ERR_UNSUPPORTED
+    assert lib.gemma_qk_prologue(ref(good), 0, 1, 8, fake, fake, fake, None, None, None, None, None) == ga.GA_ERR_INVALID_ARG
+    keqv = ga.Config(num_heads=8, num_kv_heads=1, head_dim=512, k_eq_v=True).to_c()
+    need = lib.gemma_attn_decode_workspace_size(ref(keqv), 0, 4, 1000)
+    assert need > 0
+    assert lib.gemma_attn_decode(ref(keqv), 0, 4, 1000, fake, fake, None, fake, fake, None, fake, need - 1,
+                                 None) == ga.GA_ERR_WORKSPACE
+    assert lib.gemma_attn_decode(ref(keqv), 0, 4, 1000, fake, fake, None, fake, fake, None, None, need,
+                                 None) == ga.GA_ERR_WORKSPACE
+    assert lib.gemma_attn_decode(ref(good), 0, 4, 1000, fake, fake, None, fake, fake, None, fake, 1 << 30,
+                                 None) == ga.GA_ERR_INVALID_ARG   # v_cache missing without keys-as-values
+    assert lib.gemma_attn_decode(ref(keqv), 0, 4, 0, fake, fake, None, fake, fake, None, fake, need,
+                                 None) == ga.GA_ERR_INVALID_ARG
+    assert lib.gemma_attn_decode_workspace_size(ref(keqv), 0, 4, 0) == 0
+    assert ga.load().gemma_attn_strerror(ga.GA_ERR_WORKSPACE).decode().startswith("decode workspace")
+
+
+@pytest.mark.parametrize("W,max_ctx,B", [(1024, 65536, 64), (0, 65536, 64), (0, 100, 1), (4096, 3000, 2), (0, 1, 1)])
+def test_decode_workspace_covers_every_split(ga, W, max_ctx, B):
+    kw = dict(num_heads=16, num_kv_heads=8, head_dim=256, sliding_window=W, sliding_window_pattern=0)
+    need = ga.decode_workspace_size(kw, 0, B, max_ctx)
+    L = R.resolve_layer(R.GemmaAttnConfig(**kw), 0)
+    span = min(W, max_ctx) if W else max_ctx
+    # at least one fp32 (o[D], m, l) record per (sequence, head, 4096-key chunk) of the longest span
+    assert need >= B * 16 * (L["head_dim"] + 2) * 4 * -(-span // 4096)

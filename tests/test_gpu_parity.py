@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: attention outputs max-abs 2e-2 and mean-abs 2e-3 on unit-scale
+outputs; prologue outputs within one bf16 ulp of the fp64 value; integer
+facts (mask, window, GQA map, decode range) bit-exact.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from oracle import gemma_ref as R
+from synth import BF16_NAN, bf16_bits_to_f64, ctx_lengths, normal_bf16, norm_weight
+from tests.gpu_util import assert_close, bf16_ulp, from_dev_bf16_bits, from_dev_f64, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+GEMMA2 = dict(num_heads=8, num_kv_heads=4, head_dim=256, sliding_window=300, sliding_window_pattern=2,
+              rope_theta=1e4, attn_logit_softcapping=50.0, query_pre_attn_scalar=256.0)
+GEMMA3 = dict(num_heads=4, num_kv_heads=1, head_dim=256, sliding_window=128, sliding_window_pattern=6,
+              rope_theta=1e6, rope_local_theta=1e4, query_pre_attn_scalar=256.0, norm_weight_offset=1)
+GEMMA4 = dict(num_heads=16, num_kv_heads=8, num_global_kv_heads=1, head_dim=256, global_head_dim=512,
+              sliding_window=200, sliding_window_pattern=6, rope_theta=1e6, rope_local_theta=1e4,
+              partial_rotary_factor=0.25, k_eq_v=True, norm_weight_offset=0)
+TINY = dict(num_heads=4, num_kv_heads=1, head_dim=64, sliding_window=64, sliding_window_pattern=0,
+            rope_theta=1e4, attn_logit_softcapping=50.0, query_pre_attn_scalar=64.0)
+
+
+def _cfgs(kw):
+    return R.GemmaAttnConfig(**kw), kw
+
+
+def _layer_inputs(kw, layer, B, S, seed, qscale=1.0, with_norm=False):
+    cfg = R.GemmaAttnConfig(**kw)
+    L = R.resolve_layer(cfg, layer)
+    D, Hkv, Hq = L["head_dim"], L["num_kv_heads"], cfg.num_heads
+    q = normal_bf16(seed, (B, S, Hq, D), scale=qscale)
+    k = normal_bf16(seed + 1, (B, S, Hkv, D))
+    v = normal_bf16(seed + 2, (B, S, Hkv, D))
+    qw = norm_weight(seed + 3, D) if with_norm else None
+    kw_ = norm_weight(seed + 4, D) if with_norm else None
+    return cfg, L, q, k, v, qw, kw_
+
+
+# ----------------------------------------------------------------------------- end to end
+E2E = [
+    ("tiny_local", TINY, 0, 1, 256, False),
+    ("gemma2_local", GEMMA2, 0, 2, 1000, False),
+    ("gemma2_global", GEMMA2, 1, 2, 1000, False),
+    ("gemma3_local_qknorm", GEMMA3, 0, 1, 777, True),
+    ("gemma3_global_qknorm", GEMMA3, 5, 1, 777, True),
+    ("gemma4_global_keqv_partial", GEMMA4, 5, 1, 600, True),
+    ("gemma4_local_partial", GEMMA4, 0, 2, 450, True),
+]
+
+
+@pytest.mark.parametrize("name,kw,layer,B,S,norm", E2E, ids=[e[0] for e in E2E])
+def test_end_to_end_layer(gpu, name, kw, layer, B, S, norm):
+    ga = gpu
+    cfg, L, q, k, v, qw, kw_ = _layer_inputs(kw, layer, B, S, seed=100 + layer, with_norm=norm)
+    print(f"[e2e] {name} layer={layer} B={B} S={S} D={L['head_dim']} g={L['group']}", flush=True)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    qwd = to_dev(qw) if norm else None
+    kwd = to_dev(kw_) if norm else None
+    qt, kt = ga.qk_prologue(kw, layer, qd, kd, q_norm_w=qwd, k_norm_w=kwd)
+    out, lse = ga.attn_prefill(kw, layer, qt, kt, None if L["k_eq_v"] else vd, want_lse=True)
+    import torch
+
+    torch.cuda.synchronize()
+    rq, rk = R.prologue(cfg, layer, bf16_bits_to_f64(q), bf16_bits_to_f64(k), qw, kw_)
+    # the processed q and k cross the library boundary as bf16
+    ro, rl = R.prefill(cfg, layer, R.round_bf16(rq), R.round_bf16(rk), bf16_bits_to_f64(v))
+    mx, mn = assert_close(from_dev_f64(out), ro, what=name)
+    assert_close(from_dev_f64(lse), rl, max_abs=2e-2, mean_abs=2e-3, what=name + " lse")
+    rms = float(np.sqrt(np.mean((from_dev_f64(out) - ro) ** 2)) / np.sqrt(np.mean(ro ** 2)))
+    print(f"[e2e] {name}: max-abs {mx:.2e} mean-abs {mn:.2e} rms-rel {rms:.2e}", flush=True)
+
+
+# ----------------------------------------------------------------------------- prologue only
+PRO = [
+    ("d64_full", TINY, 0, None, [0]),
+    ("d256_norm1", GEMMA3, 0, 1, [0, 70000]),
+    ("d512_partial_norm0", GEMMA4, 5, 0, [3, 65535]),
+    ("d256_partial_local", GEMMA4, 1, 0, [0, 12345]),
+]
+
+
+@pytest.mark.parametrize("name,kw,layer,offset,pos0", PRO, ids=[p[0] for p in PRO])
+def test_prologue_within_one_ulp(gpu, name, kw, layer, offset, pos0):
+    ga = gpu
+    kw = dict(kw)
+    if offset is not None:
+        kw["norm_weight_offset"] = offset
+    B = len(pos0)
+    cfg, L, q, k, _, qw, kw_ = _layer_inputs(kw, layer, B, 67, seed=300, with_norm=offset is not None)
+    print(f"[prologue] {name}", flush=True)
+    p0 = np.array(pos0, dtype=np.int32)
+    qt, kt = ga.qk_prologue(kw, layer, to_dev_bf16(q), to_dev_bf16(k),
+                            q_norm_w=None if qw is None else to_dev(qw),
+                            k_norm_w=None if kw_ is None else to_dev(kw_), pos0=to_dev(p0))
+    rq, rk = R.prologue(cfg, layer, bf16_bits_to_f64(q), bf16_bits_to_f64(k), qw, kw_, p0)
+    for got, ref in ((from_dev_f64(qt), rq), (from_dev_f64(kt), rk)):
+        # one bf16 ulp of the exact value, plus the fp32 rounding of the
+        # rotation a*cos - b*sin, which is relative to the row's magnitude and
+        # shows where the two products nearly cancel
+        row_scale = np.max(np.abs(ref), axis=-1, keepdims=True)
+        tol = bf16_ulp(ref) + 2.0 ** -20 * row_scale
+        err = np.abs(got - ref)
+        bad = err > tol
+        assert not bad.any(), f"{name}: {bad.sum()} of {bad.size} beyond tolerance, max err/ulp {np.max(err / bf16_ulp(ref)):.3f}"
+        assert np.mean(err <= bf16_ulp(ref) * 0.5 + 2.0 ** -20 * row_scale) > 0.99
+
+
+def test_prologue_in_place_and_queries_only(gpu):
+    ga = gpu
+    cfg, L, q, k, _, qw, kw_ = _layer_inputs(GEMMA3, 0, 2, 40, seed=310, with_norm=True)
+    qd, kd = to_dev_bf16(q), to_dev_bf16(k)
+    a_q, a_k = ga.qk_prologue(GEMMA3, 0, qd, kd, q_norm_w=to_dev(qw), k_norm_w=to_dev(kw_))
+    ga.qk_prologue(GEMMA3, 0, qd, kd, q_out=qd, k_out=kd, q_norm_w=to_dev(qw), k_norm_w=to_dev(kw_))
+    b_q, _ = ga.qk_prologue(GEMMA3, 0, to_dev_bf16(q), None, q_norm_w=to_dev(qw))
+    assert np.array_equal(from_dev_bf16_bits(a_q), from_dev_bf16_bits(qd))
+    assert np.array_equal(from_dev_bf16_bits(a_k), from_dev_bf16_bits(kd))
+    assert np.array_equal(from_dev_bf16_bits(a_q), from_dev_bf16_bits(b_q))
+
+
+# ----------------------------------------------------------------------------- attention only, all instantiations
+MATRIX = [(D, g, kv, cap, W) for D, g, kv, cap, W in itertools.product(
+    [64, 256, 512], [1, 2, 4, 8, 16], [False, True], [0.0, 50.0], [0, 45]) if not (kv and W)]
+
+
+@pytest.mark.parametrize("D,g,keqv,cap,W", MATRIX)
+def test_prefill_instantiations(gpu, D, g, keqv, cap, W):
+    ga = gpu
+    Hkv = 2 if g <= 4 else 1
+    kw = dict(num_heads=g * Hkv, num_kv_heads=Hkv, head_dim=D, sliding_window=W, sliding_window_pattern=0,
+              attn_logit_softcapping=cap, k_eq_v=keqv)
+    cfg = R.GemmaAttnConfig(**kw)
+    B, S = 2, 163
+    print(f"[prefill] D={D} g={g} keqv={keqv} cap={cap} W={W}", flush=True)
+    q = normal_bf16(500, (B, S, g * Hkv, D), scale=2.0)
+    k = normal_bf16(501, (B, S, Hkv, D))
+    v = normal_bf16(502, (B, S, Hkv, D))
+    out, lse = ga.attn_prefill(kw, 0, to_dev_bf16(q), to_dev_bf16(k), None if keqv else to_dev_bf16(v), want_lse=True)
+    ro, rl = R.prefill(cfg, 0, bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v))
+    assert_close(from_dev_f64(out), ro, what=f"D{D} g{g}")
+    assert_close(from_dev_f64(lse), rl, what=f"D{D} g{g} lse")
+
+
+@pytest.mark.parametrize("scale", [8.0, 32.0])
+@pytest.mark.parametrize("kw,layer", [(GEMMA2, 0), (GEMMA2, 1), (GEMMA4, 5)])
+def test_prefill_peaked(gpu, kw, layer, scale):
+    """Large logits reach the soft cap's nonlinear range and give sharp maxima."""
+    ga = gpu
+    cfg, L, q, k, v, _, _ = _layer_inputs(kw, layer, 1, 333, seed=600, qscale=scale)
+    print(f"[peaked] layer={layer} scale={scale}", flush=True)
+    out = ga.attn_prefill(kw, layer, to_dev_bf16(q), to_dev_bf16(k), None if L["k_eq_v"] else to_dev_bf16(v))
+    ro, _ = R.prefill(cfg, layer, bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v))
+    assert_close(from_dev_f64(out), ro, what=f"peaked x{scale}")
+
+
+# ----------------------------------------------------------------------------- integer facts, bit-exact
+@pytest.mark.parametrize("D,g,W", [(64, 4, 64), (256, 2, 100), (512, 16, 0), (256, 1, 1)])
+def test_prefill_integer_facts(gpu, D, g, W):
+    """q = 0: every allowed key weighs exactly 1, so lse = ln(count) and the
+    output is the exact mean; V constant per KV head (distinct powers of two)
+    pins the head map; W = 1 returns v itself; row 0 returns v_0."""
+    ga = gpu
+    import torch
+
+    Hkv = 2
+    kw = dict(num_heads=g * Hkv, num_kv_heads=Hkv, head_dim=D, sliding_window=W, sliding_window_pattern=0,
+              attn_logit_softcapping=50.0)
+    B, S = 1, 150
+    q = torch.zeros((B, S, g * Hkv, D), dtype=torch.bfloat16, device="cuda")
+    k = to_dev_bf16(normal_bf16(700, (B, S, Hkv, D)))
+    vc = torch.empty((B, S, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    vc[:, :, 0] = 0.25
+    vc[:, :, 1] = 4.0
+    out, lse = ga.attn_prefill(kw, 0, q, k, vc, want_lse=True)
+    o = from_dev_f64(out)
+    assert np.all(o[:, :, :g] == 0.25) and np.all(o[:, :, g:] == 4.0)
+    cnt = np.array([i - (max(0, i - W + 1) if W else 0) + 1 for i in range(S)], dtype=np.float64)
+    l = from_dev_f64(lse)[0]
+    assert np.all(np.rint(np.exp(l)) == cnt[None, :])
+    assert np.abs(l - np.log(cnt)[None, :]).max() < 1e-5
+    # a random V: row 0 is v_0 bitwise; W = 1 gives v_i bitwise
+    v = normal_bf16(701, (B, S, Hkv, D))
+    qn = to_dev_bf16(normal_bf16(702, (B, S, g * Hkv, D)))
+    out = ga.attn_prefill(kw, 0, qn, k, to_dev_bf16(v))
+    ob = from_dev_bf16_bits(out)
+    assert np.array_equal(ob[0, 0, :g], np.broadcast_to(v[0, 0, 0], (g, D)))
+    if W == 1:
+        for hq in range(g * Hkv):
+            assert np.array_equal(ob[0, :, hq], v[0, :, hq // g])
+
+
+def test_prefill_deterministic(gpu):
+    ga = gpu
+    cfg, L, q, k, v, _, _ = _layer_inputs(GEMMA2, 0, 2, 700, seed=800)
+    a = ga.attn_prefill(GEMMA2, 0, to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v))
+    b = ga.attn_prefill(GEMMA2, 0, to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v))
+    assert np.array_equal(from_dev_bf16_bits(a), from_dev_bf16_bits(b))
+
+
+def test_keys_as_values_equals_explicit_copy(gpu):
+    ga = gpu
+    kw = dict(GEMMA4)
+    cfg, L, q, k, _, _, _ = _layer_inputs(kw, 5, 1, 300, seed=900)
+    a = ga.attn_prefill(kw, 5, to_dev_bf16(q), to_dev_bf16(k), None)
+    kw2 = dict(kw, k_eq_v=False)
+    b = ga.attn_prefill(kw2, 5, to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(k.copy()))
+    assert np.array_equal(from_dev_bf16_bits(a), from_dev_bf16_bits(b))
+
+
+# ----------------------------------------------------------------------------- decode
+DEC = [
+    ("gemma4_local", GEMMA4 | dict(sliding_window=1024), 0),
+    ("gemma4_global_keqv", GEMMA4, 5),
+    ("gemma2_local_cap", GEMMA2, 0),
+    ("tiny_mqa", TINY, 0),
+]
+
+
+@pytest.mark.parametrize("name,kw,layer", DEC, ids=[d[0] for d in DEC])
+def test_decode_vs_oracle_with_sentinels(gpu, name, kw, layer):
+    ga = gpu
+    import torch
+
+    cfg = R.GemmaAttnConfig(**kw)
+    L = R.resolve_layer(cfg, layer)
+    B, Smax = 6, 3000
+    D, Hkv, Hq = L["head_dim"], L["num_kv_heads"], cfg.num_heads
+    ctx = ctx_lengths(1234, B, 1, Smax)
+    ctx[0], ctx[1] = 1, Smax
+    print(f"[decode] {name} ctx={ctx.tolist()}", flush=True)
+    kc = normal_bf16(1300, (B, Smax, Hkv, D))
+    vc = normal_bf16(1301, (B, Smax, Hkv, D))
+    W = L["window"]
+    for b in range(B):                     # poison every row the kernel must not read
+        lo = max(0, ctx[b] - W) if W else 0
+        kc[b, :lo] = BF16_NAN
+        kc[b, ctx[b]:] = BF16_NAN
+        vc[b, :lo] = BF16_NAN
+        vc[b, ctx[b]:] = BF16_NAN
+    q = normal_bf16(1302, (B, Hq, D), scale=2.0)
+    out, lse = ga.attn_decode(kw, layer, to_dev_bf16(q), to_dev_bf16(kc), None if L["k_eq_v"] else to_dev_bf16(vc),
+                              to_dev(ctx), want_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = R.decode(cfg, layer, bf16_bits_to_f64(q), bf16_bits_to_f64(kc), bf16_bits_to_f64(vc), ctx)
+    assert_close(from_dev_f64(out), ro, what=name)
+    assert_close(from_dev_f64(lse), rl, what=name + " lse")
+    # ctx = 1: the single visible row is returned exactly
+    ob = from_dev_bf16_bits(out)
+    for hq in range(Hq):
+        assert np.array_equal(ob[0, hq], (kc if L["k_eq_v"] else vc)[0, 0, hq // L["group"]])
+
+
+def test_decode_matches_prefill_rows(gpu):
+    """decode at ctx = p + 1 equals prefill row p of the same keys (within tolerance)."""
+    ga = gpu
+    import torch
+
+    kw = GEMMA2
+    cfg = R.GemmaAttnConfig(**kw)
+    for layer in (0, 1):
+        L = R.resolve_layer(cfg, layer)
+        B, S = 2, 900
+        q = normal_bf16(1400, (B, S, 8, 256))
+        k = normal_bf16(1401, (B, S, 4, 256))
+        v = normal_bf16(1402, (B, S, 4, 256))
+        full = from_dev_f64(ga.attn_prefill(kw, layer, to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)))
+        for p in (0, 299, 300, 899):
+            ctx = np.array([p + 1, p + 1], dtype=np.int32)
+            out = ga.attn_decode(kw, layer, to_dev_bf16(np.ascontiguousarray(q[:, p])), to_dev_bf16(k),
+                                 to_dev_bf16(v), to_dev(ctx))
+            torch.cuda.synchronize()
+            assert_close(from_dev_f64(out), full[:, p], max_abs=1e-2, mean_abs=1e-3, what=f"row {p}")
+
+
+def test_decode_zero_context(gpu):
+    ga = gpu
+    kw = TINY
+    q = to_dev_bf16(normal_bf16(1500, (2, 4, 64)))
+    kc = to_dev_bf16(normal_bf16(1501, (2, 16, 1, 64)))
+    out, lse = ga.attn_decode(kw, 0, q, kc, kc, to_dev(np.array([0, 3], dtype=np.int32)), want_lse=True)
+    o, l = from_dev_f64(out), from_dev_f64(lse)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(l[0])) and np.all(np.isfinite(l[1]))

@@ -277,3 +277,18 @@ def test_work_counts_by_enumeration(S, W):
     ctx = [0, 1, 5, 9]
     span = sum(min(c, W) if W else c for c in ctx)
     assert R.decode_kv_bytes(cfg, 0, ctx) == span * 2 * 16 * 2 * 2
+
+
+def test_round_bf16_closed_forms_and_bits():
+    from synth import bf16_bits_to_f64, f32_to_bf16_bits
+
+    # ties go to the even neighbour; 8 significant bits
+    assert R.round_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    assert R.round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+    assert R.round_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -30]))[0] == 1 + 2.0 ** -7
+    assert R.round_bf16(np.array([-3.0, 0.0, 2.0 ** -100]))[1] == 0.0
+    assert R.round_bf16(np.array([255.5]))[0] == 256.0 and R.round_bf16(np.array([254.5]))[0] == 254.0
+    # agrees with bit-level round-to-nearest-even of fp32 values (fp32 -> bf16 is a single rounding)
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    assert np.array_equal(R.round_bf16(x.astype(np.float64)), bf16_bits_to_f64(f32_to_bf16_bits(x)))
