@@ -1,7 +1,6 @@
 """Build the HIP library libgemma_attn.so in-tree (gfx950).
 
     python -m decoder_attention_amd.build          # compile every source, link
-    python -m decoder_attention_amd.build --host   # also build the host-logic test binary (g++)
 
 Objects go to decoder_attention_amd/_build/; the shared library is written next
 to this file.  Every call recompiles.
@@ -67,23 +66,11 @@ def build(jobs: int | None = None) -> str:
     return LIB
 
 
-def build_host_test() -> str:
-    """g++ build of the host logic alone (no HIP), for CPU tests."""
-    os.makedirs(BUILD, exist_ok=True)
-    out = os.path.join(BUILD, "libgemma_attn_host.so")
-    _run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-I", INCLUDE, "-I", CSRC,
-          os.path.join(CSRC, "host_logic.cpp"), os.path.join(CSRC, "host_logic_capi.cpp"), "-o", out])
-    return out
-
-
 def main() -> None:
     ap = argparse.ArgumentParser()
-    ap.add_argument("--host", action="store_true")
     ap.add_argument("-j", type=int, default=None)
     a = ap.parse_args()
     print(build(a.j))
-    if a.host:
-        print(build_host_test())
 
 
 if __name__ == "__main__":
