@@ -21,8 +21,12 @@
 //   the tile's keys, so the row max and row sum are in-lane plus one exchange
 //   with lane ^ 32, and the output rescale is a per-lane scalar.
 //   Scale, tanh soft cap, causal/window mask (boundary tiles only), online
-//   softmax in the exp2 domain; probabilities rounded to bf16 and the row sum
-//   taken over the same rounded values.
+//   softmax in the exp2 domain with a lazily updated running max (the
+//   accumulators are rescaled only when a row's max grows by more than 2^8);
+//   probabilities rounded to bf16 and the row sum taken over the same
+//   rounded values.
+//   The next K/V tile is loaded into registers while the current one is
+//   computed and written to the second LDS buffer: one barrier per tile.
 //   O^T[D x 32 cols] += V^T . P^T           (same MFMA)
 //     A = V^T read straight from the row-major LDS tile with the gfx950
 //     transpose read (ds_read_b64_tr_b16), B = P^T from the score registers.
@@ -46,6 +50,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kCols = 32;                 // query columns per wave
 constexpr int kKeys = 32;                 // keys per tile
 constexpr int kPad = 8;                   // bf16 elements of padding per LDS row
+constexpr float kTau = 8.f;               // lazy-rescale threshold (log2 units)
 
 struct PrefillParams {
   const uint16_t* q;
@@ -77,12 +82,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   constexpr int kDS = kDW / 16;       // k-steps of QK^T per wave
   constexpr int kDB = kDW / 32;       // 32-row blocks of O^T per wave
   constexpr int kLd = D + kPad;       // LDS row pitch (elements)
-  constexpr int kChunks = kKeys * D / 8;
+  constexpr int kChunks = kKeys * D / 8;   // 16-byte pieces per tile
+  constexpr int kPer = kChunks / kThreads;  // pieces per thread
+  constexpr int kTile = kKeys * kLd;        // elements per LDS tile buffer
+  static_assert(kChunks % kThreads == 0, "tile must split evenly over the workgroup");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKeys * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[KEQV ? 8 : kKeys * kLd];
+  // Two tile buffers: the next tile is written while the current one is read.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[KEQV ? 8 : 2 * kTile];
   __shared__ __attribute__((aligned(16))) float sx_lds[kSplit > 1 ? kWaves * 64 * 16 : 4];
-  const uint16_t* vt_lds = KEQV ? k_lds : v_lds;
 
   const int32_t S = p.seq;
   const int32_t qb = p.n_qblocks - 1 - static_cast<int32_t>(blockIdx.x);
@@ -126,31 +134,55 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   float l_run = 0.f;
 
   const int64_t kv_row0 = static_cast<int64_t>(b) * S;
+  const int32_t n_tiles = (kv_end - kv_begin + kKeys - 1) / kKeys;
 
-  for (int32_t kt = kv_begin; kt < kv_end; kt += kKeys) {
-    __syncthreads();
-    // Stage the K (and V) tile: 16-byte pieces, row-major, zero past the end.
+  // Register staging of one tile: thread tid owns 16-byte pieces tid + i*256.
+  u32x4 kreg[kPer];
+  u32x4 vreg[KEQV ? 1 : kPer];
+  auto load_tile = [&](int32_t kt) {
 #pragma unroll
-    for (int i = tid; i < kChunks; i += kThreads) {
-      const int32_t row = i / (D / 8);
-      const int32_t c8 = i % (D / 8);
+    for (int i = 0; i < kPer; ++i) {
+      const int32_t idx = tid + i * kThreads;
+      const int32_t row = idx / (D / 8);
+      const int32_t c8 = idx % (D / 8);
       const int32_t key = kt + row;
-      u32x4 kv4 = u32x4{0u, 0u, 0u, 0u};
-      u32x4 vv4 = u32x4{0u, 0u, 0u, 0u};
+      kreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (!KEQV) vreg[KEQV ? 0 : i] = u32x4{0u, 0u, 0u, 0u};
       if (key < S) {
         const int64_t off = ((kv_row0 + key) * p.hkv + kvh) * D + c8 * 8;
-        kv4 = *reinterpret_cast<const u32x4*>(p.k + off);
-        if (!KEQV) vv4 = *reinterpret_cast<const u32x4*>(p.v + off);
+        kreg[i] = *reinterpret_cast<const u32x4*>(p.k + off);
+        if (!KEQV) vreg[KEQV ? 0 : i] = *reinterpret_cast<const u32x4*>(p.v + off);
       }
-      *reinterpret_cast<u32x4*>(&k_lds[row * kLd + c8 * 8]) = kv4;
-      if (!KEQV) *reinterpret_cast<u32x4*>(&v_lds[row * kLd + c8 * 8]) = vv4;
     }
-    __syncthreads();
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int32_t idx = tid + i * kThreads;
+      const int32_t row = idx / (D / 8);
+      const int32_t c8 = idx % (D / 8);
+      *reinterpret_cast<u32x4*>(&k_lds[buf * kTile + row * kLd + c8 * 8]) = kreg[i];
+      if (!KEQV) *reinterpret_cast<u32x4*>(&v_lds[buf * kTile + row * kLd + c8 * 8]) = vreg[KEQV ? 0 : i];
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(kv_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int32_t it = 0; it < n_tiles; ++it) {
+    const int32_t kt = kv_begin + it * kKeys;
+    const int32_t buf = it & 1;
+    const bool more = it + 1 < n_tiles;
+    if (more) load_tile(kt + kKeys);      // in flight while this tile is computed
+    const uint16_t* kb = k_lds + buf * kTile;
+    const uint16_t* vb = (KEQV ? k_lds : v_lds) + buf * kTile;
 
     // Does this wave see any key of the tile?  (wave-uniform; equal for both
     // waves of a D-split pair)
     const bool need = kt <= w_hi && (W == 0 || kt + kKeys - 1 >= w_lo - W + 1);
-    if (kSplit == 1 && !need) continue;
     const bool full = kt + kKeys - 1 <= w_lo && (W == 0 || kt >= w_hi - W + 1);
 
     // S^T = K . Q^T (partial over this wave's D slice when split)
@@ -158,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     if (need) {
 #pragma unroll
       for (int ds = 0; ds < kDS; ++ds) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[j * kLd + dlo + ds * 16 + h * 8]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[j * kLd + dlo + ds * 16 + h * 8]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc, 0, 0, 0);
       }
     }
@@ -169,74 +201,86 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < 16; r += 4) mine[(r / 4) * 64] = f32x4{sacc[r], sacc[r + 1], sacc[r + 2], sacc[r + 3]};
       __syncthreads();
-      if (!need) continue;
+      if (need) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const f32x4 t4 = other[(r / 4) * 64];
-        sacc[r] += t4[0];
-        sacc[r + 1] += t4[1];
-        sacc[r + 2] += t4[2];
-        sacc[r + 3] += t4[3];
+        for (int r = 0; r < 16; r += 4) {
+          const f32x4 t4 = other[(r / 4) * 64];
+          sacc[r] += t4[0];
+          sacc[r + 1] += t4[1];
+          sacc[r + 2] += t4[2];
+          sacc[r + 3] += t4[3];
+        }
       }
     }
 
-    // Logits in the exp2 domain; lane holds keys kt + (r/4)*8 + h*4 + r%4.
-    float x[16];
-    float mx = -INFINITY;
+    if (need) {
+      // Logits in the exp2 domain; lane holds keys kt + (r/4)*8 + h*4 + r%4.
+      float x[16];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float t;
-      if (CAP) {
-        // cap * tanh(s*scale/cap) = cap - 2*cap / (exp(2*s*scale/cap) + 1)
-        const float e = __builtin_amdgcn_exp2f(sacc[r] * p.cap_in2);
-        t = fmaf(-2.f * p.cap_log2, __builtin_amdgcn_rcpf(e + 1.f), p.cap_log2);
-      } else {
-        t = sacc[r] * p.scale_log2;
+      for (int r = 0; r < 16; ++r) {
+        float t;
+        if (CAP) {
+          // cap * tanh(s*scale/cap) = cap - 2*cap / (exp(2*s*scale/cap) + 1)
+          const float e = __builtin_amdgcn_exp2f(sacc[r] * p.cap_in2);
+          t = fmaf(-2.f * p.cap_log2, __builtin_amdgcn_rcpf(e + 1.f), p.cap_log2);
+        } else {
+          t = sacc[r] * p.scale_log2;
+        }
+        if (!full) {
+          const int32_t key = kt + (r >> 2) * 8 + h * 4 + (r & 3);
+          const bool ok = key <= pos_m && (W == 0 || pos_m - key < W);
+          t = ok ? t : -INFINITY;
+        }
+        x[r] = t;
+        mx = fmaxf(mx, t);
       }
-      if (!full) {
-        const int32_t key = kt + (r >> 2) * 8 + h * 4 + (r & 3);
-        const bool ok = key <= pos_m && (W == 0 || pos_m - key < W);
-        t = ok ? t : -INFINITY;
+      mx = wave_max_xor32(mx);
+      // The running max only moves when the tile exceeds it by more than
+      // kTau (log2 units): probabilities then stay <= 2^kTau and the output
+      // rescale, a pass over every accumulator, is rare.
+      const bool grow = mx > m_run + kTau;
+      const float m_next = grow ? mx : m_run;
+      const float m_use = m_next == -INFINITY ? 0.f : m_next;
+      if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) o[db] *= alpha;
       }
-      x[r] = t;
-      mx = fmaxf(mx, t);
-    }
-    mx = wave_max_xor32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+      m_run = m_next;
 
-    uint32_t pk[8];
-    float ls = 0.f;
+      uint32_t pk[8];
+      float ls = 0.f;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float e0 = __builtin_amdgcn_exp2f(x[2 * r] - m_use);
-      const float e1 = __builtin_amdgcn_exp2f(x[2 * r + 1] - m_use);
-      pk[r] = pack_bf16x2(e0, e1);
-      ls += lo_bf16(pk[r]) + hi_bf16(pk[r]);
-    }
-    l_run = fmaf(l_run, alpha, ls);
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) o[db] *= alpha;
+      for (int r = 0; r < 8; ++r) {
+        const float e0 = __builtin_amdgcn_exp2f(x[2 * r] - m_use);
+        const float e1 = __builtin_amdgcn_exp2f(x[2 * r + 1] - m_use);
+        pk[r] = pack_bf16x2(e0, e1);
+        ls += lo_bf16(pk[r]) + hi_bf16(pk[r]);
+      }
+      l_run += ls;
 
-    // O^T += V^T . P^T, two 16-key halves per tile.
-    const int32_t grp = lane >> 4;
-    const int32_t i16 = lane & 15;
+      // O^T += V^T . P^T, two 16-key halves per tile.
+      const int32_t grp = lane >> 4;
+      const int32_t i16 = lane & 15;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const u32x4 pb = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
-      const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
-      const int32_t r0 = 16 * t + 4 * h + (i16 >> 2);
-      const int32_t cbase = (grp & 1) * 16 + 4 * (i16 & 3);
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 pb = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
+        const int32_t r0 = 16 * t + 4 * h + (i16 >> 2);
+        const int32_t cbase = (grp & 1) * 16 + 4 * (i16 & 3);
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const i16x4 a0 = lds_read_tr16(&vt_lds[r0 * kLd + dlo + db * 32 + cbase]);
-        const i16x4 a1 = lds_read_tr16(&vt_lds[(r0 + 8) * kLd + dlo + db * 32 + cbase]);
-        const bf16x8 aop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, o[db], 0, 0, 0);
+        for (int db = 0; db < kDB; ++db) {
+          const i16x4 a0 = lds_read_tr16(&vb[r0 * kLd + dlo + db * 32 + cbase]);
+          const i16x4 a1 = lds_read_tr16(&vb[(r0 + 8) * kLd + dlo + db * 32 + cbase]);
+          const bf16x8 aop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, o[db], 0, 0, 0);
+        }
       }
     }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   const float l_tot = wave_sum_xor32(l_run);
