@@ -1,36 +1,50 @@
 // Causal / sliding-window prefill attention for the Gemma family (gfx950).
 //
 // Work decomposition
-//   One workgroup = 4 waves = 128 query "columns" of one (sequence, KV head):
-//   the g query heads of the KV group times 128/g consecutive positions
+//   One workgroup = 4 waves covering the query "columns" of one (sequence,
+//   KV head): the g query heads of the KV group times consecutive positions
 //   (column c -> position p0 + c/g, head kvh*g + c%g).  Stacking the group's
 //   heads makes every K/V tile staged in LDS serve 128 query rows, whatever g.
-//   Grid = (q-blocks, KV heads, batch); q-blocks are issued last-first so the
-//   longest causal rows start first.
+//   Head width 512 does not fit one wave's registers (Q^T 128 + O^T 256 per
+//   lane), so there the two waves of a pair share 32 columns and split D: each
+//   holds half of Q^T and O^T, computes a partial S^T over its half and the
+//   pair exchanges the partials through LDS (fp32 a+b == b+a, so both waves
+//   see the same scores bit for bit).  A workgroup then covers 64 columns.
 //
-// Head width 512 does not fit one wave's registers (Q^T 128 + O^T 256 per
-// lane), so there the two waves of a pair share 32 columns and split D: each
-// holds half of Q^T and O^T, computes a partial S^T over its half and the pair
-// exchanges the partials through LDS (fp32 a+b == b+a, so both waves see the
-// same scores bit for bit).  A workgroup then covers 64 columns.
+// Block order
+//   The dispatcher deals linear block ids round-robin over the 8 XCDs, each
+//   with its own L2.  Blocks are renumbered so that the blocks an XCD runs
+//   together belong to as few (sequence, KV head) pairs as possible -- they
+//   then stream the same K/V tiles through that XCD's L2 -- while every XCD
+//   gets the same amount of work; inside a pair, the longest causal rows go
+//   first.
+//
+// K/V staging
+//   Tiles of 32 keys are copied HBM -> LDS by the gfx950 direct-to-LDS loads
+//   (global_load_lds_dwordx4, no register round trip) into a ring of three
+//   buffers (two when three do not fit), up to two tiles ahead of the one
+//   being computed; one barrier per tile.
+//   Rows are unpadded and their 16-byte chunks are XOR-swizzled (chunk c of
+//   row r sits at c ^ rot3(r)), which keeps both the K operand reads
+//   (ds_read_b128, 8 rows per phase) and the transposed V reads
+//   (ds_read_b64_tr_b16, 4 rows x 2 chunks per 16-lane group) free of bank
+//   conflicts.
 //
 // Per wave (32 columns), per tile of 32 keys:
 //   S^T[32 keys x 32 cols] = K_tile . Q^T   (v_mfma_f32_32x32x16_bf16, fp32 acc)
-//     A = K rows from LDS (ds_read_b128), B = Q^T held in registers.
+//     A = K rows from LDS, B = Q^T held in registers.
 //   In this orientation every lane owns ONE query column (lane % 32) and 16 of
-//   the tile's keys, so the row max and row sum are in-lane plus one exchange
-//   with lane ^ 32, and the output rescale is a per-lane scalar.
+//   the tile's keys, so the row max and row sum are in-lane plus one
+//   v_permlane32_swap with the other half of the wave.
 //   Scale, tanh soft cap, causal/window mask (boundary tiles only), online
 //   softmax in the exp2 domain with a lazily updated running max (the
 //   accumulators are rescaled only when a row's max grows by more than 2^8);
 //   probabilities rounded to bf16 and the row sum taken over the same
 //   rounded values.
-//   The next K/V tile is loaded into registers while the current one is
-//   computed and written to the second LDS buffer: one barrier per tile.
 //   O^T[D x 32 cols] += V^T . P^T           (same MFMA)
-//     A = V^T read straight from the row-major LDS tile with the gfx950
-//     transpose read (ds_read_b64_tr_b16), B = P^T from the score registers.
-//     With keys-as-values the same LDS tile is both K and V.
+//     A = V^T read straight from the row-major tile with the transpose read,
+//     B = P^T from the score registers.  With keys-as-values the same LDS
+//     tile is both K and V.
 //   Tiles outside a wave's causal/window band are skipped by that wave.
 //
 // Sources: causal decoder attention (Gemma page), sliding-window local layers
@@ -49,7 +63,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kCols = 32;                 // query columns per wave
 constexpr int kKeys = 32;                 // keys per tile
-constexpr int kPad = 8;                   // bf16 elements of padding per LDS row
+constexpr int kLdsBudget = 160 * 1024;   // bytes of LDS per workgroup
 constexpr float kTau = 8.f;               // lazy-rescale threshold (log2 units)
 
 struct PrefillParams {
@@ -58,7 +72,7 @@ struct PrefillParams {
   const uint16_t* v;
   uint16_t* out;
   float* lse;
-  int32_t seq, hq, hkv, window, n_qblocks;
+  int32_t seq, hq, hkv, window, n_qblocks, n_qblocks_pad, batch;
   float scale_log2;   // scale * log2(e)            (no cap)
   float cap_in2;      // 2 * scale * log2(e) / cap  (cap: exp2 argument of tanh)
   float cap_log2;     // cap * log2(e)
@@ -74,28 +88,94 @@ constexpr int positions_per_block() {
   return (kWaves / DSplit<D>::value) * kCols / G;
 }
 
-template <int D, int G, bool KEQV, bool CAP>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
-  constexpr int kSplit = DSplit<D>::value;
-  constexpr int kDW = D / kSplit;     // D slice of one wave
-  constexpr int kP = positions_per_block<D, G>();
-  constexpr int kDS = kDW / 16;       // k-steps of QK^T per wave
-  constexpr int kDB = kDW / 32;       // 32-row blocks of O^T per wave
-  constexpr int kLd = D + kPad;       // LDS row pitch (elements)
-  constexpr int kChunks = kKeys * D / 8;   // 16-byte pieces per tile
-  constexpr int kPer = kChunks / kThreads;  // pieces per thread
-  constexpr int kTile = kKeys * kLd;        // elements per LDS tile buffer
-  static_assert(kChunks % kThreads == 0, "tile must split evenly over the workgroup");
+// 3-bit rotate: the XOR pattern of the 16-byte chunks of LDS row r.
+__device__ __forceinline__ int32_t swz(int32_t r) { return ((r << 1) | ((r >> 2) & 1)) & 7; }
 
-  // Two tile buffers: the next tile is written while the current one is read.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2 * kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[KEQV ? 8 : 2 * kTile];
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// The lane index, hidden from loop-invariant code motion: lane-derived LDS
+// and DMA offsets are recomputed each tile (a few integer ops) instead of
+// being held in registers across the loop, which would not fit.
+__device__ __forceinline__ int32_t lane_id_here() {
+  int32_t l = static_cast<int32_t>(threadIdx.x);
+  asm volatile("" : "+v"(l));
+  return l & 63;
+}
+
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Linear block id -> (pair = b*Hkv + kvh, t = rank in heavy-first order), or
+// t >= n_qblocks for padding blocks.
+__device__ __forceinline__ void block_work(const PrefillParams& p, int32_t& pair, int32_t& t) {
+  const int32_t lin = static_cast<int32_t>(blockIdx.x);
+  const int32_t npairs = p.batch * p.hkv;
+  const int32_t nq = p.n_qblocks_pad;
+  const int32_t xcd = lin & 7;
+  const int32_t slot = lin >> 3;
+  if ((npairs & 7) == 0) {          // every XCD owns npairs/8 pairs, one after another
+    pair = xcd + 8 * (slot / nq);
+    t = slot % nq;
+  } else if ((8 % npairs) == 0) {   // 8/npairs XCDs share a pair and interleave its q-blocks
+    const int32_t k = 8 / npairs;
+    pair = xcd % npairs;
+    t = slot * k + xcd / npairs;
+  } else {
+    pair = lin / nq;
+    t = lin % nq;
+  }
+}
+
+// Two waves per SIMD (two workgroups per CU) wherever the LDS ring allows:
+// the register budget is then 256 VGPRs per lane and one wave's softmax
+// overlaps the other's matrix work.
+template <int D, bool KEQV>
+constexpr int waves_per_simd() {
+  return (D <= 256 || KEQV) ? 2 : 1;
+}
+
+template <int D, int G, bool KEQV, bool CAP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, KEQV>(), 2)))
+void prefill_kernel(PrefillParams p) {
+  constexpr int kSplit = DSplit<D>::value;
+  constexpr int kDW = D / kSplit;            // D slice of one wave
+  constexpr int kP = positions_per_block<D, G>();
+  constexpr int kDS = kDW / 16;              // k-steps of QK^T per wave
+  constexpr int kDB = kDW / 32;              // 32-row blocks of O^T per wave
+  constexpr int kRowChunks = D / 8;          // 16-byte chunks per key row
+  constexpr int kTileElems = kKeys * D;
+  constexpr int kWaveLoads = kKeys * kRowChunks / 64 / kWaves;   // DMA ops per wave per tensor
+  constexpr int kLoadsPerTile = kWaveLoads * (KEQV ? 1 : 2);
+  static_assert(kKeys * kRowChunks % (64 * kWaves) == 0, "tile must split evenly over the waves");
+  // Ring depth: three tiles when two workgroups (two waves per SIMD) still
+  // fit in LDS, else two.
+  constexpr int kSxBytes = kSplit > 1 ? kWaves * 64 * 16 * 4 : 16;
+  constexpr int kTileBytes = kTileElems * 2 * (KEQV ? 1 : 2);
+  constexpr int kBufs = 2 * (3 * kTileBytes + kSxBytes) <= kLdsBudget ? 3 : 2;
+  constexpr int kAhead = kBufs - 1;          // tiles in flight beyond the one computed
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBufs * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[KEQV ? 8 : kBufs * kTileElems];
   __shared__ __attribute__((aligned(16))) float sx_lds[kSplit > 1 ? kWaves * 64 * 16 : 4];
 
+  int32_t pair, tq;
+  block_work(p, pair, tq);
+  if (tq >= p.n_qblocks) return;                       // padding block (uniform)
   const int32_t S = p.seq;
-  const int32_t qb = p.n_qblocks - 1 - static_cast<int32_t>(blockIdx.x);
-  const int32_t kvh = blockIdx.y;
-  const int32_t b = blockIdx.z;
+  const int32_t qb = p.n_qblocks - 1 - tq;
+  const int32_t b = pair / p.hkv;
+  const int32_t kvh = pair % p.hkv;
   const int32_t p0 = qb * kP;
   const int32_t tid = threadIdx.x;
   const int32_t wave = tid >> 6;
@@ -111,21 +191,56 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int32_t pos_m = col_valid ? pos : S - 1;
   const int32_t W = p.window;
 
+  const int32_t w_lo = p0 + (cw * kCols) / G;                         // wave's first position
+  const int32_t w_hi = min(p0 + (cw * kCols + kCols - 1) / G, S - 1); // wave's last valid position
+  const int32_t kv_end = min(S, p0 + kP);
+  int32_t kv_begin = W > 0 ? max(0, p0 - W + 1) : 0;
+  kv_begin &= ~(kKeys - 1);
+  const int32_t n_tiles = (kv_end - kv_begin + kKeys - 1) / kKeys;
+
+  // Issue the direct-to-LDS copies of the tile starting at key kt into ring
+  // slot buf.  Addresses are a wave-uniform tile base plus a 32-bit per-lane
+  // byte offset (row * row pitch + chunk), so they need no 64-bit registers.
+  const char* kbase = reinterpret_cast<const char*>(p.k) + static_cast<int64_t>(b) * S * p.hkv * D * 2;
+  const char* vbase = reinterpret_cast<const char*>(KEQV ? p.k : p.v) + static_cast<int64_t>(b) * S * p.hkv * D * 2;
+  const uint32_t row_pitch = static_cast<uint32_t>(p.hkv) * D * 2;
+  auto issue = [&](int32_t kt, int32_t buf) {
+    const int64_t tile_off = (static_cast<int64_t>(kt) * p.hkv + kvh) * D * 2;
+    const char* kt_base = kbase + tile_off;
+    const char* vt_base = vbase + tile_off;
+    const int32_t last_row = S - 1 - kt;     // rows beyond it are past the end (masked)
+    const int32_t ln = lane_id_here();
+#pragma unroll
+    for (int i = 0; i < kWaveLoads; ++i) {
+      const int32_t base = (wave * kWaveLoads + i) * 64;     // first physical chunk of this op
+      const int32_t pc = base + ln;
+      int32_t row = pc / kRowChunks;
+      const int32_t lc = (pc % kRowChunks) ^ swz(row);        // logical chunk held at pc
+      row = min(row, last_row);
+      const uint32_t off = static_cast<uint32_t>(row) * row_pitch + static_cast<uint32_t>(lc) * 16u;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt_base + off),
+                                       (__attribute__((address_space(3))) void*)(k_lds + buf * kTileElems + base * 8),
+                                       16, 0, 0);
+      if (!KEQV) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt_base + off),
+                                         (__attribute__((address_space(3))) void*)(v_lds + buf * kTileElems + base * 8),
+                                         16, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int a = 0; a < kAhead; ++a) {
+    if (a < n_tiles) issue(kv_begin + a * kKeys, a);
+  }
+
   // Q^T operand: lane holds d = ds*16 + h*8 + [0, 8) of its column.
   bf16x8 qf[kDS];
   {
     const uint16_t* qrow = p.q + ((static_cast<int64_t>(b) * S + pos_m) * p.hq + head) * D + dlo + h * 8;
 #pragma unroll
-    for (int ds = 0; ds < kDS; ++ds) {
-      qf[ds] = *reinterpret_cast<const bf16x8*>(qrow + ds * 16);
-    }
+    for (int ds = 0; ds < kDS; ++ds) qf[ds] = *reinterpret_cast<const bf16x8*>(qrow + ds * 16);
   }
-
-  const int32_t w_lo = p0 + (cw * kCols) / G;                       // wave's first position
-  const int32_t w_hi = min(p0 + (cw * kCols + kCols - 1) / G, S - 1); // wave's last valid position
-  const int32_t kv_end = min(S, p0 + kP);
-  int32_t kv_begin = W > 0 ? max(0, p0 - W + 1) : 0;
-  kv_begin &= ~(kKeys - 1);
 
   f32x16 o[kDB];
 #pragma unroll
@@ -133,52 +248,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  const int64_t kv_row0 = static_cast<int64_t>(b) * S;
-  const int32_t n_tiles = (kv_end - kv_begin + kKeys - 1) / kKeys;
-
-  // Register staging of one tile: thread tid owns 16-byte pieces tid + i*256.
-  u32x4 kreg[kPer];
-  u32x4 vreg[KEQV ? 1 : kPer];
-  auto load_tile = [&](int32_t kt) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int32_t idx = tid + i * kThreads;
-      const int32_t row = idx / (D / 8);
-      const int32_t c8 = idx % (D / 8);
-      const int32_t key = kt + row;
-      kreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (!KEQV) vreg[KEQV ? 0 : i] = u32x4{0u, 0u, 0u, 0u};
-      if (key < S) {
-        const int64_t off = ((kv_row0 + key) * p.hkv + kvh) * D + c8 * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(p.k + off);
-        if (!KEQV) vreg[KEQV ? 0 : i] = *reinterpret_cast<const u32x4*>(p.v + off);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int32_t idx = tid + i * kThreads;
-      const int32_t row = idx / (D / 8);
-      const int32_t c8 = idx % (D / 8);
-      *reinterpret_cast<u32x4*>(&k_lds[buf * kTile + row * kLd + c8 * 8]) = kreg[i];
-      if (!KEQV) *reinterpret_cast<u32x4*>(&v_lds[buf * kTile + row * kLd + c8 * 8]) = vreg[KEQV ? 0 : i];
-    }
-  };
-
-  if (n_tiles > 0) {
-    load_tile(kv_begin);
-    store_tile(0);
-  }
+  wait_vmcnt<0>();   // Q^T and the first tiles
   __syncthreads();
 
   for (int32_t it = 0; it < n_tiles; ++it) {
     const int32_t kt = kv_begin + it * kKeys;
-    const int32_t buf = it & 1;
-    const bool more = it + 1 < n_tiles;
-    if (more) load_tile(kt + kKeys);      // in flight while this tile is computed
-    const uint16_t* kb = k_lds + buf * kTile;
-    const uint16_t* vb = (KEQV ? k_lds : v_lds) + buf * kTile;
+    const int32_t buf = it % kBufs;
+    if (it + kAhead < n_tiles) issue(kt + kAhead * kKeys, (it + kAhead) % kBufs);
+    const uint16_t* kb = k_lds + buf * kTileElems;
+    const uint16_t* vb = (KEQV ? k_lds : v_lds) + buf * kTileElems;
 
     // Does this wave see any key of the tile?  (wave-uniform; equal for both
     // waves of a D-split pair)
@@ -188,16 +266,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     // S^T = K . Q^T (partial over this wave's D slice when split)
     f32x16 sacc = f32x16{};
     if (need) {
+      const int32_t ln = lane_id_here();
+      const int32_t jj = ln & 31;
+      const int32_t hh = ln >> 5;
+      const int32_t sw = swz(jj);
 #pragma unroll
       for (int ds = 0; ds < kDS; ++ds) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[j * kLd + dlo + ds * 16 + h * 8]);
+        const int32_t lc = (dlo >> 3) + ds * 2 + hh;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[jj * D + ((lc ^ sw) << 3)]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc, 0, 0, 0);
       }
     }
     if (kSplit > 1) {
       // [wave][r/4][lane] float4 layout: consecutive lanes, consecutive 16 bytes.
-      f32x4* mine = reinterpret_cast<f32x4*>(sx_lds) + wave * 256 + lane;
-      const f32x4* other = reinterpret_cast<const f32x4*>(sx_lds) + (wave ^ 1) * 256 + lane;
+      const int32_t ln = lane_id_here();
+      f32x4* mine = reinterpret_cast<f32x4*>(sx_lds) + wave * 256 + ln;
+      const f32x4* other = reinterpret_cast<const f32x4*>(sx_lds) + (wave ^ 1) * 256 + ln;
 #pragma unroll
       for (int r = 0; r < 16; r += 4) mine[(r / 4) * 64] = f32x4{sacc[r], sacc[r + 1], sacc[r + 2], sacc[r + 3]};
       __syncthreads();
@@ -235,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         x[r] = t;
         mx = fmaxf(mx, t);
       }
-      mx = wave_max_xor32(mx);
+      mx = xhalf_max(mx);
       // The running max only moves when the tile exceeds it by more than
       // kTau (log2 units): probabilities then stay <= 2^kTau and the output
       // rescale, a pass over every accumulator, is rare.
@@ -262,28 +346,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       l_run += ls;
 
       // O^T += V^T . P^T, two 16-key halves per tile.
-      const int32_t grp = lane >> 4;
-      const int32_t i16 = lane & 15;
+      const int32_t ln = lane_id_here();
+      const int32_t lgrp = ln >> 4;
+      const int32_t li16 = ln & 15;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const u32x4 pb = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
         const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
-        const int32_t r0 = 16 * t + 4 * h + (i16 >> 2);
-        const int32_t cbase = (grp & 1) * 16 + 4 * (i16 & 3);
+        const int32_t r0 = 16 * t + 4 * (ln >> 5) + (li16 >> 2);
+        const int32_t r1 = r0 + 8;
+        const int32_t sw0 = swz(r0);
+        const int32_t sw1 = swz(r1);
+        const int32_t half8 = (li16 & 1) * 4;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
-          const i16x4 a0 = lds_read_tr16(&vb[r0 * kLd + dlo + db * 32 + cbase]);
-          const i16x4 a1 = lds_read_tr16(&vb[(r0 + 8) * kLd + dlo + db * 32 + cbase]);
+          const int32_t lc = ((dlo + db * 32 + (lgrp & 1) * 16) >> 3) + ((li16 & 3) >> 1);
+          const i16x4 a0 = lds_read_tr16(&vb[r0 * D + ((lc ^ sw0) << 3) + half8]);
+          const i16x4 a1 = lds_read_tr16(&vb[r1 * D + ((lc ^ sw1) << 3) + half8]);
           const bf16x8 aop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, o[db], 0, 0, 0);
         }
       }
     }
-    if (more) store_tile(buf ^ 1);
+    // The next tile's copies must have landed before anyone reads them; the
+    // copies of the tile after it may stay in flight.
+    if (kAhead > 1 && it + 2 < n_tiles) wait_vmcnt<(kAhead > 1 ? kLoadsPerTile : 0)>(); else wait_vmcnt<0>();
     __syncthreads();
   }
 
-  const float l_tot = wave_sum_xor32(l_run);
+  const float l_tot = xhalf_sum(l_run);
   if (col_valid) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = p.out + ((static_cast<int64_t>(b) * S + pos) * p.hq + head) * D + dlo;
@@ -310,8 +401,17 @@ hipError_t launch_t(const PrefillArgs& a, const PrefillParams& prm, hipStream_t 
   constexpr int kP = positions_per_block<D, G>();
   PrefillParams pp = prm;
   pp.n_qblocks = (a.seq + kP - 1) / kP;
-  const dim3 grid(static_cast<uint32_t>(pp.n_qblocks), static_cast<uint32_t>(a.hkv), static_cast<uint32_t>(a.batch));
-  hipLaunchKernelGGL((prefill_kernel<D, G, KEQV, CAP>), grid, dim3(kThreads), 0, stream, pp);
+  const int32_t npairs = a.batch * a.hkv;
+  int32_t pad = pp.n_qblocks;
+  if ((npairs & 7) != 0 && (8 % npairs) == 0) {
+    const int32_t k = 8 / npairs;
+    pad = (pp.n_qblocks + k - 1) / k * k;
+  }
+  pp.n_qblocks_pad = pad;
+  const int64_t blocks = static_cast<int64_t>(npairs) * pad;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<D, G, KEQV, CAP>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0,
+                     stream, pp);
   return hipGetLastError();
 }
 
@@ -348,7 +448,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   prm.hq = a.hq;
   prm.hkv = a.hkv;
   prm.window = a.window;
+  prm.batch = a.batch;
   prm.n_qblocks = 0;
+  prm.n_qblocks_pad = 0;
   const double log2e = 1.4426950408889634;
   prm.scale_log2 = static_cast<float>(a.scale * log2e);
   prm.cap_in2 = a.softcap > 0.0 ? static_cast<float>(2.0 * a.scale * log2e / a.softcap) : 0.f;
