@@ -52,6 +52,8 @@
 // table), query_pre_attn_scalar (Gemma 2 / Gemma 3 tables), GQA/MQA head
 // sharing (Gemma 2 "Grouped-query attention"; Gemma "multi-query attention"),
 // keys-as-values global layers (Gemma 4 "K=V global MQA").
+#include <type_traits>
+
 #include "ga_device.h"
 #include "ga_kernels.h"
 
@@ -155,9 +157,10 @@ void prefill_kernel(PrefillParams p) {
   constexpr int kDB = kDW / 32;              // 32-row blocks of O^T per wave
   constexpr int kRowChunks = D / 8;          // 16-byte chunks per key row
   constexpr int kTileElems = kKeys * D;
-  constexpr int kWaveLoads = kKeys * kRowChunks / 64 / kWaves;   // DMA ops per wave per tensor
+  constexpr int kOps = kKeys * kRowChunks / 64;                  // 1 KB DMA ops per tensor per tile
+  constexpr int kWaveLoads = (kOps + kWaves - 1) / kWaves;        // DMA ops per wave per tensor
   constexpr int kLoadsPerTile = kWaveLoads * (KEQV ? 1 : 2);
-  static_assert(kKeys * kRowChunks % (64 * kWaves) == 0, "tile must split evenly over the waves");
+  static_assert(kKeys * kRowChunks % 64 == 0, "tile must split into whole 1 KB ops");
   // Ring depth: three tiles when two workgroups (two waves per SIMD) still
   // fit in LDS, else two.
   constexpr int kSxBytes = kSplit > 1 ? kWaves * 64 * 16 * 4 : 16;
@@ -165,9 +168,28 @@ void prefill_kernel(PrefillParams p) {
   constexpr int kBufs = 2 * (3 * kTileBytes + kSxBytes) <= kLdsBudget ? 3 : 2;
   constexpr int kAhead = kBufs - 1;          // tiles in flight beyond the one computed
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBufs * kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[KEQV ? 8 : kBufs * kTileElems];
+  // One LDS array per ring slot: every access names its slot at compile time
+  // (the loop is unrolled by the ring depth), so the compiler can tell a read
+  // of the current tile from the copies still landing in the other slots and
+  // does not wait for them.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds2[kBufs > 2 ? kTileElems : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[KEQV ? 8 : kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[KEQV ? 8 : kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds2[(KEQV || kBufs < 3) ? 8 : kTileElems];
   __shared__ __attribute__((aligned(16))) float sx_lds[kSplit > 1 ? kWaves * 64 * 16 : 4];
+  auto kslot = [&](auto B) -> uint16_t* {
+    if constexpr (decltype(B)::value == 0) return k_lds0;
+    else if constexpr (decltype(B)::value == 1) return k_lds1;
+    else return k_lds2;
+  };
+  auto vslot = [&](auto B) -> uint16_t* {
+    if constexpr (KEQV) return kslot(B);
+    else if constexpr (decltype(B)::value == 0) return v_lds0;
+    else if constexpr (decltype(B)::value == 1) return v_lds1;
+    else return v_lds2;
+  };
 
   int32_t pair, tq;
   block_work(p, pair, tq);
@@ -178,7 +200,7 @@ void prefill_kernel(PrefillParams p) {
   const int32_t kvh = pair % p.hkv;
   const int32_t p0 = qb * kP;
   const int32_t tid = threadIdx.x;
-  const int32_t wave = tid >> 6;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar from here on
   const int32_t lane = tid & 63;
   const int32_t j = lane & 31;       // column within the wave
   const int32_t h = lane >> 5;       // half of the wave
@@ -190,6 +212,7 @@ void prefill_kernel(PrefillParams p) {
   const bool col_valid = pos < S;
   const int32_t pos_m = col_valid ? pos : S - 1;
   const int32_t W = p.window;
+  const int32_t key_lo = W > 0 ? pos_m - W + 1 : 0;   // first key this column may see
 
   const int32_t w_lo = p0 + (cw * kCols) / G;                         // wave's first position
   const int32_t w_hi = min(p0 + (cw * kCols + kCols - 1) / G, S - 1); // wave's last valid position
@@ -199,19 +222,22 @@ void prefill_kernel(PrefillParams p) {
   const int32_t n_tiles = (kv_end - kv_begin + kKeys - 1) / kKeys;
 
   // Issue the direct-to-LDS copies of the tile starting at key kt into ring
-  // slot buf.  Addresses are a wave-uniform tile base plus a 32-bit per-lane
+  // slot B.  Addresses are a wave-uniform tile base plus a 32-bit per-lane
   // byte offset (row * row pitch + chunk), so they need no 64-bit registers.
   const char* kbase = reinterpret_cast<const char*>(p.k) + static_cast<int64_t>(b) * S * p.hkv * D * 2;
   const char* vbase = reinterpret_cast<const char*>(KEQV ? p.k : p.v) + static_cast<int64_t>(b) * S * p.hkv * D * 2;
   const uint32_t row_pitch = static_cast<uint32_t>(p.hkv) * D * 2;
-  auto issue = [&](int32_t kt, int32_t buf) {
+  auto issue = [&](int32_t kt, auto B) {
     const int64_t tile_off = (static_cast<int64_t>(kt) * p.hkv + kvh) * D * 2;
     const char* kt_base = kbase + tile_off;
     const char* vt_base = vbase + tile_off;
     const int32_t last_row = S - 1 - kt;     // rows beyond it are past the end (masked)
     const int32_t ln = lane_id_here();
+    uint16_t* kdst = kslot(B);
+    uint16_t* vdst = vslot(B);
 #pragma unroll
     for (int i = 0; i < kWaveLoads; ++i) {
+      if (kOps % kWaves != 0 && wave * kWaveLoads + i >= kOps) break;   // uniform per wave
       const int32_t base = (wave * kWaveLoads + i) * 64;     // first physical chunk of this op
       const int32_t pc = base + ln;
       int32_t row = pc / kRowChunks;
@@ -219,20 +245,19 @@ void prefill_kernel(PrefillParams p) {
       row = min(row, last_row);
       const uint32_t off = static_cast<uint32_t>(row) * row_pitch + static_cast<uint32_t>(lc) * 16u;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt_base + off),
-                                       (__attribute__((address_space(3))) void*)(k_lds + buf * kTileElems + base * 8),
-                                       16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(kdst + base * 8), 16, 0, 0);
       if (!KEQV) {
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt_base + off),
-                                         (__attribute__((address_space(3))) void*)(v_lds + buf * kTileElems + base * 8),
-                                         16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(vdst + base * 8), 16, 0, 0);
       }
     }
   };
 
-#pragma unroll
-  for (int a = 0; a < kAhead; ++a) {
-    if (a < n_tiles) issue(kv_begin + a * kKeys, a);
-  }
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (0 < n_tiles) issue(kv_begin, I0{});
+  if (kAhead > 1 && 1 < n_tiles) issue(kv_begin + kKeys, I1{});
 
   // Q^T operand: lane holds d = ds*16 + h*8 + [0, 8) of its column.
   bf16x8 qf[kDS];
@@ -251,12 +276,15 @@ void prefill_kernel(PrefillParams p) {
   wait_vmcnt<0>();   // Q^T and the first tiles
   __syncthreads();
 
-  for (int32_t it = 0; it < n_tiles; ++it) {
+  int32_t it = 0;
+  // One tile: compute from ring slot B while the copies for slot
+  // (B + kAhead) % kBufs are issued.
+  auto step = [&](auto B) {
+    constexpr int kB = decltype(B)::value;
     const int32_t kt = kv_begin + it * kKeys;
-    const int32_t buf = it % kBufs;
-    if (it + kAhead < n_tiles) issue(kt + kAhead * kKeys, (it + kAhead) % kBufs);
-    const uint16_t* kb = k_lds + buf * kTileElems;
-    const uint16_t* vb = (KEQV ? k_lds : v_lds) + buf * kTileElems;
+    if (it + kAhead < n_tiles) issue(kt + kAhead * kKeys, std::integral_constant<int, (kB + kAhead) % kBufs>{});
+    const uint16_t* kb = kslot(B);
+    const uint16_t* vb = vslot(B);
 
     // Does this wave see any key of the tile?  (wave-uniform; equal for both
     // waves of a D-split pair)
@@ -312,8 +340,9 @@ void prefill_kernel(PrefillParams p) {
           t = sacc[r] * p.scale_log2;
         }
         if (!full) {
+          // allowed iff key_lo <= key <= pos (branch-free; key_lo from the window)
           const int32_t key = kt + (r >> 2) * 8 + h * 4 + (r & 3);
-          const bool ok = key <= pos_m && (W == 0 || pos_m - key < W);
+          const bool ok = (key <= pos_m) & (key >= key_lo);
           t = ok ? t : -INFINITY;
         }
         x[r] = t;
@@ -372,6 +401,16 @@ void prefill_kernel(PrefillParams p) {
     // copies of the tile after it may stay in flight.
     if (kAhead > 1 && it + 2 < n_tiles) wait_vmcnt<(kAhead > 1 ? kLoadsPerTile : 0)>(); else wait_vmcnt<0>();
     __syncthreads();
+    ++it;
+  };
+  while (it < n_tiles) {
+    step(I0{});
+    if (it >= n_tiles) break;
+    step(I1{});
+    if constexpr (kBufs > 2) {
+      if (it >= n_tiles) break;
+      step(I2{});
+    }
   }
 
   const float l_tot = xhalf_sum(l_run);
