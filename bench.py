@@ -301,6 +301,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip decode and the other prefill configs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 1 GiB device copy (counter scale)")
+    ap.add_argument("--workload", default="all", choices=["all", "pair", "gemma3", "gemma4", "decode"],
+                    help="restrict to one workload (for profiling); the JSON line is printed for 'all'/'pair' only")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (the attention path is "
@@ -312,6 +314,17 @@ def main():
 
     torch.cuda.set_device(0)
     ga.load()
+    if a.workload in ("gemma3", "gemma4", "decode"):
+        out = {}
+        if a.workload == "gemma3":
+            for layer, name in ((0, "gemma3_1b_local_w512"), (5, "gemma3_1b_global")):
+                out[name] = bench_prefill_layer(ga, 3, GEMMA3_STACK, layer, 4, 16384, True, reps=a.steps)
+        elif a.workload == "gemma4":
+            out["gemma4_12b_global_keqv_d512"] = bench_prefill_layer(ga, 4, GEMMA4_12B, 5, 1, 32768, True, reps=a.steps)
+        else:
+            out["decode"] = bench_decode(ga, reps=a.steps)
+        print(json.dumps({"workload": a.workload, **out}), flush=True)
+        return
     log("[bench] gemma2 pair: generating inputs")
     pair = bench_pair(ga, a.steps, a.warmup)
     log(f"[bench] gemma2 pair: {pair['value']:.1f} TFLOP/s, step {pair['step_ms']:.3f} ms")
@@ -346,7 +359,7 @@ def main():
         for _ in range(3):
             y.copy_(x)
         torch.cuda.synchronize()
-    if not a.no_extra:
+    if not a.no_extra and a.workload == "all":
         log("[bench] gemma3 stack / gemma4 global prefill")
         cfgs = {}
         for layer, name in ((0, "gemma3_1b_local_w512"), (5, "gemma3_1b_global")):
@@ -363,7 +376,7 @@ def main():
         log("[bench] gemma4 decode: building caches")
         line["decode"] = bench_decode(ga)
         log(f"[bench] decode: {json.dumps(line['decode'])}")
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and a.workload == "all":
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -25,9 +25,9 @@
 //   buffers (two when three do not fit), up to two tiles ahead of the one
 //   being computed; one barrier per tile.
 //   Rows are unpadded and their 16-byte chunks are XOR-swizzled (chunk c of
-//   row r sits at c ^ rot3(r)), which keeps both the K operand reads
-//   (ds_read_b128, 8 rows per phase) and the transposed V reads
-//   (ds_read_b64_tr_b16, 4 rows x 2 chunks per 16-lane group) free of bank
+//   row r sits at c ^ f(r)), which keeps both the K operand reads
+//   (ds_read_b128, 16 rows per 256-byte phase) and the transposed V reads
+//   (ds_read_b64_tr_b16, 4 rows x 4 chunks per half-wave) free of bank
 //   conflicts.
 //
 // Per wave (32 columns), per tile of 32 keys:
@@ -90,8 +90,18 @@ constexpr int positions_per_block() {
   return (kWaves / DSplit<D>::value) * kCols / G;
 }
 
-// 3-bit rotate: the XOR pattern of the 16-byte chunks of LDS row r.
-__device__ __forceinline__ int32_t swz(int32_t r) { return ((r << 1) | ((r >> 2) & 1)) & 7; }
+// XOR pattern of the 16-byte chunks of LDS row r.  The LDS serves 256 bytes
+// (64 banks) per cycle: a ds_read_b128 phase is 16 lanes = 16 consecutive K
+// rows at one logical chunk, a ds_read_b64_tr_b16 half-wave is 4 rows (aligned
+// to 4) x 4 chunks (aligned to 4).  Rows of >= 256 bytes: a 4-bit rotate of
+// r, a permutation of 16 consecutive rows whose bits 2-3 differ within every
+// aligned group of 4 rows.  128-byte rows (D = 64) pair up in a 256-byte
+// window, so the pattern uses 3 bits and separates rows r and r + 2.
+template <int D>
+__device__ __forceinline__ int32_t swz(int32_t r) {
+  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -227,23 +237,35 @@ void prefill_kernel(PrefillParams p) {
   const char* kbase = reinterpret_cast<const char*>(p.k) + static_cast<int64_t>(b) * S * p.hkv * D * 2;
   const char* vbase = reinterpret_cast<const char*>(KEQV ? p.k : p.v) + static_cast<int64_t>(b) * S * p.hkv * D * 2;
   const uint32_t row_pitch = static_cast<uint32_t>(p.hkv) * D * 2;
+  // Per-lane byte offsets of this wave's copy ops inside a tile (rows not
+  // clamped); loop-invariant, so the copies of a full tile cost no VALU.
+  uint32_t doff[kWaveLoads];
+#pragma unroll
+  for (int i = 0; i < kWaveLoads; ++i) {
+    const int32_t pc = (wave * kWaveLoads + i) * 64 + lane;
+    const int32_t row = pc / kRowChunks;
+    const int32_t lc = (pc % kRowChunks) ^ swz<D>(row);       // logical chunk held at pc
+    doff[i] = static_cast<uint32_t>(row) * row_pitch + static_cast<uint32_t>(lc) * 16u;
+  }
   auto issue = [&](int32_t kt, auto B) {
     const int64_t tile_off = (static_cast<int64_t>(kt) * p.hkv + kvh) * D * 2;
     const char* kt_base = kbase + tile_off;
     const char* vt_base = vbase + tile_off;
-    const int32_t last_row = S - 1 - kt;     // rows beyond it are past the end (masked)
-    const int32_t ln = lane_id_here();
+    const bool tail = kt + kKeys > S;        // rows past the end repeat the last row (masked)
     uint16_t* kdst = kslot(B);
     uint16_t* vdst = vslot(B);
 #pragma unroll
     for (int i = 0; i < kWaveLoads; ++i) {
       if (kOps % kWaves != 0 && wave * kWaveLoads + i >= kOps) break;   // uniform per wave
       const int32_t base = (wave * kWaveLoads + i) * 64;     // first physical chunk of this op
-      const int32_t pc = base + ln;
-      int32_t row = pc / kRowChunks;
-      const int32_t lc = (pc % kRowChunks) ^ swz(row);        // logical chunk held at pc
-      row = min(row, last_row);
-      const uint32_t off = static_cast<uint32_t>(row) * row_pitch + static_cast<uint32_t>(lc) * 16u;
+      uint32_t off = doff[i];
+      if (tail) {
+        const int32_t ln = lane_id_here();
+        const int32_t pc = base + ln;
+        const int32_t row = pc / kRowChunks;
+        const int32_t lc = (pc % kRowChunks) ^ swz<D>(row);
+        off = static_cast<uint32_t>(min(row, S - 1 - kt)) * row_pitch + static_cast<uint32_t>(lc) * 16u;
+      }
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt_base + off),
                                        (__attribute__((address_space(3))) void*)(kdst + base * 8), 16, 0, 0);
       if (!KEQV) {
@@ -297,7 +319,7 @@ void prefill_kernel(PrefillParams p) {
       const int32_t ln = lane_id_here();
       const int32_t jj = ln & 31;
       const int32_t hh = ln >> 5;
-      const int32_t sw = swz(jj);
+      const int32_t sw = swz<D>(jj);
 #pragma unroll
       for (int ds = 0; ds < kDS; ++ds) {
         const int32_t lc = (dlo >> 3) + ds * 2 + hh;
@@ -326,18 +348,20 @@ void prefill_kernel(PrefillParams p) {
     }
 
     if (need) {
-      // Logits in the exp2 domain; lane holds keys kt + (r/4)*8 + h*4 + r%4.
+      // Logits: lane holds keys kt + (r/4)*8 + h*4 + r%4.  Without a cap the
+      // scale is folded into the exponent, exp2(s*scale*log2e - m), and the
+      // max is taken on the raw scores (the scale is positive).
       float x[16];
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float t;
         if (CAP) {
-          // cap * tanh(s*scale/cap) = cap - 2*cap / (exp(2*s*scale/cap) + 1)
+          // cap * tanh(s*scale/cap) = cap - 2*cap / (exp(2*s*scale/cap) + 1), in log2 units
           const float e = __builtin_amdgcn_exp2f(sacc[r] * p.cap_in2);
           t = fmaf(-2.f * p.cap_log2, __builtin_amdgcn_rcpf(e + 1.f), p.cap_log2);
         } else {
-          t = sacc[r] * p.scale_log2;
+          t = sacc[r];
         }
         if (!full) {
           // allowed iff key_lo <= key <= pos (branch-free; key_lo from the window)
@@ -349,6 +373,7 @@ void prefill_kernel(PrefillParams p) {
         mx = fmaxf(mx, t);
       }
       mx = xhalf_max(mx);
+      if (!CAP) mx *= p.scale_log2;
       // The running max only moves when the tile exceeds it by more than
       // kTau (log2 units): probabilities then stay <= 2^kTau and the output
       // rescale, a pass over every accumulator, is rare.
@@ -363,16 +388,23 @@ void prefill_kernel(PrefillParams p) {
       }
       m_run = m_next;
 
+      // Probabilities rounded to bf16; the row sum adds the same rounded
+      // values (v_dot2_f32_bf16 against (1, 1)).
       uint32_t pk[8];
-      float ls = 0.f;
+      const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float e0 = __builtin_amdgcn_exp2f(x[2 * r] - m_use);
-        const float e1 = __builtin_amdgcn_exp2f(x[2 * r + 1] - m_use);
+        float e0, e1;
+        if (CAP) {
+          e0 = __builtin_amdgcn_exp2f(x[2 * r] - m_use);
+          e1 = __builtin_amdgcn_exp2f(x[2 * r + 1] - m_use);
+        } else {
+          e0 = __builtin_amdgcn_exp2f(fmaf(x[2 * r], p.scale_log2, -m_use));
+          e1 = __builtin_amdgcn_exp2f(fmaf(x[2 * r + 1], p.scale_log2, -m_use));
+        }
         pk[r] = pack_bf16x2(e0, e1);
-        ls += lo_bf16(pk[r]) + hi_bf16(pk[r]);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r]), ones, l_run, false);
       }
-      l_run += ls;
 
       // O^T += V^T . P^T, two 16-key halves per tile.
       const int32_t ln = lane_id_here();
@@ -384,8 +416,8 @@ void prefill_kernel(PrefillParams p) {
         const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
         const int32_t r0 = 16 * t + 4 * (ln >> 5) + (li16 >> 2);
         const int32_t r1 = r0 + 8;
-        const int32_t sw0 = swz(r0);
-        const int32_t sw1 = swz(r1);
+        const int32_t sw0 = swz<D>(r0);
+        const int32_t sw1 = swz<D>(r1);
         const int32_t half8 = (li16 & 1) * 4;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
