@@ -7,16 +7,14 @@
 // group; a second kernel merges the partials of each (sequence, head) in a
 // fixed order (log-sum-exp combine).
 //
-// Inside a workgroup each of the 4 waves streams 32-key tiles of the chunk
-// (tiles interleaved across waves):
-//   * K rows are loaded from HBM straight into the A-operand layout of
-//     v_mfma_f32_16x16x32_bf16 (16-byte loads, lane = key row);
-//   * S^T[16 keys x 16 cols] = K . Q^T with the g heads as columns (padded to
-//     16), so each lane owns one head and the softmax reductions are over the
-//     four lanes that share it;
-//   * the value rows (the same registers with keys-as-values) are written to
-//     the wave's own LDS tile and read back transposed (ds_read_b64_tr_b16) as
-//     the A operand of O^T += V^T . P^T.
+// Inside a workgroup (2 waves) tiles of 16 cache rows stream HBM -> LDS with
+// the direct-to-LDS loads into two slots per team (one tile in flight while
+// the other is computed), rows XOR-swizzled by 16-byte chunk:
+//   * S^T[16 keys x 16 cols] = K . Q^T (v_mfma_f32_16x16x32_bf16) with the g
+//     heads as columns (padded to 16), so each lane owns one head and the
+//     softmax reductions are over the four lanes that share it;
+//   * O^T += V^T . P^T with V^T read transposed from the row-major tile
+//     (ds_read_b64_tr_b16); with keys-as-values the one tile is both.
 // Cache rows outside the sequence's range are never loaded.
 //
 // Sources: generate() decoding over cached keys and values (Gemma 4 page, API;
@@ -29,10 +27,7 @@ namespace ga {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kKeys = 32;   // keys per wave tile
-constexpr int kPad = 8;
+constexpr int kTK = 16;     // keys per wave tile
 
 struct DecodeParams {
   const uint16_t* q;
@@ -56,15 +51,60 @@ __device__ __forceinline__ void seq_range(const DecodeParams& p, int32_t b, int3
   lo = c - span;
 }
 
-template <int D, int G, bool KEQV, bool CAP>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
-  constexpr int kDS = D / 32;        // k-steps of QK^T (16x16x32)
-  constexpr int kDB = D / 16;        // 16-row blocks of O^T
-  constexpr int kLd = D + kPad;
-  constexpr int kTileElems = kKeys * kLd;
-  static_assert(G <= 16, "at most 16 query heads per KV head");
+// XOR pattern of the 16-byte chunks of LDS row r (a 16-lane ds_read_b128
+// phase reads 16 consecutive rows at one chunk; a transpose read reads 4
+// rows x 4 chunks per half-wave).  See the prefill kernel for the derivation.
+template <int D>
+__device__ __forceinline__ int32_t dswz(int32_t r) {
+  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+// The lane index, hidden from loop-invariant code motion, so lane-derived
+// offsets are recomputed per tile instead of held in registers.
+__device__ __forceinline__ int32_t lane_here() {
+  int32_t l = static_cast<int32_t>(threadIdx.x);
+  asm volatile("" : "+v"(l));
+  return l & 63;
+}
+
+// Workgroup = 2 waves.  Head width 512: the two waves are one team that
+// streams the same tiles; both compute the full scores (QK^T is a third of the
+// matrix work) and each accumulates O^T for its half of D, so neither holds
+// more than 128 accumulator/query registers.  Narrower heads: each wave is a
+// team of its own and streams its own tiles.  Each team owns two LDS slots.
+template <int D>
+struct DecodeShape {
+  static constexpr int kWaves = 2;
+  static constexpr int kTeam = D > 256 ? 2 : 1;       // waves per team
+  static constexpr int kTeams = kWaves / kTeam;
+};
+
+template <int D, int G, bool KEQV, bool CAP>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(DecodeParams p) {
+  using Sh = DecodeShape<D>;
+  constexpr int kTeam = Sh::kTeam;
+  constexpr int kTeams = Sh::kTeams;
+  constexpr int kDW = D / kTeam;     // D slice of one wave's accumulators
+  constexpr int kDS = D / 32;        // k-steps of QK^T (16x16x32)
+  constexpr int kDB = kDW / 16;      // 16-row blocks of this wave's O^T
+  constexpr int kRowChunks = D / 8;  // 16-byte chunks per cache row
+  constexpr int kSlotElems = kTK * D;
+  constexpr int kOps = kTK * kRowChunks / 64;   // 1 KB copy ops per tensor per tile
+  constexpr int kWaveOps = kOps / kTeam;        // issued by each wave of a team
+  constexpr int kOpsPerTile = kWaveOps * (KEQV ? 1 : 2);
+  static_assert(G <= 16, "at most 16 query heads per KV head");
+  static_assert(kTK * kRowChunks % (64 * kTeam) == 0, "tile must split into whole 1 KB ops");
+
+  // Two slots per team, one LDS array per slot (so reads of one slot are not
+  // ordered behind the copies landing in the other).
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[kTeams * kSlotElems];
+  __shared__ __attribute__((aligned(16))) uint16_t ks1[kTeams * kSlotElems];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[KEQV ? 8 : kTeams * kSlotElems];
+  __shared__ __attribute__((aligned(16))) uint16_t vs1[KEQV ? 8 : kTeams * kSlotElems];
+  __shared__ float m_w[2][16];
+  __shared__ float l_w[2][16];
+  static_assert(kTeams == 1 || kSlotElems * kTeams * 2 >= 16 * D * 4, "merge buffer reuses slot 0");
 
   const int32_t split = blockIdx.x;
   const int32_t kvh = blockIdx.y;
@@ -74,13 +114,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int32_t s_lo = lo + split * p.chunk;
   if (s_lo >= ctx) return;   // this split is empty for the sequence (uniform)
   const int32_t s_hi = min(ctx, s_lo + p.chunk);
+  const int32_t n_t = (s_hi - s_lo + kTK - 1) / kTK;
 
   const int32_t tid = threadIdx.x;
-  const int32_t wave = tid >> 6;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t team = wave / kTeam;
+  const int32_t member = wave % kTeam;
+  const int32_t dlo = member * kDW;
   const int32_t lane = tid & 63;
   const int32_t col = lane & 15;     // query head within the group (valid if < G)
   const int32_t grp = lane >> 4;     // 16-lane group
-  uint16_t* tile = smem + wave * kTileElems;
 
   // Q^T operand: lane holds d = ds*32 + grp*8 + [0, 8) of head `col`.
   bf16x8 qf[kDS];
@@ -99,140 +142,173 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  const int64_t row_stride = static_cast<int64_t>(p.hkv) * D;
-  const uint16_t* kbase = p.kc + (static_cast<int64_t>(b) * p.max_ctx * p.hkv + kvh) * D;
-  const uint16_t* vbase = KEQV ? kbase : p.vc + (static_cast<int64_t>(b) * p.max_ctx * p.hkv + kvh) * D;
+  const uint32_t row_pitch = static_cast<uint32_t>(p.hkv) * D * 2;    // bytes between cache rows
+  const char* kseq = reinterpret_cast<const char*>(p.kc) + (static_cast<int64_t>(b) * p.max_ctx * p.hkv + kvh) * D * 2;
+  const char* vseq = KEQV ? kseq : reinterpret_cast<const char*>(p.vc) + (static_cast<int64_t>(b) * p.max_ctx * p.hkv + kvh) * D * 2;
 
-  for (int32_t kt = s_lo + wave * kKeys; kt < s_hi; kt += kWaves * kKeys) {
-    // K rows in A layout (lane: key kt + 16*kk + col, d = ds*32 + grp*8).
-    bf16x8 ka[2][kDS];
-    bf16x8 va[KEQV ? 1 : 2][KEQV ? 1 : kDS];
+  // Copy this wave's share of tile ti (keys s_lo + 16*ti ...) into a slot.
+  // Rows past s_hi repeat row s_hi - 1, so no row outside the sequence's
+  // range is read.
+  auto copy_tile = [&](int32_t ti, uint16_t* kdst, uint16_t* vdst) {
+    const int32_t k0 = s_lo + ti * kTK;
+    const int32_t last = s_hi - 1 - k0;
+    const char* kb = kseq + static_cast<int64_t>(k0) * row_pitch;
+    const char* vb = vseq + static_cast<int64_t>(k0) * row_pitch;
+    const int32_t ln = lane_here();
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int32_t key = kt + 16 * kk + col;
-      const bool ok = key < s_hi;
-      const uint16_t* kr = kbase + static_cast<int64_t>(key) * row_stride + grp * 8;
-      const uint16_t* vr = vbase + static_cast<int64_t>(key) * row_stride + grp * 8;
-#pragma unroll
-      for (int ds = 0; ds < kDS; ++ds) {
-        ka[kk][ds] = ok ? *reinterpret_cast<const bf16x8*>(kr + ds * 32) : bf16x8{};
-        if (!KEQV) va[kk][ds] = ok ? *reinterpret_cast<const bf16x8*>(vr + ds * 32) : bf16x8{};
+    for (int i = 0; i < kWaveOps; ++i) {
+      const int32_t op = member * kWaveOps + i;
+      const int32_t pc = op * 64 + ln;
+      const int32_t row = pc / kRowChunks;
+      const int32_t lc = (pc % kRowChunks) ^ dswz<D>(row);
+      const uint32_t off = static_cast<uint32_t>(min(row, last)) * row_pitch + static_cast<uint32_t>(lc) * 16u;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + off),
+                                       (__attribute__((address_space(3))) void*)(kdst + op * 512), 16, 0, 0);
+      if (!KEQV) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + off),
+                                         (__attribute__((address_space(3))) void*)(vdst + op * 512), 16, 0, 0);
       }
     }
-    // Value rows into this wave's LDS tile, row-major [key][d].
+  };
+
+  // One tile from slot (kb, vb).
+  auto compute = [&](int32_t ti, const uint16_t* kb, const uint16_t* vb) {
+    const int32_t k0 = s_lo + ti * kTK;
+    // S^T[16 keys x 16 heads] = K . Q^T; lane: key row li16, d chunk ds*4 + lgrp.
+    f32x4 sacc = f32x4{};
+    const int32_t ln = lane_here();
+    const int32_t li16 = ln & 15;
+    const int32_t lgrp = ln >> 4;
+    const int32_t sw = dswz<D>(li16);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int ds = 0; ds < kDS; ++ds) {
-        const bf16x8 vv = KEQV ? ka[kk][ds] : va[KEQV ? 0 : kk][KEQV ? 0 : ds];
-        *reinterpret_cast<bf16x8*>(&tile[(16 * kk + col) * kLd + ds * 32 + grp * 8]) = vv;
-      }
+    for (int ds = 0; ds < kDS; ++ds) {
+      const int32_t lc = ds * 4 + lgrp;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[li16 * D + ((lc ^ sw) << 3)]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ds], sacc, 0, 0, 0);
     }
-    // S^T for the two 16-key halves.
-    f32x4 sacc[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      sacc[kk] = f32x4{};
-#pragma unroll
-      for (int ds = 0; ds < kDS; ++ds) {
-        sacc[kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk][ds], qf[ds], sacc[kk], 0, 0, 0);
-      }
-    }
-    // Lane holds keys kt + 16*kk + grp*4 + r for head `col`.
-    float x[8];
+    // Lane holds keys k0 + grp*4 + r for head `col`.
+    float x[4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float t;
-        if (CAP) {
-          const float e = __builtin_amdgcn_exp2f(sacc[kk][r] * p.cap_in2);
-          t = fmaf(-2.f * p.cap_log2, __builtin_amdgcn_rcpf(e + 1.f), p.cap_log2);
-        } else {
-          t = sacc[kk][r] * p.scale_log2;
-        }
-        const int32_t key = kt + 16 * kk + grp * 4 + r;
-        t = key < s_hi ? t : -INFINITY;
-        x[kk * 4 + r] = t;
-        mx = fmaxf(mx, t);
+    for (int r = 0; r < 4; ++r) {
+      float t;
+      if (CAP) {
+        const float e = __builtin_amdgcn_exp2f(sacc[r] * p.cap_in2);
+        t = fmaf(-2.f * p.cap_log2, __builtin_amdgcn_rcpf(e + 1.f), p.cap_log2);
+      } else {
+        t = sacc[r] * p.scale_log2;
       }
+      t = (k0 + grp * 4 + r < s_hi) ? t : -INFINITY;
+      x[r] = t;
+      mx = fmaxf(mx, t);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    uint32_t pk[4];
-    float ls = 0.f;
+    const bool grow = mx > m_run + 8.f;          // lazily updated running max
+    const float m_next = grow ? mx : m_run;
+    const float m_use = m_next == -INFINITY ? 0.f : m_next;
+    if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pk[r] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2 * r] - m_use), __builtin_amdgcn_exp2f(x[2 * r + 1] - m_use));
-      ls += lo_bf16(pk[r]) + hi_bf16(pk[r]);
+      for (int db = 0; db < kDB; ++db) o[db] *= alpha;
     }
-    l_run = fmaf(l_run, alpha, ls);
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) o[db] *= alpha;
-    // P^T operand: slots 0-3 = keys grp*4 + [0,4), slots 4-7 = keys 16 + grp*4 + [0,4).
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-    const int32_t i16 = lane & 15;
-    const int32_t r0 = grp * 4 + (i16 >> 2);
+    m_run = m_next;
+    const uint32_t pk0 = pack_bf16x2(__builtin_amdgcn_exp2f(x[0] - m_use), __builtin_amdgcn_exp2f(x[1] - m_use));
+    const uint32_t pk1 = pack_bf16x2(__builtin_amdgcn_exp2f(x[2] - m_use), __builtin_amdgcn_exp2f(x[3] - m_use));
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk0), ones, l_run, false);
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk1), ones, l_run, false);
+    // P^T operand: slots 0-3 = keys grp*4 + [0,4), slots 4-7 empty.
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk0, pk1, 0u, 0u});
+    // V^T operand (transpose read of rows grp*4 + [0,4) at d = dlo + db*16 + li16).
+    const int32_t r0 = lgrp * 4 + (li16 >> 2);
+    const int32_t sw0 = dswz<D>(r0);
+    const int32_t half8 = (li16 & 1) * 4;
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
-      const int32_t cc = db * 16 + 4 * (i16 & 3);
-      const i16x4 a0 = lds_read_tr16(&tile[r0 * kLd + cc]);
-      const i16x4 a1 = lds_read_tr16(&tile[(r0 + 16) * kLd + cc]);
-      const bf16x8 aop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+      const int32_t lc = (dlo >> 3) + db * 2 + ((li16 & 3) >> 1);
+      const i16x4 a0 = lds_read_tr16(&vb[r0 * D + ((lc ^ sw0) << 3) + half8]);
+      const bf16x8 aop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, i16x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pb, o[db], 0, 0, 0);
     }
-  }
+  };
 
-  // ---- merge the 4 waves' partials of this chunk ----
+  // The team's tiles: ti = team, team + kTeams, ...; alternate slots.
+  uint16_t* k0s = ks0 + team * kSlotElems;
+  uint16_t* k1s = ks1 + team * kSlotElems;
+  uint16_t* v0s = KEQV ? k0s : vs0 + team * kSlotElems;
+  uint16_t* v1s = KEQV ? k1s : vs1 + team * kSlotElems;
+  // A team of two shares its slots: a barrier publishes both halves of a
+  // tile and fences the slot being refilled (every wave runs the same trips).
+  auto team_sync = [&]() {
+    if constexpr (kTeam > 1) __syncthreads();
+  };
+  int32_t ti = team;
+  if (ti < n_t) copy_tile(ti, k0s, v0s);
+  while (ti < n_t) {
+    const int32_t tn = ti + kTeams;
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));   // this wave's copies of tile ti
+    team_sync();
+    if (tn < n_t) copy_tile(tn, k1s, v1s);                 // in flight during compute
+    compute(ti, k0s, v0s);
+    ti = tn;
+    if (ti >= n_t) break;
+    const int32_t tn2 = ti + kTeams;
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+    team_sync();
+    if (tn2 < n_t) copy_tile(tn2, k0s, v0s);
+    compute(ti, k1s, v1s);
+    ti = tn2;
+  }
+  (void)kOpsPerTile;
+
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  __shared__ float m_w[kWaves][16];
-  __shared__ float l_w[kWaves][16];
-  __syncthreads();   // every wave is done with its tile; LDS reused below
-  if (grp == 0) {
-    m_w[wave][col] = m_run;
-    l_w[wave][col] = l_run;
-  }
-  __syncthreads();
-  float m_all = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) m_all = fmaxf(m_all, m_w[w][col]);
-  const float m_ref = m_all == -INFINITY ? 0.f : m_all;
-  const float f = __builtin_amdgcn_exp2f(m_run - m_ref);
-  float* obuf = reinterpret_cast<float*>(smem);   // [16 cols][D] fp32
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+  const int64_t part = (static_cast<int64_t>(b) * p.hq + kvh * G) * p.n_split + split;
+  if constexpr (kTeams == 1) {
+    // One team: both waves hold the same (m, l) and disjoint halves of D.
+    if (col < G) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float* dst = obuf + col * D + db * 16 + grp * 4 + r;
-          const float v = o[db][r] * f;
-          *dst = (w == 0) ? v : *dst + v;
-        }
+        float* dst = p.ws_o + (part + static_cast<int64_t>(col) * p.n_split) * D + dlo + db * 16 + grp * 4;
+        *reinterpret_cast<f32x4*>(dst) = o[db];
+      }
+      if (member == 0 && grp == 0) {
+        p.ws_m[part + static_cast<int64_t>(col) * p.n_split] = m_run;
+        p.ws_l[part + static_cast<int64_t>(col) * p.n_split] = l_run;
       }
     }
-    __syncthreads();
-  }
-  const int64_t part = (static_cast<int64_t>(b) * p.hq + kvh * G) * p.n_split + split;
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int32_t cc = i / D;
-    const int32_t d = i % D;
-    p.ws_o[(part + static_cast<int64_t>(cc) * p.n_split) * D + d] = obuf[cc * D + d];
-  }
-  if (tid < G) {
-    float l_sum = 0.f;
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = m_w[w][tid];
-      l_sum += l_w[w][tid] * __builtin_amdgcn_exp2f(mw - (m_all == -INFINITY ? 0.f : m_all));
+  } else {
+    // Two teams (waves) over different keys: merge through LDS.
+    __syncthreads();   // both waves are done with their slots; LDS reused below
+    if (grp == 0) {
+      m_w[wave][col] = m_run;
+      l_w[wave][col] = l_run;
     }
-    p.ws_m[part + static_cast<int64_t>(tid) * p.n_split] = m_all;
-    p.ws_l[part + static_cast<int64_t>(tid) * p.n_split] = l_sum;
+    __syncthreads();
+    const float m_all = fmaxf(m_w[0][col], m_w[1][col]);
+    const float m_ref = m_all == -INFINITY ? 0.f : m_all;
+    const float f = __builtin_amdgcn_exp2f(m_run - m_ref);
+    float* obuf = reinterpret_cast<float*>(ks0);   // [16 heads][D] fp32
+    if (wave == 0) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) *reinterpret_cast<f32x4*>(obuf + col * D + db * 16 + grp * 4) = o[db] * f;
+    }
+    __syncthreads();
+    if (wave == 1 && col < G) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const f32x4 prev = *reinterpret_cast<const f32x4*>(obuf + col * D + db * 16 + grp * 4);
+        float* dst = p.ws_o + (part + static_cast<int64_t>(col) * p.n_split) * D + db * 16 + grp * 4;
+        *reinterpret_cast<f32x4*>(dst) = prev + o[db] * f;
+      }
+      if (grp == 0) {
+        p.ws_m[part + static_cast<int64_t>(col) * p.n_split] = m_all;
+        p.ws_l[part + static_cast<int64_t>(col) * p.n_split] =
+            l_w[0][col] * __builtin_amdgcn_exp2f(m_w[0][col] - m_ref) + l_w[1][col] * __builtin_amdgcn_exp2f(m_w[1][col] - m_ref);
+      }
+    }
   }
 }
 
@@ -277,17 +353,9 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
 
 template <int D, int G, bool KEQV, bool CAP>
 hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t stream) {
-  constexpr int kLd = D + kPad;
-  size_t lds = static_cast<size_t>(kWaves) * kKeys * kLd * sizeof(uint16_t);
-  const size_t merge = static_cast<size_t>(16) * D * sizeof(float);
-  if (merge > lds) lds = merge;
-  auto kfn = decode_split_kernel<D, G, KEQV, CAP>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
-  if (e != hipSuccess) return e;
   const dim3 grid(static_cast<uint32_t>(a.n_split), static_cast<uint32_t>(a.hkv), static_cast<uint32_t>(a.batch));
-  hipLaunchKernelGGL(kfn, grid, dim3(kThreads), lds, stream, prm);
-  e = hipGetLastError();
+  hipLaunchKernelGGL((decode_split_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D>::kWaves * 64), 0, stream, prm);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(static_cast<uint32_t>(a.hq), static_cast<uint32_t>(a.batch)),
                      dim3(64), 0, stream, prm);

@@ -84,6 +84,9 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
   if (want < 1) want = 1;
   long long chunk = 256;
   while (chunk < 4096 && chunk * want < p.span_max) chunk *= 2;
+  // With enough units to fill the chip, longer chunks amortise each
+  // workgroup's start-up (first copy latency, merge, partial write-back).
+  if (units >= 256 && chunk < 1024) chunk = 1024;
   p.chunk = static_cast<int32_t>(chunk);
   // Splits are relative to the first key a sequence reads, so span/chunk
   // chunks (rounded up) cover every sequence.
