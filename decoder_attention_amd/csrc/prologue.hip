@@ -1,11 +1,15 @@
 // Fused QK-norm + dual-base partial rotary prologue (gfx950).
 //
-// One workgroup per token (b, s).  The token's rotary table cos/sin(p * w_i)
-// is built once in LDS (angle formed and reduced modulo 2*pi in fp64, then
-// fp32 sincos) and shared by every q and k head of that token.  Each head row
-// of width D is handled by D/8 lanes holding 8 contiguous bf16 (one 16-byte
-// load); the RMS reduction is a butterfly inside those lanes; the rotate-half
-// partner element comes through an LDS copy of the normalised row.
+// One workgroup per group of kTok consecutive tokens (flattened over batch and
+// sequence).  The rotary frequencies w_i = theta^(-2i/r) are formed once per
+// workgroup in fp64, then each token's cos/sin(p * w_i) table (angle reduced
+// modulo 2*pi in fp64, fp32 sincos) goes to LDS; the row loads are issued
+// before the tables are built so their latency overlaps it.  Each head row of
+// width D is handled by D/8 lanes holding 8 contiguous bf16 (one 16-byte
+// load); the RMS reduction is a butterfly inside those lanes.  The rotate-half
+// partner of element d (d +- r/2) sits r/16 lanes away at the same slot, so
+// when r/16 is a power of two it is one lane shuffle (lane ^ r/16); other
+// rotary widths go through an LDS copy of the normalised row.
 //
 // Sources: RMSNorm QK-norm (google-gemma-4 atlas summary; weight used as w on
 // Gemma 4, "Plain-weight RMSNorm", and as 1 + w on earlier Gemma), partial
@@ -19,103 +23,154 @@ namespace ga {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kTok = 4;                 // tokens per workgroup
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
-__global__ __launch_bounds__(kThreads) void qk_prologue_kernel(
-    const uint16_t* q_in, const uint16_t* k_in,
-    uint16_t* q_out, uint16_t* k_out,
-    const float* __restrict__ qw, const float* __restrict__ kw,
-    const int32_t* __restrict__ pos0, int32_t seq, int32_t hq, int32_t hkv, int32_t dim,
-    int32_t rotary_dim, double theta, float eps, float offset) {
-  __shared__ float2 cs_tab[256];
-  __shared__ float rowbuf[kThreads * 8];
+struct ProParams {
+  const uint16_t* q_in;
+  const uint16_t* k_in;
+  uint16_t* q_out;
+  uint16_t* k_out;
+  const float* qw;
+  const float* kw;
+  const int32_t* pos0;
+  int64_t tokens;
+  int32_t seq, hq, hkv, dim, rotary_dim;
+  double theta;
+  float eps, offset;
+};
 
-  const int64_t token = blockIdx.x;
-  const int32_t b = static_cast<int32_t>(token / seq);
-  const int32_t s = static_cast<int32_t>(token % seq);
+// SHFL: the partner is lane ^ (r/16) (r/16 a power of two, r <= D); else LDS.
+template <bool SHFL>
+__global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
+  __shared__ double omega[256];
+  __shared__ float2 cs_tab[kTok][256];
+  __shared__ float rowbuf[SHFL ? 1 : kThreads * 8];
+
   const int32_t tid = threadIdx.x;
-  const int32_t half = rotary_dim >> 1;
-
-  const int64_t pos = static_cast<int64_t>(pos0 ? pos0[b] : 0) + s;
-  for (int32_t i = tid; i < half; i += kThreads) {
-    const double w = pow(theta, -2.0 * i / rotary_dim);
-    double ang = fmod(static_cast<double>(pos) * w, kTwoPi);
-    if (ang < 0) ang += kTwoPi;
-    float sn, cn;
-    sincosf(static_cast<float>(ang), &sn, &cn);
-    cs_tab[i] = make_float2(cn, sn);
-  }
-  __syncthreads();
-
+  const int32_t half = p.rotary_dim >> 1;
+  const int32_t dim = p.dim;
   const int32_t tpr = dim >> 3;                 // lanes per row (power of two <= 64)
   const int32_t rows_per_pass = kThreads / tpr;
-  const int32_t rows = hq + (k_in ? hkv : 0);
+  const int32_t heads = p.hq + (p.k_in ? p.hkv : 0);
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kTok;
+  const int32_t rows = kTok * heads;
   const int32_t sub = tid / tpr;
   const int32_t lane = tid % tpr;
   const int32_t d0 = lane * 8;
 
+  // Row r of this workgroup: token tok0 + r / heads, head r % heads.
+  auto row_ptrs = [&](int32_t row, const uint16_t*& src, uint16_t*& dst, const float*& w) -> bool {
+    const int32_t tt = row / heads;
+    const int32_t hh = row % heads;
+    const int64_t token = tok0 + tt;
+    if (row >= rows || token >= p.tokens) return false;
+    if (hh < p.hq) {
+      const int64_t off = (token * p.hq + hh) * dim + d0;
+      src = p.q_in + off;
+      dst = p.q_out + off;
+      w = p.qw;
+    } else {
+      const int64_t off = (token * p.hkv + (hh - p.hq)) * dim + d0;
+      src = p.k_in + off;
+      dst = p.k_out + off;
+      w = p.kw;
+    }
+    return true;
+  };
+
+  // Issue the first pass's row load before building the tables.
+  u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+  {
+    const uint16_t* src;
+    uint16_t* dst;
+    const float* w;
+    if (row_ptrs(sub, src, dst, w)) raw = *reinterpret_cast<const u32x4*>(src);
+  }
+
+  for (int32_t i = tid; i < half; i += kThreads) omega[i] = pow(p.theta, -2.0 * i / p.rotary_dim);
+  __syncthreads();
+  for (int32_t e = tid; e < kTok * half; e += kThreads) {
+    const int32_t tt = e / half;
+    const int32_t i = e % half;
+    const int64_t token = tok0 + tt;
+    float sn = 0.f, cn = 1.f;
+    if (token < p.tokens) {
+      const int32_t b = static_cast<int32_t>(token / p.seq);
+      const int32_t s = static_cast<int32_t>(token % p.seq);
+      const int64_t pos = static_cast<int64_t>(p.pos0 ? p.pos0[b] : 0) + s;
+      double ang = fmod(static_cast<double>(pos) * omega[i], kTwoPi);
+      if (ang < 0) ang += kTwoPi;
+      sincosf(static_cast<float>(ang), &sn, &cn);
+    }
+    cs_tab[tt][i] = make_float2(cn, sn);
+  }
+  __syncthreads();
+
+  const int32_t pmask = p.rotary_dim >> 4;   // partner lane distance (SHFL)
   for (int32_t row0 = 0; row0 < rows; row0 += rows_per_pass) {
     const int32_t row = row0 + sub;
-    const bool active = row < rows;
-    const bool is_q = row < hq;
     const uint16_t* src = nullptr;
     uint16_t* dst = nullptr;
     const float* w = nullptr;
-    if (active) {
-      if (is_q) {
-        const int64_t off = (token * hq + row) * dim + d0;
-        src = q_in + off;
-        dst = q_out + off;
-        w = qw;
-      } else {
-        const int64_t off = (token * hkv + (row - hq)) * dim + d0;
-        src = k_in + off;
-        dst = k_out + off;
-        w = kw;
-      }
+    const bool active = row_ptrs(row, src, dst, w);
+    // prefetch the next pass's row
+    u32x4 next = u32x4{0u, 0u, 0u, 0u};
+    if (row0 + rows_per_pass < rows) {
+      const uint16_t* s2;
+      uint16_t* d2;
+      const float* w2;
+      if (row_ptrs(row + rows_per_pass, s2, d2, w2)) next = *reinterpret_cast<const u32x4*>(s2);
     }
     float x[8];
-    if (active) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = lo_bf16(raw[e]);
-        x[2 * e + 1] = hi_bf16(raw[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = lo_bf16(raw[e]);
+      x[2 * e + 1] = hi_bf16(raw[e]);
     }
-    // RMSNorm (only when this side has a weight); the flag is uniform per row.
+    // RMSNorm (only when this side has a weight).
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
     for (int m = tpr >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
     if (active && w) {
-      const float inv = 1.0f / sqrtf(ss / static_cast<float>(dim) + eps);
+      const float inv = 1.0f / sqrtf(ss / static_cast<float>(dim) + p.eps);
       const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + d0);
       const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + d0 + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = x[e] * inv * (w0[e] + offset);
-        x[e + 4] = x[e + 4] * inv * (w1[e] + offset);
+        x[e] = x[e] * inv * (w0[e] + p.offset);
+        x[e + 4] = x[e + 4] * inv * (w1[e] + p.offset);
       }
     }
-    float* rb = rowbuf + sub * dim;
+    float partner[8];
+    if constexpr (SHFL) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rb[d0 + e] = x[e];
-    __syncthreads();
+      for (int e = 0; e < 8; ++e) partner[e] = __shfl_xor(x[e], pmask, 64);
+    } else {
+      float* rb = rowbuf + sub * dim;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rb[d0 + e] = x[e];
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int32_t d = d0 + e;
+        partner[e] = d < half ? rb[d + half] : (d < p.rotary_dim ? rb[d - half] : 0.f);
+      }
+      __syncthreads();
+    }
     if (active) {
+      const int32_t tt = row / heads;
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int32_t d = d0 + e;
         if (d < half) {
-          const float2 c = cs_tab[d];
-          y[e] = x[e] * c.x - rb[d + half] * c.y;
-        } else if (d < rotary_dim) {
-          const float2 c = cs_tab[d - half];
-          y[e] = x[e] * c.x + rb[d - half] * c.y;
+          const float2 c = cs_tab[tt][d];
+          y[e] = x[e] * c.x - partner[e] * c.y;
+        } else if (d < p.rotary_dim) {
+          const float2 c = cs_tab[tt][d - half];
+          y[e] = x[e] * c.x + partner[e] * c.y;
         } else {
           y[e] = x[e];
         }
@@ -125,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(
       for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
       *reinterpret_cast<u32x4*>(dst) = o;
     }
-    __syncthreads();
+    raw = next;
   }
 }
 
@@ -134,10 +189,31 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(
 hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream) {
   const int64_t tokens = static_cast<int64_t>(a.batch) * a.seq;
   if (tokens == 0) return hipSuccess;
-  hipLaunchKernelGGL(qk_prologue_kernel, dim3(static_cast<uint32_t>(tokens)), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(a.q_in), static_cast<const uint16_t*>(a.k_in),
-                     static_cast<uint16_t*>(a.q_out), static_cast<uint16_t*>(a.k_out), a.q_norm_w, a.k_norm_w,
-                     a.pos0, a.seq, a.hq, a.hkv, a.dim, a.rotary_dim, a.theta, a.eps, a.offset);
+  ProParams p;
+  p.q_in = static_cast<const uint16_t*>(a.q_in);
+  p.k_in = static_cast<const uint16_t*>(a.k_in);
+  p.q_out = static_cast<uint16_t*>(a.q_out);
+  p.k_out = static_cast<uint16_t*>(a.k_out);
+  p.qw = a.q_norm_w;
+  p.kw = a.k_norm_w;
+  p.pos0 = a.pos0;
+  p.tokens = tokens;
+  p.seq = a.seq;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.dim = a.dim;
+  p.rotary_dim = a.rotary_dim;
+  p.theta = a.theta;
+  p.eps = a.eps;
+  p.offset = a.offset;
+  const int64_t blocks = (tokens + kTok - 1) / kTok;
+  const int32_t r16 = a.rotary_dim >> 4;
+  const bool shfl = a.rotary_dim % 16 == 0 && r16 > 0 && (r16 & (r16 - 1)) == 0 && a.rotary_dim <= a.dim;
+  if (shfl || a.rotary_dim == 0) {
+    hipLaunchKernelGGL(qk_prologue_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(qk_prologue_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
