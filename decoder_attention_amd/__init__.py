@@ -136,6 +136,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gemma_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.gemma_attn_decode.argtypes = [cfgp, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
     lib.gemma_attn_decode.restype = ctypes.c_int
+    lib.gemma_attn_decode_multi.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                            ctypes.c_size_t, _VP]
+    lib.gemma_attn_decode_multi.restype = ctypes.c_int
+    lib.gemma_attn_decode_multi_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
+    lib.gemma_attn_decode_multi_workspace_size.restype = ctypes.c_size_t
+    lib.gemma_qk_prologue_cache.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.gemma_qk_prologue_cache.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -283,3 +290,70 @@ def attn_decode(cfg, layer_idx, q, k_cache, v_cache, ctx_len, out=None, lse=None
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "gemma_attn_decode")
     return (out, lse) if lse is not None else out
+
+
+def decode_multi_workspace_size(cfg, layer_idx, batch, q_len, max_ctx) -> int:
+    cfg = Config.from_any(cfg)
+    return int(load().gemma_attn_decode_multi_workspace_size(ctypes.byref(cfg.to_c()), int(layer_idx), int(batch),
+                                                             int(q_len), int(max_ctx)))
+
+
+def attn_decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len, out=None, lse=None, want_lse=False,
+                      workspace=None, stream=None):
+    """gemma_attn_decode_multi; q [B,L,Hq,D]; returns out [B,L,Hq,D], or (out, lse [B,Hq,L])."""
+    import torch
+
+    cfg = Config.from_any(cfg)
+    L = resolve_layer(cfg, layer_idx)
+    B, Lq = q.shape[0], q.shape[1]
+    Smax = k_cache.shape[1]
+    _expect(q, (B, Lq, cfg.num_heads, L["head_dim"]), "q")
+    _expect(k_cache, (B, Smax, L["num_kv_heads"], L["head_dim"]), "k_cache")
+    if v_cache is not None and not L["k_eq_v"]:
+        _expect(v_cache, (B, Smax, L["num_kv_heads"], L["head_dim"]), "v_cache")
+    _expect(ctx_len, (B,), "ctx_len")
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, cfg.num_heads, Lq), dtype=torch.float32, device=q.device)
+    need = decode_multi_workspace_size(cfg, layer_idx, B, Lq, Smax)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    bf = torch.bfloat16
+    rc = load().gemma_attn_decode_multi(
+        ctypes.byref(cfg.to_c()), int(layer_idx), B, Lq, Smax, _ptr(q, bf, "q"), _ptr(k_cache, bf, "k_cache"),
+        None if L["k_eq_v"] else _ptr(v_cache, bf, "v_cache"), _ptr(ctx_len, torch.int32, "ctx_len"),
+        _ptr(out, bf, "out"), _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "gemma_attn_decode_multi")
+    return (out, lse) if lse is not None else out
+
+
+def qk_prologue_cache(cfg, layer_idx, q, k, v, k_cache, v_cache, ctx_len, q_out=None, q_norm_w=None, k_norm_w=None,
+                      stream=None):
+    """gemma_qk_prologue_cache: q [B,L,Hq,D] -> q_out; k (normed, rotated) and v (copied) appended to the
+    caches at rows ctx_len[b] - L + s.  Returns q_out."""
+    import torch
+
+    cfg = Config.from_any(cfg)
+    L = resolve_layer(cfg, layer_idx)
+    B, Lq = q.shape[0], q.shape[1]
+    Smax = k_cache.shape[1]
+    D, Hkv = L["head_dim"], L["num_kv_heads"]
+    _expect(q, (B, Lq, cfg.num_heads, D), "q")
+    _expect(k, (B, Lq, Hkv, D), "k")
+    _expect(k_cache, (B, Smax, Hkv, D), "k_cache")
+    if not L["k_eq_v"]:
+        _expect(v, (B, Lq, Hkv, D), "v")
+        _expect(v_cache, (B, Smax, Hkv, D), "v_cache")
+    _expect(ctx_len, (B,), "ctx_len")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    bf = torch.bfloat16
+    rc = load().gemma_qk_prologue_cache(
+        ctypes.byref(cfg.to_c()), int(layer_idx), B, Lq, Smax, _ptr(q, bf, "q"), _ptr(k, bf, "k"),
+        None if L["k_eq_v"] else _ptr(v, bf, "v"), _ptr(q_out, bf, "q_out"), _ptr(k_cache, bf, "k_cache"),
+        None if L["k_eq_v"] else _ptr(v_cache, bf, "v_cache"), _ptr(q_norm_w, torch.float32, "q_norm_w"),
+        _ptr(k_norm_w, torch.float32, "k_norm_w"), _ptr(ctx_len, torch.int32, "ctx_len"), _stream(stream))
+    _check(rc, "gemma_qk_prologue_cache")
+    return q_out

@@ -1,11 +1,13 @@
 // Split-KV decode attention over a contiguous KV cache (gfx950).
 //
-// One query token per sequence (the decode step of generate()).  The keys a
-// sequence reads -- [ctx - W, ctx) on local layers, [0, ctx) on global layers
-// -- are cut into chunks; one workgroup handles one (chunk, KV head, sequence)
-// and produces an unnormalised partial (m, l, o) for the g query heads of the
-// group; a second kernel merges the partials of each (sequence, head) in a
-// fixed order (log-sum-exp combine).
+// q_len query tokens per sequence (1 for the decode step of generate(); more
+// for chunked prefill or draft verification), at positions ctx - q_len ..
+// ctx - 1, each causal and windowed on its own position.  The keys a sequence
+// reads -- back to the window of its first query on local layers, [0, ctx) on
+// global layers -- are cut into chunks; one workgroup handles one (chunk,
+// KV head, block of 16 (token, head) columns, sequence) and produces an
+// unnormalised partial (m, l, o) per column; a second kernel merges the
+// partials of each (sequence, token, head) in a fixed order (log-sum-exp).
 //
 // Inside a workgroup (2 waves) tiles of 16 cache rows stream HBM -> LDS with
 // the direct-to-LDS loads into two slots per team (one tile in flight while
@@ -40,13 +42,16 @@ struct DecodeParams {
   float* ws_m;
   float* ws_l;
   int32_t max_ctx, hq, hkv, window, chunk, n_split;
+  int32_t q_len, n_cb;        // query tokens per sequence; 16-column blocks per KV head
   float scale_log2, cap_in2, cap_log2;
 };
 
+// Keys sequence b can read: [lo, ctx).  With q_len query tokens at positions
+// ctx - q_len .. ctx - 1, a local layer reads back to the window of the first.
 __device__ __forceinline__ void seq_range(const DecodeParams& p, int32_t b, int32_t& lo, int32_t& ctx) {
   int32_t c = p.ctx_len[b];
   c = c < 0 ? 0 : (c > p.max_ctx ? p.max_ctx : c);
-  const int32_t span = p.window > 0 ? min(c, p.window) : c;
+  const int32_t span = p.window > 0 ? min(c, p.window + p.q_len - 1) : c;
   ctx = c;
   lo = c - span;
 }
@@ -107,7 +112,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(kTeams == 1 || kSlotElems * kTeams * 2 >= 16 * D * 4, "merge buffer reuses slot 0");
 
   const int32_t split = blockIdx.x;
-  const int32_t kvh = blockIdx.y;
+  const int32_t kvh = static_cast<int32_t>(blockIdx.y) / p.n_cb;
+  const int32_t cb = static_cast<int32_t>(blockIdx.y) % p.n_cb;   // 16-column block
   const int32_t b = blockIdx.z;
   int32_t lo, ctx;
   seq_range(p, b, lo, ctx);
@@ -122,17 +128,23 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int32_t member = wave % kTeam;
   const int32_t dlo = member * kDW;
   const int32_t lane = tid & 63;
-  const int32_t col = lane & 15;     // query head within the group (valid if < G)
+  const int32_t col = lane & 15;     // column of the block: (token, head) = divmod(cb*16 + col, g)
   const int32_t grp = lane >> 4;     // 16-lane group
+  const int32_t gcol = cb * 16 + col;
+  const bool col_ok = gcol < G * p.q_len;
+  const int32_t tok = col_ok ? gcol / G : 0;
+  const int32_t head = kvh * G + (col_ok ? gcol % G : 0);
+  // Keys this column may see: [key_lo, key_hi] (its own position and the window).
+  const int32_t key_hi = col_ok ? ctx - p.q_len + tok : -1;
+  const int32_t key_lo = p.window > 0 ? key_hi - p.window + 1 : 0;
 
-  // Q^T operand: lane holds d = ds*32 + grp*8 + [0, 8) of head `col`.
+  // Q^T operand: lane holds d = ds*32 + grp*8 + [0, 8) of its (token, head).
   bf16x8 qf[kDS];
   {
-    const int32_t hcol = col < G ? col : 0;
-    const uint16_t* qrow = p.q + (static_cast<int64_t>(b) * p.hq + kvh * G + hcol) * D + grp * 8;
+    const uint16_t* qrow = p.q + ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * D + grp * 8;
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds) {
-      qf[ds] = col < G ? *reinterpret_cast<const bf16x8*>(qrow + ds * 32) : bf16x8{};
+      qf[ds] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 32) : bf16x8{};
     }
   }
 
@@ -198,7 +210,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       } else {
         t = sacc[r] * p.scale_log2;
       }
-      t = (k0 + grp * 4 + r < s_hi) ? t : -INFINITY;
+      const int32_t key = k0 + grp * 4 + r;
+      t = ((key < s_hi) & (key <= key_hi) & (key >= key_lo)) ? t : -INFINITY;
       x[r] = t;
       mx = fmaxf(mx, t);
     }
@@ -265,18 +278,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  const int64_t part = (static_cast<int64_t>(b) * p.hq + kvh * G) * p.n_split + split;
+  // Partial of (sequence b, token tok, head): row ((b*q_len + tok)*Hq + head).
+  const int64_t part = ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * p.n_split + split;
   if constexpr (kTeams == 1) {
     // One team: both waves hold the same (m, l) and disjoint halves of D.
-    if (col < G) {
+    if (col_ok) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        float* dst = p.ws_o + (part + static_cast<int64_t>(col) * p.n_split) * D + dlo + db * 16 + grp * 4;
+        float* dst = p.ws_o + part * D + dlo + db * 16 + grp * 4;
         *reinterpret_cast<f32x4*>(dst) = o[db];
       }
       if (member == 0 && grp == 0) {
-        p.ws_m[part + static_cast<int64_t>(col) * p.n_split] = m_run;
-        p.ws_l[part + static_cast<int64_t>(col) * p.n_split] = l_run;
+        p.ws_m[part] = m_run;
+        p.ws_l[part] = l_run;
       }
     }
   } else {
@@ -296,16 +310,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int db = 0; db < kDB; ++db) *reinterpret_cast<f32x4*>(obuf + col * D + db * 16 + grp * 4) = o[db] * f;
     }
     __syncthreads();
-    if (wave == 1 && col < G) {
+    if (wave == 1 && col_ok) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         const f32x4 prev = *reinterpret_cast<const f32x4*>(obuf + col * D + db * 16 + grp * 4);
-        float* dst = p.ws_o + (part + static_cast<int64_t>(col) * p.n_split) * D + db * 16 + grp * 4;
+        float* dst = p.ws_o + part * D + db * 16 + grp * 4;
         *reinterpret_cast<f32x4*>(dst) = prev + o[db] * f;
       }
       if (grp == 0) {
-        p.ws_m[part + static_cast<int64_t>(col) * p.n_split] = m_all;
-        p.ws_l[part + static_cast<int64_t>(col) * p.n_split] =
+        p.ws_m[part] = m_all;
+        p.ws_l[part] =
             l_w[0][col] * __builtin_amdgcn_exp2f(m_w[0][col] - m_ref) + l_w[1][col] * __builtin_amdgcn_exp2f(m_w[1][col] - m_ref);
       }
     }
@@ -316,13 +330,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
   constexpr int kPer = D / 64 > 0 ? D / 64 : 1;   // elements per lane
-  const int32_t head = blockIdx.x;
+  const int32_t tok = static_cast<int32_t>(blockIdx.x) / p.hq;
+  const int32_t head = static_cast<int32_t>(blockIdx.x) % p.hq;
   const int32_t b = blockIdx.y;
   const int32_t lane = threadIdx.x;
   int32_t lo, ctx;
   seq_range(p, b, lo, ctx);
   const int32_t n_valid = ctx > lo ? (ctx - lo + p.chunk - 1) / p.chunk : 0;
-  const int64_t part = (static_cast<int64_t>(b) * p.hq + head) * p.n_split;
+  const int64_t row = (static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head;
+  const int64_t part = row * p.n_split;
   float m_all = -INFINITY;
   for (int s = 0; s < n_valid; ++s) m_all = fmaxf(m_all, p.ws_m[part + s]);
   float acc[kPer];
@@ -342,22 +358,23 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
   }
   const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
   if (d0 < D) {
-    uint16_t* dst = p.out + (static_cast<int64_t>(b) * p.hq + head) * D + d0;
+    uint16_t* dst = p.out + row * D + d0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) dst[e] = f32_to_bf16(acc[e] * inv);
   }
   if (p.lse && lane == 0) {
-    p.lse[static_cast<int64_t>(b) * p.hq + head] = l_all > 0.f ? (m_all + __log2f(l_all)) * kLn2 : -INFINITY;
+    p.lse[(static_cast<int64_t>(b) * p.hq + head) * p.q_len + tok] =
+        l_all > 0.f ? (m_all + __log2f(l_all)) * kLn2 : -INFINITY;
   }
 }
 
 template <int D, int G, bool KEQV, bool CAP>
 hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(a.n_split), static_cast<uint32_t>(a.hkv), static_cast<uint32_t>(a.batch));
+  const dim3 grid(static_cast<uint32_t>(a.n_split), static_cast<uint32_t>(a.hkv * prm.n_cb), static_cast<uint32_t>(a.batch));
   hipLaunchKernelGGL((decode_split_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D>::kWaves * 64), 0, stream, prm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(static_cast<uint32_t>(a.hq), static_cast<uint32_t>(a.batch)),
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(static_cast<uint32_t>(a.hq * a.q_len), static_cast<uint32_t>(a.batch)),
                      dim3(64), 0, stream, prm);
   return hipGetLastError();
 }
@@ -401,6 +418,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.window = a.window;
   prm.chunk = a.chunk;
   prm.n_split = a.n_split;
+  prm.q_len = a.q_len;
+  prm.n_cb = (a.group * a.q_len + 15) / 16;
   const double log2e = 1.4426950408889634;
   prm.scale_log2 = static_cast<float>(a.scale * log2e);
   prm.cap_in2 = a.softcap > 0.0 ? static_cast<float>(2.0 * a.scale * log2e / a.softcap) : 0.f;

@@ -17,6 +17,13 @@ struct PrologueArgs {
   const int32_t* pos0;
   double theta;
   float eps, offset;
+  // Cache mode (ctx_len != null): token s of sequence b sits at position
+  // ctx_len[b] - seq + s; k_out and v_out are caches [B, max_ctx, Hkv, D] and
+  // the processed keys (and raw values, when v_in is set) land at that row.
+  const int32_t* ctx_len;
+  int32_t max_ctx;
+  const void* v_in;
+  void* v_out;
 };
 hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream);
 
@@ -34,7 +41,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   int32_t batch, max_ctx, hq, hkv, dim, group, window, k_eq_v;
-  int32_t chunk, n_split;
+  int32_t chunk, n_split, q_len;
   const void* q;
   const void* k_cache;
   const void* v_cache;

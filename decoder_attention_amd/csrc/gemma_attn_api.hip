@@ -69,6 +69,10 @@ int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
   a.theta = L.theta;
   a.eps = static_cast<float>(cfg->norm_eps);
   a.offset = static_cast<float>(cfg->norm_weight_offset);
+  a.ctx_len = nullptr;
+  a.max_ctx = 0;
+  a.v_in = nullptr;
+  a.v_out = nullptr;
   return hip_rc(ga::launch_qk_prologue(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -103,30 +107,38 @@ int gemma_attn_prefill(const gemma_attn_config* cfg, int32_t layer_idx, int32_t 
   return hip_rc(ga::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
-size_t gemma_attn_decode_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
-                                        int32_t max_ctx) {
+size_t gemma_attn_decode_multi_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
+                                              int32_t q_len, int32_t max_ctx) {
   gemma_attn_layer L;
   if (ga::resolve_layer(cfg, layer_idx, &L) != GA_OK) return 0;
-  if (batch < 0 || max_ctx < 1) return 0;
-  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx);
-  return ga::decode_workspace(L, cfg->num_heads, batch, plan).total;
+  if (batch < 0 || max_ctx < 1 || q_len < 1 || q_len > max_ctx) return 0;
+  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len);
+  return ga::decode_workspace(L, cfg->num_heads, batch, q_len, plan).total;
 }
 
-int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t max_ctx,
-                      const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_len,
-                      void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+size_t gemma_attn_decode_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
+                                        int32_t max_ctx) {
+  return gemma_attn_decode_multi_workspace_size(cfg, layer_idx, batch, 1, max_ctx);
+}
+
+int gemma_attn_decode_multi(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                            int32_t max_ctx, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* ctx_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   gemma_attn_layer L;
   const int rc = ga::resolve_layer(cfg, layer_idx, &L);
   if (rc != GA_OK) return rc;
-  if (batch < 0 || max_ctx < 1) return GA_ERR_INVALID_ARG;
+  if (batch < 0 || max_ctx < 1 || q_len < 1 || q_len > max_ctx) return GA_ERR_INVALID_ARG;
   if (!ga::attn_dim_supported(L.head_dim) || !ga::attn_group_supported(L.group)) return GA_ERR_UNSUPPORTED;
-  if (batch > 65535 || L.num_kv_heads > 65535 || cfg->num_heads > 65535) return GA_ERR_UNSUPPORTED;
+  const long long col_blocks = (static_cast<long long>(L.group) * q_len + 15) / 16;
+  if (batch > 65535 || L.num_kv_heads * col_blocks > 65535 || static_cast<long long>(cfg->num_heads) * q_len > 0x7fffffff)
+    return GA_ERR_UNSUPPORTED;
   if (batch == 0) return GA_OK;
   if (!dev_ok(q) || !dev_ok(k_cache) || !dev_ok(out) || ctx_len == nullptr) return GA_ERR_INVALID_ARG;
   if (!L.k_eq_v && !dev_ok(v_cache)) return GA_ERR_INVALID_ARG;
   if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
-  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx);
-  const ga::DecodeWorkspace ws = ga::decode_workspace(L, cfg->num_heads, batch, plan);
+  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len);
+  const ga::DecodeWorkspace ws = ga::decode_workspace(L, cfg->num_heads, batch, q_len, plan);
   if (workspace == nullptr || !ga::aligned16(workspace) || workspace_bytes < ws.total) return GA_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(workspace);
   ga::DecodeArgs a;
@@ -140,6 +152,7 @@ int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
   a.k_eq_v = L.k_eq_v;
   a.chunk = plan.chunk;
   a.n_split = plan.n_split;
+  a.q_len = q_len;
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = L.k_eq_v ? k_cache : v_cache;
@@ -152,6 +165,52 @@ int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
   a.scale = L.scale;
   a.softcap = L.softcap;
   return hip_rc(ga::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t max_ctx,
+                      const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_len,
+                      void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemma_attn_decode_multi(cfg, layer_idx, batch, 1, max_ctx, q, k_cache, v_cache, ctx_len, out, lse, workspace,
+                                 workspace_bytes, stream);
+}
+
+int gemma_qk_prologue_cache(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                            int32_t max_ctx, const void* q_in, const void* k_in, const void* v_in, void* q_out,
+                            void* k_cache, void* v_cache, const float* q_norm_w, const float* k_norm_w,
+                            const int32_t* ctx_len, void* stream) {
+  gemma_attn_layer L;
+  const int rc = ga::resolve_layer(cfg, layer_idx, &L);
+  if (rc != GA_OK) return rc;
+  if (batch < 0 || q_len < 0 || max_ctx < 1 || q_len > max_ctx) return GA_ERR_INVALID_ARG;
+  if (static_cast<long long>(batch) * q_len > INT_MAX) return GA_ERR_UNSUPPORTED;
+  if (!ga::prologue_dim_supported(L.head_dim)) return GA_ERR_UNSUPPORTED;
+  if (batch == 0 || q_len == 0) return GA_OK;
+  if (!dev_ok(q_in) || !dev_ok(q_out) || !dev_ok(k_in) || !dev_ok(k_cache) || ctx_len == nullptr)
+    return GA_ERR_INVALID_ARG;
+  if (!L.k_eq_v && (!dev_ok(v_in) || !dev_ok(v_cache))) return GA_ERR_INVALID_ARG;
+  if ((q_norm_w && !ga::aligned16(q_norm_w)) || (k_norm_w && !ga::aligned16(k_norm_w))) return GA_ERR_INVALID_ARG;
+  ga::PrologueArgs a;
+  a.batch = batch;
+  a.seq = q_len;
+  a.hq = cfg->num_heads;
+  a.hkv = L.num_kv_heads;
+  a.dim = L.head_dim;
+  a.rotary_dim = L.rotary_dim;
+  a.q_in = q_in;
+  a.k_in = k_in;
+  a.q_out = q_out;
+  a.k_out = k_cache;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.pos0 = nullptr;
+  a.theta = L.theta;
+  a.eps = static_cast<float>(cfg->norm_eps);
+  a.offset = static_cast<float>(cfg->norm_weight_offset);
+  a.ctx_len = ctx_len;
+  a.max_ctx = max_ctx;
+  a.v_in = L.k_eq_v ? nullptr : v_in;
+  a.v_out = L.k_eq_v ? nullptr : v_cache;
+  return hip_rc(ga::launch_qk_prologue(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -72,14 +72,18 @@ bool attn_dim_supported(int32_t d) { return d == 64 || d == 256 || d == 512; }
 
 bool attn_group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
-DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t max_ctx) {
+DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t max_ctx, int32_t q_len) {
   (void)num_heads;
   DecodePlan p;
-  p.span_max = L.window > 0 ? (L.window < max_ctx ? L.window : max_ctx) : max_ctx;
+  const long long ql = q_len > 0 ? q_len : 1;
+  const long long wspan = static_cast<long long>(L.window) + ql - 1;
+  p.span_max = L.window > 0 ? static_cast<int32_t>(wspan < max_ctx ? wspan : max_ctx) : max_ctx;
   if (p.span_max < 1) p.span_max = 1;
-  // Aim for >= 2048 workgroups over (split, KV head, sequence) so that 256 CUs
-  // stay busy on ragged lengths; chunks are powers of two in [256, 4096] keys.
-  const long long units = static_cast<long long>(batch > 0 ? batch : 1) * L.num_kv_heads;
+  // Aim for >= 2048 workgroups over (split, KV head x 16-column block,
+  // sequence) so that 256 CUs stay busy on ragged lengths; chunks are powers
+  // of two in [256, 4096] keys.
+  const long long col_blocks = (static_cast<long long>(L.group) * ql + 15) / 16;
+  const long long units = static_cast<long long>(batch > 0 ? batch : 1) * L.num_kv_heads * col_blocks;
   long long want = (2048 + units - 1) / units;
   if (want < 1) want = 1;
   long long chunk = 256;
@@ -96,10 +100,10 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
   return p;
 }
 
-DecodeWorkspace decode_workspace(const gemma_attn_layer& L, int32_t num_heads, int32_t batch,
+DecodeWorkspace decode_workspace(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t q_len,
                                  const DecodePlan& p) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  const size_t rows = static_cast<size_t>(batch) * num_heads * p.n_split;
+  const size_t rows = static_cast<size_t>(batch) * num_heads * static_cast<size_t>(q_len) * p.n_split;
   DecodeWorkspace w;
   w.o_off = 0;
   w.m_off = up(rows * L.head_dim * sizeof(float));

@@ -1,5 +1,11 @@
 // Fused QK-norm + dual-base partial rotary prologue (gfx950).
 //
+// Two modes: rows in, rows out (positions pos0[b] + s); or cache mode, where
+// the seq new tokens of each sequence sit at positions ctx_len[b] - seq + s
+// and their processed keys (and raw values) are written straight into the
+// contiguous caches at those rows -- the cache append of a decode or
+// chunked-prefill step.
+//
 // One workgroup per group of kTok consecutive tokens (flattened over batch and
 // sequence).  The rotary frequencies w_i = theta^(-2i/r) are formed once per
 // workgroup in fp64, then each token's cos/sin(p * w_i) table (angle reduced
@@ -34,11 +40,24 @@ struct ProParams {
   const float* qw;
   const float* kw;
   const int32_t* pos0;
+  const int32_t* ctx_len;     // cache mode: positions ctx_len[b] - seq + s
+  const uint16_t* v_in;       // cache mode: raw values copied into v_out
+  uint16_t* v_out;
   int64_t tokens;
-  int32_t seq, hq, hkv, dim, rotary_dim;
+  int32_t seq, hq, hkv, dim, rotary_dim, max_ctx;
   double theta;
   float eps, offset;
 };
+
+// Position of token s of sequence b.
+__device__ __forceinline__ int64_t token_pos(const ProParams& p, int32_t b, int32_t s) {
+  if (p.ctx_len) {
+    int32_t c = p.ctx_len[b];
+    c = c < 0 ? 0 : (c > p.max_ctx ? p.max_ctx : c);
+    return static_cast<int64_t>(c) - p.seq + s;
+  }
+  return static_cast<int64_t>(p.pos0 ? p.pos0[b] : 0) + s;
+}
 
 // SHFL: the partner is lane ^ (r/16) (r/16 a power of two, r <= D); else LDS.
 template <bool SHFL>
@@ -52,29 +71,42 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
   const int32_t dim = p.dim;
   const int32_t tpr = dim >> 3;                 // lanes per row (power of two <= 64)
   const int32_t rows_per_pass = kThreads / tpr;
-  const int32_t heads = p.hq + (p.k_in ? p.hkv : 0);
+  const int32_t heads = p.hq + (p.k_in ? p.hkv : 0) + (p.v_in ? p.hkv : 0);
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kTok;
   const int32_t rows = kTok * heads;
   const int32_t sub = tid / tpr;
   const int32_t lane = tid % tpr;
   const int32_t d0 = lane * 8;
 
-  // Row r of this workgroup: token tok0 + r / heads, head r % heads.
-  auto row_ptrs = [&](int32_t row, const uint16_t*& src, uint16_t*& dst, const float*& w) -> bool {
+  // Row r of this workgroup: token tok0 + r / heads, head r % heads: the q
+  // heads, then the k heads, then (cache mode) the v heads, which are copied
+  // unchanged.  In cache mode k and v rows go to cache row ctx - seq + s and
+  // are skipped when that row is outside the cache.
+  auto row_ptrs = [&](int32_t row, const uint16_t*& src, uint16_t*& dst, const float*& w, bool& copy) -> bool {
     const int32_t tt = row / heads;
     const int32_t hh = row % heads;
     const int64_t token = tok0 + tt;
+    copy = false;
     if (row >= rows || token >= p.tokens) return false;
     if (hh < p.hq) {
       const int64_t off = (token * p.hq + hh) * dim + d0;
       src = p.q_in + off;
       dst = p.q_out + off;
       w = p.qw;
+      return true;
+    }
+    const int32_t kh = (hh - p.hq) % p.hkv;
+    const bool is_v = hh >= p.hq + p.hkv;
+    src = (is_v ? p.v_in : p.k_in) + (token * p.hkv + kh) * dim + d0;
+    w = is_v ? nullptr : p.kw;
+    copy = is_v;
+    if (p.ctx_len) {
+      const int32_t b = static_cast<int32_t>(token / p.seq);
+      const int64_t pos = token_pos(p, b, static_cast<int32_t>(token % p.seq));
+      if (pos < 0 || pos >= p.max_ctx) return false;
+      dst = (is_v ? p.v_out : p.k_out) + ((static_cast<int64_t>(b) * p.max_ctx + pos) * p.hkv + kh) * dim + d0;
     } else {
-      const int64_t off = (token * p.hkv + (hh - p.hq)) * dim + d0;
-      src = p.k_in + off;
-      dst = p.k_out + off;
-      w = p.kw;
+      dst = p.k_out + (token * p.hkv + kh) * dim + d0;
     }
     return true;
   };
@@ -85,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
     const uint16_t* src;
     uint16_t* dst;
     const float* w;
-    if (row_ptrs(sub, src, dst, w)) raw = *reinterpret_cast<const u32x4*>(src);
+    bool cp;
+    if (row_ptrs(sub, src, dst, w, cp)) raw = *reinterpret_cast<const u32x4*>(src);
   }
 
   for (int32_t i = tid; i < half; i += kThreads) omega[i] = pow(p.theta, -2.0 * i / p.rotary_dim);
@@ -98,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
     if (token < p.tokens) {
       const int32_t b = static_cast<int32_t>(token / p.seq);
       const int32_t s = static_cast<int32_t>(token % p.seq);
-      const int64_t pos = static_cast<int64_t>(p.pos0 ? p.pos0[b] : 0) + s;
+      const int64_t pos = token_pos(p, b, s);
       double ang = fmod(static_cast<double>(pos) * omega[i], kTwoPi);
       if (ang < 0) ang += kTwoPi;
       sincosf(static_cast<float>(ang), &sn, &cn);
@@ -113,14 +146,16 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
     const uint16_t* src = nullptr;
     uint16_t* dst = nullptr;
     const float* w = nullptr;
-    const bool active = row_ptrs(row, src, dst, w);
+    bool copy = false;
+    const bool active = row_ptrs(row, src, dst, w, copy);
     // prefetch the next pass's row
     u32x4 next = u32x4{0u, 0u, 0u, 0u};
     if (row0 + rows_per_pass < rows) {
       const uint16_t* s2;
       uint16_t* d2;
       const float* w2;
-      if (row_ptrs(row + rows_per_pass, s2, d2, w2)) next = *reinterpret_cast<const u32x4*>(s2);
+      bool c2;
+      if (row_ptrs(row + rows_per_pass, s2, d2, w2, c2)) next = *reinterpret_cast<const u32x4*>(s2);
     }
     float x[8];
 #pragma unroll
@@ -165,7 +200,9 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int32_t d = d0 + e;
-        if (d < half) {
+        if (copy) {
+          y[e] = x[e];
+        } else if (d < half) {
           const float2 c = cs_tab[tt][d];
           y[e] = x[e] * c.x - partner[e] * c.y;
         } else if (d < p.rotary_dim) {
@@ -197,6 +234,10 @@ hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream) {
   p.qw = a.q_norm_w;
   p.kw = a.k_norm_w;
   p.pos0 = a.pos0;
+  p.ctx_len = a.ctx_len;
+  p.v_in = static_cast<const uint16_t*>(a.v_in);
+  p.v_out = static_cast<uint16_t*>(a.v_out);
+  p.max_ctx = a.max_ctx;
   p.tokens = tokens;
   p.seq = a.seq;
   p.hq = a.hq;

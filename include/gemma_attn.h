@@ -160,6 +160,45 @@ int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
                       const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_len,
                       void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Several new tokens per sequence against the contiguous cache: chunked
+ * prefill and the verification of speculative drafts (generate() on the Gemma
+ * pages; the atlas summary's MTP drafter, which scores any draft length).
+ * Token t of sequence b sits at position i = ctx_len[b] - q_len + t and sees
+ * cache rows j <= i, and on local layers j > i - W (the same mask as prefill,
+ * against the cache).  q [B,q_len,Hq,D] bf16 holds the processed queries; the
+ * caches hold processed keys and values of positions 0..ctx-1, new tokens
+ * included (see gemma_qk_prologue_cache); v_cache is ignored on keys-as-values
+ * layers.  out [B,q_len,Hq,D] bf16; lse fp32 [B,Hq,q_len] or NULL.  Rows with
+ * no visible key (i < 0) give out = 0, lse = -inf.  ctx_len entries are
+ * clamped to [0, max_ctx] on the device; 1 <= q_len <= max_ctx.  workspace: at
+ * least gemma_attn_decode_multi_workspace_size() bytes.  q_len = 1 is exactly
+ * gemma_attn_decode.
+ */
+int gemma_attn_decode_multi(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                            int32_t max_ctx, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* ctx_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes of gemma_attn_decode_multi; 0 when the arguments are invalid. */
+size_t gemma_attn_decode_multi_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
+                                              int32_t q_len, int32_t max_ctx);
+
+/*
+ * Prologue of q_len new tokens per sequence that appends them to the cache:
+ * the same QK-norm and rotary as gemma_qk_prologue, with token s of sequence
+ * b at position p = ctx_len[b] - q_len + s (ctx_len counts the new tokens).
+ * q_in [B,q_len,Hq,D] -> q_out (bf16, may alias q_in exactly); k_in
+ * [B,q_len,Hkv,D] is normed and rotated into k_cache [B,max_ctx,Hkv,D] at row
+ * p; v_in [B,q_len,Hkv,D] is copied unchanged into v_cache at row p (both
+ * ignored, may be NULL, on keys-as-values layers).  Rows p outside
+ * [0, max_ctx) are skipped; no other cache row is written.
+ */
+int gemma_qk_prologue_cache(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                            int32_t max_ctx, const void* q_in, const void* k_in, const void* v_in, void* q_out,
+                            void* k_cache, void* v_cache, const float* q_norm_w, const float* k_norm_w,
+                            const int32_t* ctx_len, void* stream);
+
 /* Static, human-readable text of an error code. */
 const char* gemma_attn_strerror(int code);
 

@@ -39,6 +39,7 @@ from .gemma_ref import (  # noqa: F401
     prefill,
     prefill_rows,
     decode,
+    decode_multi,
     prefill_flops,
     decode_kv_bytes,
 )

@@ -337,6 +337,39 @@ def decode(cfg, layer_idx, q, k_cache, v_cache, ctx_len, batches=None):
     return out, lse
 
 
+def decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len):
+    """Several new tokens per sequence against a contiguous cache.
+
+    q [B,L,Hq,D] holds the processed queries of the tokens at positions
+    ctx_b - L + t (reading: the cache already holds the new tokens, as in
+    single-token decode).  Token t at position i sees cache rows j with
+    0 <= j <= i and, on local layers, i - j < W -- the prefill mask.  A token
+    with i < 0 sees nothing (out 0, lse -inf).  Returns out [B,L,Hq,D] and
+    lse [B,Hq,L].
+    """
+    Lr = resolve_layer(cfg, layer_idx)
+    q = np.asarray(q, dtype=np.float64)
+    B, Lq, Hq, D = q.shape
+    g, W = Lr["group"], Lr["window"]
+    out = np.zeros((B, Lq, Hq, D))
+    lse = np.full((B, Hq, Lq), -np.inf)
+    for b in range(B):
+        c = int(ctx_len[b])
+        for t in range(Lq):
+            i = c - Lq + t
+            if i < 0:
+                continue
+            lo = max(0, i - W + 1) if W > 0 else 0
+            for h in range(Lr["num_kv_heads"]):
+                keys = np.asarray(k_cache[b, lo:i + 1, h, :], dtype=np.float64)
+                vals = keys if Lr["k_eq_v"] else np.asarray(v_cache[b, lo:i + 1, h, :], dtype=np.float64)
+                qb = q[b, t, h * g:(h + 1) * g, :][:, None, :]
+                o, l = _rows_block(qb, keys, vals, np.array([i]), np.arange(lo, i + 1), Lr)
+                out[b, t, h * g:(h + 1) * g, :] = o[:, 0, :]
+                lse[b, h * g:(h + 1) * g, t] = l[:, 0]
+    return out, lse
+
+
 def prefill_flops(cfg, layer_idx, batch: int, seq: int) -> int:
     """Algorithmic prefill work: 4*D FLOPs per allowed (query head, key) pair."""
     L = resolve_layer(cfg, layer_idx)

@@ -33,7 +33,9 @@ def _declared_functions():
 def test_exports_every_declared_symbol(ga):
     names = _declared_functions()
     assert set(names) == {"gemma_attn_resolve_layer", "gemma_qk_prologue", "gemma_attn_prefill",
-                          "gemma_attn_decode_workspace_size", "gemma_attn_decode", "gemma_attn_strerror"}
+                          "gemma_attn_decode_workspace_size", "gemma_attn_decode", "gemma_attn_strerror",
+                          "gemma_attn_decode_multi", "gemma_attn_decode_multi_workspace_size",
+                          "gemma_qk_prologue_cache"}
     lib = ctypes.CDLL(ga.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -143,3 +145,47 @@ def test_decode_workspace_covers_every_split(ga, W, max_ctx, B):
     span = min(W, max_ctx) if W else max_ctx
     # at least one fp32 (o[D], m, l) record per (sequence, head, 4096-key chunk) of the longest span
     assert need >= B * 16 * (L["head_dim"] + 2) * 4 * -(-span // 4096)
+
+
+def test_multi_token_entry_points_reject_bad_arguments(ga):
+    lib, ref, fake = ga.load(), ctypes.byref, ctypes.c_void_p(1 << 20)
+    keqv = ga.Config(num_heads=8, num_kv_heads=1, head_dim=512, k_eq_v=True).to_c()
+    good = ga.Config(num_heads=8, num_kv_heads=4, head_dim=256).to_c()
+    need = lib.gemma_attn_decode_multi_workspace_size(ref(keqv), 0, 4, 5, 1000)
+    assert need > lib.gemma_attn_decode_workspace_size(ref(keqv), 0, 4, 1000) > 0
+    assert lib.gemma_attn_decode_multi_workspace_size(ref(keqv), 0, 4, 1, 1000) == \
+        lib.gemma_attn_decode_workspace_size(ref(keqv), 0, 4, 1000)
+    for q_len, max_ctx in [(0, 1000), (1001, 1000), (-1, 1000), (1, 0)]:
+        assert lib.gemma_attn_decode_multi_workspace_size(ref(keqv), 0, 4, q_len, max_ctx) == 0
+        assert lib.gemma_attn_decode_multi(ref(keqv), 0, 4, q_len, max_ctx, fake, fake, None, fake, fake, None,
+                                           fake, 1 << 30, None) == ga.GA_ERR_INVALID_ARG
+    assert lib.gemma_attn_decode_multi(ref(keqv), 0, 4, 5, 1000, fake, fake, None, fake, fake, None, fake,
+                                       need - 1, None) == ga.GA_ERR_WORKSPACE
+    assert lib.gemma_attn_decode_multi(ref(good), 0, 4, 5, 1000, fake, fake, None, fake, fake, None, fake,
+                                       1 << 30, None) == ga.GA_ERR_INVALID_ARG   # v_cache missing
+    assert lib.gemma_attn_decode_multi(ref(keqv), 0, 4, 5, 1000, fake, fake, None, None, fake, None, fake,
+                                       1 << 30, None) == ga.GA_ERR_INVALID_ARG   # ctx_len missing
+    # too many 16-column blocks for the grid
+    g16 = ga.Config(num_heads=16 * 4096, num_kv_heads=4096, head_dim=64).to_c()
+    assert lib.gemma_attn_decode_multi(ref(g16), 0, 1, 300, 1000, fake, fake, fake, fake, fake, None, fake,
+                                       1 << 40, None) == ga.GA_ERR_UNSUPPORTED
+    # prologue with cache append
+    P = lib.gemma_qk_prologue_cache
+    assert P(ref(good), 0, 2, 4, 3, fake, fake, fake, fake, fake, fake, None, None, fake, None) == ga.GA_ERR_INVALID_ARG
+    assert P(ref(good), 0, 2, 4, 16, fake, fake, None, fake, fake, fake, None, None, fake, None) == ga.GA_ERR_INVALID_ARG
+    assert P(ref(good), 0, 2, 4, 16, fake, fake, fake, fake, fake, fake, None, None, None, None) == ga.GA_ERR_INVALID_ARG
+    assert P(ref(good), 0, 0, 4, 16, None, None, None, None, None, None, None, None, None, None) == ga.GA_OK
+    odd = ga.Config(num_heads=8, num_kv_heads=4, head_dim=96).to_c()
+    assert P(ref(odd), 0, 2, 4, 16, fake, fake, fake, fake, fake, fake, None, None, fake, None) == ga.GA_ERR_UNSUPPORTED
+    # keys-as-values: no value tensors needed
+    assert P(ref(keqv), 0, 0, 4, 16, fake, fake, None, fake, fake, None, None, None, fake, None) == ga.GA_OK
+
+
+@pytest.mark.parametrize("W,max_ctx,B,q_len", [(1024, 65536, 8, 16), (0, 4096, 2, 7), (100, 3000, 3, 64),
+                                               (0, 64, 1, 64)])
+def test_decode_multi_workspace_covers_every_split(ga, W, max_ctx, B, q_len):
+    kw = dict(num_heads=16, num_kv_heads=8, head_dim=256, sliding_window=W, sliding_window_pattern=0)
+    need = ga.decode_multi_workspace_size(kw, 0, B, q_len, max_ctx)
+    span = min(W + q_len - 1, max_ctx) if W else max_ctx
+    # one fp32 (o[D], m, l) record per (sequence, token, head, 4096-key chunk) of the longest span
+    assert need >= B * q_len * 16 * (256 + 2) * 4 * -(-span // 4096)

@@ -292,3 +292,23 @@ def test_round_bf16_closed_forms_and_bits():
     rng = np.random.default_rng(3)
     x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
     assert np.array_equal(R.round_bf16(x.astype(np.float64)), bf16_bits_to_f64(f32_to_bf16_bits(x)))
+
+
+@pytest.mark.parametrize("W,tied", [(0, False), (5, False), (0, True)])
+def test_decode_multi_equals_prefill_tail_and_decode(W, tied):
+    cfg = _small_cfg(sliding_window=W, k_eq_v=tied, attn_logit_softcapping=7.0)
+    B, S, Lq = 2, 17, 6
+    q, k, v = _inputs(91, B, S, 4, 2, 16, qscale=2.0)
+    o, l = R.prefill(cfg, 0, q, k, v)
+    # caches longer than the context, poisoned past it
+    kc = np.concatenate([k, np.full((B, 4, 2, 16), np.nan)], axis=1)
+    vc = np.concatenate([v, np.full((B, 4, 2, 16), np.nan)], axis=1)
+    om, lm = R.decode_multi(cfg, 0, q[:, S - Lq:], kc, vc, [S, S])
+    assert np.abs(om - o[:, S - Lq:]).max() < 1e-13
+    assert np.abs(lm - l[:, :, S - Lq:]).max() < 1e-13
+    o1, l1 = R.decode_multi(cfg, 0, q[:, S - 1:], kc, vc, [S, 9])
+    od, ld = R.decode(cfg, 0, np.stack([q[0, S - 1], q[1, S - 1]]), kc, vc, [S, 9])
+    assert np.array_equal(o1[:, 0], od) and np.array_equal(l1[:, :, 0], ld)
+    # more new tokens than context: early tokens see nothing
+    oz, lz = R.decode_multi(cfg, 0, q[:, :3], kc, vc, [2, 2])
+    assert np.all(oz[:, 0] == 0) and np.all(np.isneginf(lz[:, :, 0]))
