@@ -40,6 +40,9 @@ from .gemma_ref import (  # noqa: F401
     prefill_rows,
     decode,
     decode_multi,
+    quantize_int8,
+    dequantize_int8,
+    decode_int8,
     prefill_flops,
     decode_kv_bytes,
 )

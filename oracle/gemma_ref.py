@@ -370,6 +370,46 @@ def decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len):
     return out, lse
 
 
+def quantize_int8(x):
+    """Symmetric int8 quantization of each vector along the last axis.
+
+    The "google-gemma-4" atlas summary ("Training" section, efficiency entry)
+    says int8 KV caching is offered and gives no format.  Reading: one fp32
+    scale per (token, KV head) vector, s = max|x| / 127, codes
+    c = round-half-even(x / s) in [-127, 127]; an all-zero vector has s = 0 and
+    codes 0.  The decision is taken in fp32 (IEEE division), the precision of
+    the bf16 activations' arithmetic, so both sides reach the same integers.
+    Returns (codes int8 [..., D], scales fp32 [...]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        c = np.rint(np.divide(x, safe[..., None], dtype=np.float32))
+    c = np.where(s[..., None] > 0, c, 0.0)
+    return np.clip(c, -127, 127).astype(np.int8), s
+
+
+def dequantize_int8(codes, scales):
+    """codes * scale per vector, exact in fp64 (a 7-bit integer times an fp32)."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def decode_int8(cfg, layer_idx, q, k_codes, k_scales, v_codes, v_scales, ctx_len):
+    """Decode (any number of new tokens) against an int8 cache.
+
+    Cache codes [B,Smax,Hkv,D] int8 with scales [B,Hkv,Smax] fp32 (one per
+    token and head).  The attention is the one of ``decode_multi`` on the
+    dequantized cache; values are ignored on keys-as-values layers.  q
+    [B,L,Hq,D].  Returns out [B,L,Hq,D] and lse [B,Hq,L].
+    """
+    L = resolve_layer(cfg, layer_idx)
+    kd = dequantize_int8(k_codes, np.swapaxes(np.asarray(k_scales), 1, 2))
+    vd = kd if L["k_eq_v"] else dequantize_int8(v_codes, np.swapaxes(np.asarray(v_scales), 1, 2))
+    return decode_multi(cfg, layer_idx, q, kd, vd, ctx_len)
+
+
 def prefill_flops(cfg, layer_idx, batch: int, seq: int) -> int:
     """Algorithmic prefill work: 4*D FLOPs per allowed (query head, key) pair."""
     L = resolve_layer(cfg, layer_idx)
@@ -381,11 +421,13 @@ def prefill_flops(cfg, layer_idx, batch: int, seq: int) -> int:
     return 4 * L["head_dim"] * int(batch) * cfg.num_heads * n
 
 
-def decode_kv_bytes(cfg, layer_idx, ctx_len) -> int:
-    """Algorithmic decode bytes: every allowed cache element read once (bf16)."""
+def decode_kv_bytes(cfg, layer_idx, ctx_len, int8: bool = False) -> int:
+    """Algorithmic decode bytes: every allowed cache element read once (bf16,
+    or int8 codes plus one fp32 scale per token and head)."""
     L = resolve_layer(cfg, layer_idx)
     W = L["window"]
     c = np.asarray(ctx_len, dtype=np.int64)
     span = np.minimum(c, W) if W > 0 else c
-    per_tok = L["num_kv_heads"] * L["head_dim"] * 2 * (1 if L["k_eq_v"] else 2)
+    row = L["head_dim"] + 4 if int8 else L["head_dim"] * 2
+    per_tok = L["num_kv_heads"] * row * (1 if L["k_eq_v"] else 2)
     return int(np.sum(np.maximum(span, 0)) * per_tok)
