@@ -143,6 +143,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gemma_attn_decode_multi_workspace_size.restype = ctypes.c_size_t
     lib.gemma_qk_prologue_cache.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
     lib.gemma_qk_prologue_cache.restype = ctypes.c_int
+    lib.gemma_attn_decode_int8.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                           ctypes.c_size_t, _VP]
+    lib.gemma_attn_decode_int8.restype = ctypes.c_int
+    lib.gemma_qk_prologue_cache_int8.argtypes = [cfgp, i32, i32, i32, i32] + [_VP] * 12
+    lib.gemma_qk_prologue_cache_int8.restype = ctypes.c_int
+    lib.gemma_kv_quantize_int8.argtypes = [i32, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP]
+    lib.gemma_kv_quantize_int8.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -357,3 +364,90 @@ def qk_prologue_cache(cfg, layer_idx, q, k, v, k_cache, v_cache, ctx_len, q_out=
         _ptr(k_norm_w, torch.float32, "k_norm_w"), _ptr(ctx_len, torch.int32, "ctx_len"), _stream(stream))
     _check(rc, "gemma_qk_prologue_cache")
     return q_out
+
+
+# ----------------------------------------------------------------------------- int8 KV cache
+# codes [B,Smax,Hkv,D] torch.int8; scales [B,Hkv,Smax] torch.float32 (one per token and head).
+def attn_decode_int8(cfg, layer_idx, q, k_codes, k_scales, v_codes, v_scales, ctx_len, out=None, lse=None,
+                     want_lse=False, workspace=None, stream=None):
+    """gemma_attn_decode_int8; q [B,L,Hq,D]; returns out [B,L,Hq,D], or (out, lse [B,Hq,L])."""
+    import torch
+
+    cfg = Config.from_any(cfg)
+    L = resolve_layer(cfg, layer_idx)
+    B, Lq = q.shape[0], q.shape[1]
+    Smax = k_codes.shape[1]
+    D, Hkv = L["head_dim"], L["num_kv_heads"]
+    _expect(q, (B, Lq, cfg.num_heads, D), "q")
+    _expect(k_codes, (B, Smax, Hkv, D), "k_codes")
+    _expect(k_scales, (B, Hkv, Smax), "k_scales")
+    if not L["k_eq_v"]:
+        _expect(v_codes, (B, Smax, Hkv, D), "v_codes")
+        _expect(v_scales, (B, Hkv, Smax), "v_scales")
+    _expect(ctx_len, (B,), "ctx_len")
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, cfg.num_heads, Lq), dtype=torch.float32, device=q.device)
+    need = decode_multi_workspace_size(cfg, layer_idx, B, Lq, Smax)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    kv = not L["k_eq_v"]
+    rc = load().gemma_attn_decode_int8(
+        ctypes.byref(cfg.to_c()), int(layer_idx), B, Lq, Smax, _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_codes, torch.int8, "k_codes"), _ptr(k_scales, torch.float32, "k_scales"),
+        _ptr(v_codes, torch.int8, "v_codes") if kv else None, _ptr(v_scales, torch.float32, "v_scales") if kv else None,
+        _ptr(ctx_len, torch.int32, "ctx_len"), _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "gemma_attn_decode_int8")
+    return (out, lse) if lse is not None else out
+
+
+def qk_prologue_cache_int8(cfg, layer_idx, q, k, v, k_codes, k_scales, v_codes, v_scales, ctx_len, q_out=None,
+                           q_norm_w=None, k_norm_w=None, stream=None):
+    """gemma_qk_prologue_cache_int8: like qk_prologue_cache, appending to an int8 cache.  Returns q_out."""
+    import torch
+
+    cfg = Config.from_any(cfg)
+    L = resolve_layer(cfg, layer_idx)
+    B, Lq = q.shape[0], q.shape[1]
+    Smax = k_codes.shape[1]
+    D, Hkv = L["head_dim"], L["num_kv_heads"]
+    _expect(q, (B, Lq, cfg.num_heads, D), "q")
+    _expect(k, (B, Lq, Hkv, D), "k")
+    _expect(k_codes, (B, Smax, Hkv, D), "k_codes")
+    _expect(k_scales, (B, Hkv, Smax), "k_scales")
+    kv = not L["k_eq_v"]
+    if kv:
+        _expect(v, (B, Lq, Hkv, D), "v")
+        _expect(v_codes, (B, Smax, Hkv, D), "v_codes")
+        _expect(v_scales, (B, Hkv, Smax), "v_scales")
+    _expect(ctx_len, (B,), "ctx_len")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    bf = torch.bfloat16
+    rc = load().gemma_qk_prologue_cache_int8(
+        ctypes.byref(cfg.to_c()), int(layer_idx), B, Lq, Smax, _ptr(q, bf, "q"), _ptr(k, bf, "k"),
+        _ptr(v, bf, "v") if kv else None, _ptr(q_out, bf, "q_out"), _ptr(k_codes, torch.int8, "k_codes"),
+        _ptr(k_scales, torch.float32, "k_scales"), _ptr(v_codes, torch.int8, "v_codes") if kv else None,
+        _ptr(v_scales, torch.float32, "v_scales") if kv else None, _ptr(q_norm_w, torch.float32, "q_norm_w"),
+        _ptr(k_norm_w, torch.float32, "k_norm_w"), _ptr(ctx_len, torch.int32, "ctx_len"), _stream(stream))
+    _check(rc, "gemma_qk_prologue_cache_int8")
+    return q_out
+
+
+def kv_quantize_int8(x, codes, scales, pos0=None, stream=None):
+    """gemma_kv_quantize_int8: rows x [B,S,Hkv,D] bf16 into codes [B,Smax,Hkv,D] / scales [B,Hkv,Smax]
+    at rows pos0[b] + s."""
+    import torch
+
+    B, S, Hkv, D = x.shape
+    Smax = codes.shape[1]
+    _expect(codes, (B, Smax, Hkv, D), "codes")
+    _expect(scales, (B, Hkv, Smax), "scales")
+    if pos0 is not None:
+        _expect(pos0, (B,), "pos0")
+    rc = load().gemma_kv_quantize_int8(B, S, Hkv, D, Smax, _ptr(x, torch.bfloat16, "x"),
+                                       _ptr(pos0, torch.int32, "pos0"), _ptr(codes, torch.int8, "codes"),
+                                       _ptr(scales, torch.float32, "scales"), _stream(stream))
+    _check(rc, "gemma_kv_quantize_int8")

@@ -41,6 +41,8 @@ struct DecodeParams {
   float* ws_o;
   float* ws_m;
   float* ws_l;
+  const float* ks;            // int8 caches: scales [B, Hkv, max_ctx] of keys and values
+  const float* vs;
   int32_t max_ctx, hq, hkv, window, chunk, n_split;
   int32_t q_len, n_cb;        // query tokens per sequence; 16-column blocks per KV head
   float scale_log2, cap_in2, cap_log2;
@@ -84,6 +86,59 @@ struct DecodeShape {
   static constexpr int kTeam = D > 256 ? 2 : 1;       // waves per team
   static constexpr int kTeams = kWaves / kTeam;
 };
+
+// Write the partial (m, l, o) of this workgroup's 16 columns.  One team: both
+// waves hold the same (m, l) and disjoint slices of D.  Two teams (one wave
+// each, over different keys): merged through LDS first; merge_buf is
+// [16 columns][D] fp32 and reuses a slot (both waves are past their last
+// tile when the first barrier returns).
+template <int D, int kTeams, int kDB>
+__device__ __forceinline__ void write_partial(const DecodeParams& p, int64_t part, bool col_ok, const f32x4 (&o)[kDB],
+                                              float m_run, float l_run, int32_t wave, int32_t member, int32_t dlo,
+                                              int32_t grp, int32_t col, float* merge_buf, float (*m_w)[16],
+                                              float (*l_w)[16]) {
+  if constexpr (kTeams == 1) {
+    if (col_ok) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        float* dst = p.ws_o + part * D + dlo + db * 16 + grp * 4;
+        *reinterpret_cast<f32x4*>(dst) = o[db];
+      }
+      if (member == 0 && grp == 0) {
+        p.ws_m[part] = m_run;
+        p.ws_l[part] = l_run;
+      }
+    }
+  } else {
+    __syncthreads();
+    if (grp == 0) {
+      m_w[wave][col] = m_run;
+      l_w[wave][col] = l_run;
+    }
+    __syncthreads();
+    const float m_all = fmaxf(m_w[0][col], m_w[1][col]);
+    const float m_ref = m_all == -INFINITY ? 0.f : m_all;
+    const float f = __builtin_amdgcn_exp2f(m_run - m_ref);
+    if (wave == 0) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) *reinterpret_cast<f32x4*>(merge_buf + col * D + db * 16 + grp * 4) = o[db] * f;
+    }
+    __syncthreads();
+    if (wave == 1 && col_ok) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const f32x4 prev = *reinterpret_cast<const f32x4*>(merge_buf + col * D + db * 16 + grp * 4);
+        float* dst = p.ws_o + part * D + db * 16 + grp * 4;
+        *reinterpret_cast<f32x4*>(dst) = prev + o[db] * f;
+      }
+      if (grp == 0) {
+        p.ws_m[part] = m_all;
+        p.ws_l[part] =
+            l_w[0][col] * __builtin_amdgcn_exp2f(m_w[0][col] - m_ref) + l_w[1][col] * __builtin_amdgcn_exp2f(m_w[1][col] - m_ref);
+      }
+    }
+  }
+}
 
 template <int D, int G, bool KEQV, bool CAP>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(DecodeParams p) {
@@ -280,50 +335,261 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   l_run += __shfl_xor(l_run, 32, 64);
   // Partial of (sequence b, token tok, head): row ((b*q_len + tok)*Hq + head).
   const int64_t part = ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * p.n_split + split;
-  if constexpr (kTeams == 1) {
-    // One team: both waves hold the same (m, l) and disjoint halves of D.
-    if (col_ok) {
+  write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, member, dlo, grp, col,
+                                reinterpret_cast<float*>(ks0), m_w, l_w);
+}
+
+// ---------------------------------------------------------------------------
+// int8 cache: codes [B, max_ctx, Hkv, D] int8 with one fp32 scale per (token,
+// KV head), scales laid out [B, Hkv, max_ctx] so a tile's scales are one
+// contiguous run.  Tiles hold 32 keys (the bytes of a 16-row bf16 tile).  The
+// codes convert to bf16 exactly in registers; the key scale multiplies the
+// score and the value scale folds into the probability before its bf16
+// rounding, so both products stay bf16 MFMA:
+//   s_j = ks_j * (q . c_j),   o = sum_j (p_j * vs_j) c'_j,   l = sum_j p_j.
+// Value columns reach the PV operand with ds_read_b64_tr_b8.
+constexpr int kTK8 = 32;    // keys per int8 tile
+
+// XOR pattern of the 16-byte chunks of int8 LDS row r in [0, 32).  A 16-lane
+// b128 phase of the score product reads the 16 rows of one half at one chunk;
+// a transposed value read covers rows {0-7, 16-23} (lanes 0-31) or
+// {8-15, 24-31} (lanes 32-63) at one chunk.  Both sets land on 16 distinct
+// 16-byte bank groups (D = 64: four rows share one 256-byte bank cycle).
+template <int D>
+__device__ __forceinline__ int32_t qswz(int32_t r) {
+  if constexpr (D >= 256) return (r & 15) ^ (((r >> 4) & 1) << 3);
+  else return ((r >> 2) & 3) ^ (((r >> 4) & 1) << 1);
+}
+
+template <int D, int G, bool KEQV, bool CAP>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_i8_kernel(DecodeParams p) {
+  using Sh = DecodeShape<D>;
+  constexpr int kTeam = Sh::kTeam;
+  constexpr int kTeams = Sh::kTeams;
+  constexpr int kDW = D / kTeam;     // D slice of one wave's accumulators
+  constexpr int kDS = D / 64;        // 16-byte key chunks per lane per half (two MFMAs each)
+  constexpr int kDB = kDW / 16;      // 16-row blocks of this wave's O^T
+  constexpr int kRowChunks = D / 16; // 16-byte chunks per cache row
+  constexpr int kSlotBytes = kTK8 * D;
+  constexpr int kOps = kTK8 * kRowChunks / 64;  // 1 KB copy ops per tensor per tile
+  constexpr int kWaveOps = kOps / kTeam;
+  static_assert(G <= 16, "at most 16 query heads per KV head");
+  static_assert(kOps % kTeam == 0, "tile must split into whole 1 KB ops");
+  static_assert(kTeams == 1 || kSlotBytes * kTeams >= 16 * D * 4, "merge buffer reuses slot 0");
+
+  __shared__ __attribute__((aligned(16))) uint8_t ks0[kTeams * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ks1[kTeams * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vs0[KEQV ? 16 : kTeams * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vs1[KEQV ? 16 : kTeams * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) float ksc0[kTeams * 64];
+  __shared__ __attribute__((aligned(16))) float ksc1[kTeams * 64];
+  __shared__ __attribute__((aligned(16))) float vsc0[KEQV ? 4 : kTeams * 64];
+  __shared__ __attribute__((aligned(16))) float vsc1[KEQV ? 4 : kTeams * 64];
+  __shared__ float m_w[2][16];
+  __shared__ float l_w[2][16];
+
+  const int32_t split = blockIdx.x;
+  const int32_t kvh = static_cast<int32_t>(blockIdx.y) / p.n_cb;
+  const int32_t cb = static_cast<int32_t>(blockIdx.y) % p.n_cb;
+  const int32_t b = blockIdx.z;
+  int32_t lo, ctx;
+  seq_range(p, b, lo, ctx);
+  const int32_t s_lo = lo + split * p.chunk;
+  if (s_lo >= ctx) return;
+  const int32_t s_hi = min(ctx, s_lo + p.chunk);
+  const int32_t n_t = (s_hi - s_lo + kTK8 - 1) / kTK8;
+
+  const int32_t tid = threadIdx.x;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t team = wave / kTeam;
+  const int32_t member = wave % kTeam;
+  const int32_t dlo = member * kDW;
+  const int32_t lane = tid & 63;
+  const int32_t col = lane & 15;
+  const int32_t grp = lane >> 4;
+  const int32_t gcol = cb * 16 + col;
+  const bool col_ok = gcol < G * p.q_len;
+  const int32_t tok = col_ok ? gcol / G : 0;
+  const int32_t head = kvh * G + (col_ok ? gcol % G : 0);
+  const int32_t key_hi = col_ok ? ctx - p.q_len + tok : -1;
+  const int32_t key_lo = p.window > 0 ? key_hi - p.window + 1 : 0;
+
+  // Q^T operand: step ds, MFMA m: lane holds d = (ds*4 + grp)*16 + m*8 + [0, 8),
+  // the d range of the key chunk (ds*4 + grp) that the K operand lane reads.
+  bf16x8 qf[kDS][2];
+  {
+    const uint16_t* qrow = p.q + ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * D + grp * 16;
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        float* dst = p.ws_o + part * D + dlo + db * 16 + grp * 4;
-        *reinterpret_cast<f32x4*>(dst) = o[db];
-      }
-      if (member == 0 && grp == 0) {
-        p.ws_m[part] = m_run;
-        p.ws_l[part] = l_run;
-      }
-    }
-  } else {
-    // Two teams (waves) over different keys: merge through LDS.
-    __syncthreads();   // both waves are done with their slots; LDS reused below
-    if (grp == 0) {
-      m_w[wave][col] = m_run;
-      l_w[wave][col] = l_run;
-    }
-    __syncthreads();
-    const float m_all = fmaxf(m_w[0][col], m_w[1][col]);
-    const float m_ref = m_all == -INFINITY ? 0.f : m_all;
-    const float f = __builtin_amdgcn_exp2f(m_run - m_ref);
-    float* obuf = reinterpret_cast<float*>(ks0);   // [16 heads][D] fp32
-    if (wave == 0) {
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) *reinterpret_cast<f32x4*>(obuf + col * D + db * 16 + grp * 4) = o[db] * f;
-    }
-    __syncthreads();
-    if (wave == 1 && col_ok) {
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const f32x4 prev = *reinterpret_cast<const f32x4*>(obuf + col * D + db * 16 + grp * 4);
-        float* dst = p.ws_o + part * D + db * 16 + grp * 4;
-        *reinterpret_cast<f32x4*>(dst) = prev + o[db] * f;
-      }
-      if (grp == 0) {
-        p.ws_m[part] = m_all;
-        p.ws_l[part] =
-            l_w[0][col] * __builtin_amdgcn_exp2f(m_w[0][col] - m_ref) + l_w[1][col] * __builtin_amdgcn_exp2f(m_w[1][col] - m_ref);
-      }
+    for (int ds = 0; ds < kDS; ++ds) {
+      qf[ds][0] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 64) : bf16x8{};
+      qf[ds][1] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 64 + 8) : bf16x8{};
     }
   }
+
+  f32x4 o[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) o[db] = f32x4{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const uint32_t row_pitch = static_cast<uint32_t>(p.hkv) * D;     // bytes between cache rows
+  const int64_t seq_off = (static_cast<int64_t>(b) * p.max_ctx * p.hkv + kvh) * D;
+  const char* kseq = reinterpret_cast<const char*>(p.kc) + seq_off;
+  const char* vseq = KEQV ? kseq : reinterpret_cast<const char*>(p.vc) + seq_off;
+  const int64_t sc_off = (static_cast<int64_t>(b) * p.hkv + kvh) * p.max_ctx;
+  const float* kscale = p.ks + sc_off;
+  const float* vscale = KEQV ? kscale : p.vs + sc_off;
+
+  // Copy this wave's share of tile ti into a slot; member 0 also copies the
+  // tile's key scales and the last member its value scales (64 lanes, key
+  // lane & 31, so the upper half repeats the lower).  Rows past s_hi repeat
+  // row s_hi - 1.
+  auto copy_tile = [&](int32_t ti, uint8_t* kdst, uint8_t* vdst, float* kscd, float* vscd) {
+    const int32_t k0 = s_lo + ti * kTK8;
+    const int32_t last = s_hi - 1 - k0;
+    const char* kb = kseq + static_cast<int64_t>(k0) * row_pitch;
+    const char* vb = vseq + static_cast<int64_t>(k0) * row_pitch;
+    const int32_t ln = lane_here();
+#pragma unroll
+    for (int i = 0; i < kWaveOps; ++i) {
+      const int32_t op = member * kWaveOps + i;
+      const int32_t pc = op * 64 + ln;
+      const int32_t row = pc / kRowChunks;
+      const int32_t lc = (pc % kRowChunks) ^ qswz<D>(row);
+      const uint32_t off = static_cast<uint32_t>(min(row, last)) * row_pitch + static_cast<uint32_t>(lc) * 16u;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + off),
+                                       (__attribute__((address_space(3))) void*)(kdst + op * 1024), 16, 0, 0);
+      if (!KEQV) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + off),
+                                         (__attribute__((address_space(3))) void*)(vdst + op * 1024), 16, 0, 0);
+      }
+    }
+    const int32_t key = k0 + min(ln & 31, last);
+    if (member == 0) {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kscale + key),
+                                       (__attribute__((address_space(3))) void*)(kscd), 4, 0, 0);
+    }
+    if (!KEQV && member == kTeam - 1) {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vscale + key),
+                                       (__attribute__((address_space(3))) void*)(vscd), 4, 0, 0);
+    }
+  };
+
+  auto compute = [&](int32_t ti, const uint8_t* kb, const uint8_t* vb, const float* kscs, const float* vscs) {
+    const int32_t k0 = s_lo + ti * kTK8;
+    const int32_t ln = lane_here();
+    const int32_t li16 = ln & 15;
+    const int32_t lgrp = ln >> 4;
+    // S^T[32 keys x 16 columns] in two 16-key halves.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      sacc[h2] = f32x4{};
+      const int32_t row = h2 * 16 + li16;
+      const int32_t sw = qswz<D>(row);
+#pragma unroll
+      for (int ds = 0; ds < kDS; ++ds) {
+        const int32_t c = ds * 4 + lgrp;
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + row * D + ((c ^ sw) << 4));
+        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(raw[0], raw[1]), qf[ds][0], sacc[h2], 0, 0, 0);
+        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(raw[2], raw[3]), qf[ds][1], sacc[h2], 0, 0, 0);
+      }
+    }
+    // Lane holds keys k0 + h2*16 + grp*4 + r as x[h2*4 + r].
+    const f32x4 ksa = *reinterpret_cast<const f32x4*>(kscs + grp * 4);
+    const f32x4 ksb = *reinterpret_cast<const f32x4*>(kscs + 16 + grp * 4);
+    const f32x4 vsa = *reinterpret_cast<const f32x4*>(vscs + grp * 4);
+    const f32x4 vsb = *reinterpret_cast<const f32x4*>(vscs + 16 + grp * 4);
+    float x[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sv = sacc[e >> 2][e & 3] * (e < 4 ? ksa[e & 3] : ksb[e & 3]);
+      float t;
+      if (CAP) {
+        const float ex = __builtin_amdgcn_exp2f(sv * p.cap_in2);
+        t = fmaf(-2.f * p.cap_log2, __builtin_amdgcn_rcpf(ex + 1.f), p.cap_log2);
+      } else {
+        t = sv * p.scale_log2;
+      }
+      const int32_t key = k0 + (e >> 2) * 16 + grp * 4 + (e & 3);
+      t = ((key < s_hi) & (key <= key_hi) & (key >= key_lo)) ? t : -INFINITY;
+      x[e] = t;
+      mx = fmaxf(mx, t);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool grow = mx > m_run + 8.f;
+    const float m_next = grow ? mx : m_run;
+    const float m_use = m_next == -INFINITY ? 0.f : m_next;
+    if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) o[db] *= alpha;
+    }
+    m_run = m_next;
+    float pe[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pack_bf16x2(pe[e], pe[e + 1])), ones, l_run, false);
+    }
+    // P^T operand: slot e = key (e/4)*16 + grp*4 + e%4, scaled by its value scale.
+    const bf16x8 pb = __builtin_bit_cast(
+        bf16x8, u32x4{pack_bf16x2(pe[0] * vsa[0], pe[1] * vsa[1]), pack_bf16x2(pe[2] * vsa[2], pe[3] * vsa[3]),
+                      pack_bf16x2(pe[4] * vsb[0], pe[5] * vsb[1]), pack_bf16x2(pe[6] * vsb[2], pe[7] * vsb[3])});
+    // V^T operand: lane j of group lgrp addresses key row of slot j/2 at
+    // columns d0 + 8*(j%2); the transpose read hands lane i the 8 keys at d0 + i.
+    const int32_t e2 = li16 >> 1;
+    const int32_t vrow = (e2 >> 2) * 16 + lgrp * 4 + (e2 & 3);
+    const int32_t vsw = qswz<D>(vrow);
+    const uint8_t* vbase = vb + vrow * D + (li16 & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      const int32_t c = (dlo >> 4) + db;
+      const v2i32 raw = lds_read_tr8(vbase + ((c ^ vsw) << 4));
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          i8x8_to_bf16x8(static_cast<uint32_t>(raw[0]), static_cast<uint32_t>(raw[1])), pb, o[db], 0, 0, 0);
+    }
+  };
+
+  uint8_t* k0s = ks0 + team * kSlotBytes;
+  uint8_t* k1s = ks1 + team * kSlotBytes;
+  uint8_t* v0s = KEQV ? k0s : vs0 + team * kSlotBytes;
+  uint8_t* v1s = KEQV ? k1s : vs1 + team * kSlotBytes;
+  float* kl0 = ksc0 + team * 64;
+  float* kl1 = ksc1 + team * 64;
+  float* vl0 = KEQV ? kl0 : vsc0 + team * 64;
+  float* vl1 = KEQV ? kl1 : vsc1 + team * 64;
+  auto team_sync = [&]() {
+    if constexpr (kTeam > 1) __syncthreads();
+  };
+  int32_t ti = team;
+  if (ti < n_t) copy_tile(ti, k0s, v0s, kl0, vl0);
+  while (ti < n_t) {
+    const int32_t tn = ti + kTeams;
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+    team_sync();
+    if (tn < n_t) copy_tile(tn, k1s, v1s, kl1, vl1);
+    compute(ti, k0s, v0s, kl0, vl0);
+    ti = tn;
+    if (ti >= n_t) break;
+    const int32_t tn2 = ti + kTeams;
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+    team_sync();
+    if (tn2 < n_t) copy_tile(tn2, k0s, v0s, kl0, vl0);
+    compute(ti, k1s, v1s, kl1, vl1);
+    ti = tn2;
+  }
+
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  const int64_t part = ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * p.n_split + split;
+  write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, member, dlo, grp, col,
+                                reinterpret_cast<float*>(ks0), m_w, l_w);
 }
 
 // Merge the split partials of one (sequence, query head) in split order.
@@ -371,7 +637,11 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
 template <int D, int G, bool KEQV, bool CAP>
 hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(a.n_split), static_cast<uint32_t>(a.hkv * prm.n_cb), static_cast<uint32_t>(a.batch));
-  hipLaunchKernelGGL((decode_split_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D>::kWaves * 64), 0, stream, prm);
+  if (prm.ks) {
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D>::kWaves * 64), 0, stream, prm);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D>::kWaves * 64), 0, stream, prm);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(static_cast<uint32_t>(a.hq * a.q_len), static_cast<uint32_t>(a.batch)),
@@ -412,6 +682,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.ws_o = a.ws_o;
   prm.ws_m = a.ws_m;
   prm.ws_l = a.ws_l;
+  prm.ks = a.k_scales;
+  prm.vs = a.k_eq_v ? a.k_scales : a.v_scales;
   prm.max_ctx = a.max_ctx;
   prm.hq = a.hq;
   prm.hkv = a.hkv;

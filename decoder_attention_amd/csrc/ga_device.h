@@ -47,6 +47,34 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_addr));
 }
 
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+
+// ds_read_b64_tr_b8: within each 16-lane group, lane i receives byte i%8 of
+// the 8-byte chunks addressed by lanes 2e + i/8, e = 0..7, as its bytes e.
+// Pointing lane j of a group at row key(j/2), column (c0 + 8*(j%2)) of a
+// row-major byte tile therefore gives lane i the eight rows key(0..7) at
+// column c0 + i.
+__device__ __forceinline__ v2i32 lds_read_tr8(const void* lds_addr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(lds_addr));
+}
+
+// Two signed bytes (B, B+1) of w as a bf16 pair.  Integers up to 128 in
+// magnitude have 8 significant bits, so their fp32 value truncates to bf16
+// exactly (the high half).
+template <int B>
+__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w) {
+  const float lo = static_cast<float>(static_cast<int32_t>(w << (24 - 8 * B)) >> 24);
+  const float hi = static_cast<float>(static_cast<int32_t>(w << (16 - 8 * B)) >> 24);
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Eight signed bytes (w0 bytes 0-3, w1 bytes 0-3) as eight bf16 values.
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return __builtin_bit_cast(bf16x8, u32x4{i8pair_to_bf16x2<0>(w0), i8pair_to_bf16x2<2>(w0), i8pair_to_bf16x2<0>(w1),
+                                          i8pair_to_bf16x2<2>(w1)});
+}
+
 __device__ __forceinline__ float wave_max_xor32(float v) {
   return fmaxf(v, __shfl_xor(v, 32, 64));
 }

@@ -17,13 +17,20 @@ struct PrologueArgs {
   const int32_t* pos0;
   double theta;
   float eps, offset;
-  // Cache mode (ctx_len != null): token s of sequence b sits at position
-  // ctx_len[b] - seq + s; k_out and v_out are caches [B, max_ctx, Hkv, D] and
-  // the processed keys (and raw values, when v_in is set) land at that row.
+  // Cache mode (max_ctx > 0): token s of sequence b sits at position
+  // ctx_len[b] - seq + s (pos0[b] + s when ctx_len is null); k_out and v_out
+  // are caches [B, max_ctx, Hkv, D] and the processed keys (and raw values,
+  // when v_in is set) land at that row.  With k_scales set the caches are int8
+  // instead: codes k_codes / v_codes [B, max_ctx, Hkv, D] and fp32 scales
+  // k_scales / v_scales [B, Hkv, max_ctx].
   const int32_t* ctx_len;
   int32_t max_ctx;
   const void* v_in;
   void* v_out;
+  void* k_codes;
+  float* k_scales;
+  void* v_codes;
+  float* v_scales;
 };
 hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream);
 
@@ -51,6 +58,10 @@ struct DecodeArgs {
   float* ws_o;
   float* ws_m;
   float* ws_l;
+  // int8 caches (k_scales set): k_cache / v_cache hold int8 codes and these
+  // the fp32 scales, [B, Hkv, max_ctx].
+  const float* k_scales;
+  const float* v_scales;
   double scale, softcap;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

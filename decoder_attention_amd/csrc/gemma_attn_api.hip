@@ -19,6 +19,56 @@ int hip_rc(hipError_t e) {
   return GA_ERR_HIP;
 }
 
+// Shared by the bf16 and int8 decode entry points (k_scales set: int8 caches).
+int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len, int32_t max_ctx,
+                  const void* q, const void* k_cache, const float* k_scales, const void* v_cache,
+                  const float* v_scales, const int32_t* ctx_len, void* out, float* lse, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  gemma_attn_layer L;
+  const int rc = ga::resolve_layer(cfg, layer_idx, &L);
+  if (rc != GA_OK) return rc;
+  if (batch < 0 || max_ctx < 1 || q_len < 1 || q_len > max_ctx) return GA_ERR_INVALID_ARG;
+  if (!ga::attn_dim_supported(L.head_dim) || !ga::attn_group_supported(L.group)) return GA_ERR_UNSUPPORTED;
+  const long long col_blocks = (static_cast<long long>(L.group) * q_len + 15) / 16;
+  if (batch > 65535 || L.num_kv_heads * col_blocks > 65535 || static_cast<long long>(cfg->num_heads) * q_len > 0x7fffffff)
+    return GA_ERR_UNSUPPORTED;
+  if (batch == 0) return GA_OK;
+  if (!dev_ok(q) || !dev_ok(k_cache) || !dev_ok(out) || ctx_len == nullptr) return GA_ERR_INVALID_ARG;
+  if (!L.k_eq_v && !dev_ok(v_cache)) return GA_ERR_INVALID_ARG;
+  if (k_scales && (!dev_ok(k_scales) || (!L.k_eq_v && !dev_ok(v_scales)))) return GA_ERR_INVALID_ARG;
+  if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
+  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len);
+  const ga::DecodeWorkspace ws = ga::decode_workspace(L, cfg->num_heads, batch, q_len, plan);
+  if (workspace == nullptr || !ga::aligned16(workspace) || workspace_bytes < ws.total) return GA_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(workspace);
+  ga::DecodeArgs a{};
+  a.batch = batch;
+  a.max_ctx = max_ctx;
+  a.hq = cfg->num_heads;
+  a.hkv = L.num_kv_heads;
+  a.dim = L.head_dim;
+  a.group = L.group;
+  a.window = L.window;
+  a.k_eq_v = L.k_eq_v;
+  a.chunk = plan.chunk;
+  a.n_split = plan.n_split;
+  a.q_len = q_len;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = L.k_eq_v ? k_cache : v_cache;
+  a.k_scales = k_scales;
+  a.v_scales = L.k_eq_v ? k_scales : v_scales;
+  a.ctx_len = ctx_len;
+  a.out = out;
+  a.lse = lse;
+  a.ws_o = reinterpret_cast<float*>(wsb + ws.o_off);
+  a.ws_m = reinterpret_cast<float*>(wsb + ws.m_off);
+  a.ws_l = reinterpret_cast<float*>(wsb + ws.l_off);
+  a.scale = L.scale;
+  a.softcap = L.softcap;
+  return hip_rc(ga::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -52,7 +102,7 @@ int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
   if (k_in && !dev_ok(k_out)) return GA_ERR_INVALID_ARG;
   if (k_in && !ga::aligned16(k_in)) return GA_ERR_INVALID_ARG;
   if ((q_norm_w && !ga::aligned16(q_norm_w)) || (k_norm_w && !ga::aligned16(k_norm_w))) return GA_ERR_INVALID_ARG;
-  ga::PrologueArgs a;
+  ga::PrologueArgs a{};
   a.batch = batch;
   a.seq = seq;
   a.hq = cfg->num_heads;
@@ -88,7 +138,7 @@ int gemma_attn_prefill(const gemma_attn_config* cfg, int32_t layer_idx, int32_t 
   if (!dev_ok(q) || !dev_ok(k) || !dev_ok(out)) return GA_ERR_INVALID_ARG;
   if (!L.k_eq_v && !dev_ok(v)) return GA_ERR_INVALID_ARG;
   if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
-  ga::PrefillArgs a;
+  ga::PrefillArgs a{};
   a.batch = batch;
   a.seq = seq;
   a.hq = cfg->num_heads;
@@ -125,46 +175,17 @@ int gemma_attn_decode_multi(const gemma_attn_config* cfg, int32_t layer_idx, int
                             int32_t max_ctx, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* ctx_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  gemma_attn_layer L;
-  const int rc = ga::resolve_layer(cfg, layer_idx, &L);
-  if (rc != GA_OK) return rc;
-  if (batch < 0 || max_ctx < 1 || q_len < 1 || q_len > max_ctx) return GA_ERR_INVALID_ARG;
-  if (!ga::attn_dim_supported(L.head_dim) || !ga::attn_group_supported(L.group)) return GA_ERR_UNSUPPORTED;
-  const long long col_blocks = (static_cast<long long>(L.group) * q_len + 15) / 16;
-  if (batch > 65535 || L.num_kv_heads * col_blocks > 65535 || static_cast<long long>(cfg->num_heads) * q_len > 0x7fffffff)
-    return GA_ERR_UNSUPPORTED;
-  if (batch == 0) return GA_OK;
-  if (!dev_ok(q) || !dev_ok(k_cache) || !dev_ok(out) || ctx_len == nullptr) return GA_ERR_INVALID_ARG;
-  if (!L.k_eq_v && !dev_ok(v_cache)) return GA_ERR_INVALID_ARG;
-  if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
-  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len);
-  const ga::DecodeWorkspace ws = ga::decode_workspace(L, cfg->num_heads, batch, q_len, plan);
-  if (workspace == nullptr || !ga::aligned16(workspace) || workspace_bytes < ws.total) return GA_ERR_WORKSPACE;
-  char* wsb = static_cast<char*>(workspace);
-  ga::DecodeArgs a;
-  a.batch = batch;
-  a.max_ctx = max_ctx;
-  a.hq = cfg->num_heads;
-  a.hkv = L.num_kv_heads;
-  a.dim = L.head_dim;
-  a.group = L.group;
-  a.window = L.window;
-  a.k_eq_v = L.k_eq_v;
-  a.chunk = plan.chunk;
-  a.n_split = plan.n_split;
-  a.q_len = q_len;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = L.k_eq_v ? k_cache : v_cache;
-  a.ctx_len = ctx_len;
-  a.out = out;
-  a.lse = lse;
-  a.ws_o = reinterpret_cast<float*>(wsb + ws.o_off);
-  a.ws_m = reinterpret_cast<float*>(wsb + ws.m_off);
-  a.ws_l = reinterpret_cast<float*>(wsb + ws.l_off);
-  a.scale = L.scale;
-  a.softcap = L.softcap;
-  return hip_rc(ga::launch_decode(a, static_cast<hipStream_t>(stream)));
+  return decode_common(cfg, layer_idx, batch, q_len, max_ctx, q, k_cache, nullptr, v_cache, nullptr, ctx_len, out, lse,
+                       workspace, workspace_bytes, stream);
+}
+
+int gemma_attn_decode_int8(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                           int32_t max_ctx, const void* q, const void* k_codes, const float* k_scales,
+                           const void* v_codes, const float* v_scales, const int32_t* ctx_len, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (k_scales == nullptr) return GA_ERR_INVALID_ARG;
+  return decode_common(cfg, layer_idx, batch, q_len, max_ctx, q, k_codes, k_scales, v_codes, v_scales, ctx_len, out,
+                       lse, workspace, workspace_bytes, stream);
 }
 
 int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t max_ctx,
@@ -189,7 +210,7 @@ int gemma_qk_prologue_cache(const gemma_attn_config* cfg, int32_t layer_idx, int
     return GA_ERR_INVALID_ARG;
   if (!L.k_eq_v && (!dev_ok(v_in) || !dev_ok(v_cache))) return GA_ERR_INVALID_ARG;
   if ((q_norm_w && !ga::aligned16(q_norm_w)) || (k_norm_w && !ga::aligned16(k_norm_w))) return GA_ERR_INVALID_ARG;
-  ga::PrologueArgs a;
+  ga::PrologueArgs a{};
   a.batch = batch;
   a.seq = q_len;
   a.hq = cfg->num_heads;
@@ -210,6 +231,72 @@ int gemma_qk_prologue_cache(const gemma_attn_config* cfg, int32_t layer_idx, int
   a.max_ctx = max_ctx;
   a.v_in = L.k_eq_v ? nullptr : v_in;
   a.v_out = L.k_eq_v ? nullptr : v_cache;
+  return hip_rc(ga::launch_qk_prologue(a, static_cast<hipStream_t>(stream)));
+}
+
+int gemma_qk_prologue_cache_int8(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                                 int32_t max_ctx, const void* q_in, const void* k_in, const void* v_in, void* q_out,
+                                 void* k_codes, float* k_scales, void* v_codes, float* v_scales,
+                                 const float* q_norm_w, const float* k_norm_w, const int32_t* ctx_len, void* stream) {
+  gemma_attn_layer L;
+  const int rc = ga::resolve_layer(cfg, layer_idx, &L);
+  if (rc != GA_OK) return rc;
+  if (batch < 0 || q_len < 0 || max_ctx < 1 || q_len > max_ctx) return GA_ERR_INVALID_ARG;
+  if (static_cast<long long>(batch) * q_len > INT_MAX) return GA_ERR_UNSUPPORTED;
+  if (!ga::prologue_dim_supported(L.head_dim)) return GA_ERR_UNSUPPORTED;
+  if (batch == 0 || q_len == 0) return GA_OK;
+  if (!dev_ok(q_in) || !dev_ok(q_out) || !dev_ok(k_in) || !dev_ok(k_codes) || !dev_ok(k_scales) || ctx_len == nullptr)
+    return GA_ERR_INVALID_ARG;
+  if (!L.k_eq_v && (!dev_ok(v_in) || !dev_ok(v_codes) || !dev_ok(v_scales))) return GA_ERR_INVALID_ARG;
+  if ((q_norm_w && !ga::aligned16(q_norm_w)) || (k_norm_w && !ga::aligned16(k_norm_w))) return GA_ERR_INVALID_ARG;
+  ga::PrologueArgs a{};
+  a.batch = batch;
+  a.seq = q_len;
+  a.hq = cfg->num_heads;
+  a.hkv = L.num_kv_heads;
+  a.dim = L.head_dim;
+  a.rotary_dim = L.rotary_dim;
+  a.q_in = q_in;
+  a.k_in = k_in;
+  a.q_out = q_out;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.theta = L.theta;
+  a.eps = static_cast<float>(cfg->norm_eps);
+  a.offset = static_cast<float>(cfg->norm_weight_offset);
+  a.ctx_len = ctx_len;
+  a.max_ctx = max_ctx;
+  a.v_in = L.k_eq_v ? nullptr : v_in;
+  a.k_codes = k_codes;
+  a.k_scales = k_scales;
+  a.v_codes = L.k_eq_v ? nullptr : v_codes;
+  a.v_scales = L.k_eq_v ? nullptr : v_scales;
+  return hip_rc(ga::launch_qk_prologue(a, static_cast<hipStream_t>(stream)));
+}
+
+int gemma_kv_quantize_int8(int32_t batch, int32_t seq, int32_t num_kv_heads, int32_t head_dim, int32_t max_ctx,
+                           const void* x, const int32_t* pos0, void* codes, float* scales, void* stream) {
+  if (batch < 0 || seq < 0 || num_kv_heads < 1 || head_dim < 1 || max_ctx < 1) return GA_ERR_INVALID_ARG;
+  if (static_cast<long long>(batch) * seq > INT_MAX) return GA_ERR_UNSUPPORTED;
+  if (!ga::prologue_dim_supported(head_dim)) return GA_ERR_UNSUPPORTED;
+  if (batch == 0 || seq == 0) return GA_OK;
+  if (!dev_ok(x) || !dev_ok(codes) || !dev_ok(scales)) return GA_ERR_INVALID_ARG;
+  if (pos0 && !ga::aligned16(pos0)) return GA_ERR_INVALID_ARG;
+  // The prologue kernel with no query heads, no norm and no rotation: each key
+  // row passes through unchanged and is quantized into its cache row.
+  ga::PrologueArgs a{};
+  a.batch = batch;
+  a.seq = seq;
+  a.hq = 0;
+  a.hkv = num_kv_heads;
+  a.dim = head_dim;
+  a.rotary_dim = 0;
+  a.k_in = x;
+  a.pos0 = pos0;
+  a.theta = 1.0;
+  a.max_ctx = max_ctx;
+  a.k_codes = codes;
+  a.k_scales = scales;
   return hip_rc(ga::launch_qk_prologue(a, static_cast<hipStream_t>(stream)));
 }
 

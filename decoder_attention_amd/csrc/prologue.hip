@@ -2,9 +2,11 @@
 //
 // Two modes: rows in, rows out (positions pos0[b] + s); or cache mode, where
 // the seq new tokens of each sequence sit at positions ctx_len[b] - seq + s
-// and their processed keys (and raw values) are written straight into the
-// contiguous caches at those rows -- the cache append of a decode or
-// chunked-prefill step.
+// (or pos0[b] + s without ctx_len) and their processed keys (and raw values)
+// are written straight into the contiguous caches at those rows -- the cache
+// append of a decode or chunked-prefill step.  An int8 cache stores each
+// (token, head) vector of the bf16-rounded result as codes
+// round-half-even(x / s) with s = max|x| / 127 (fp32 division), plus s.
 //
 // One workgroup per group of kTok consecutive tokens (flattened over batch and
 // sequence).  The rotary frequencies w_i = theta^(-2i/r) are formed once per
@@ -43,8 +45,12 @@ struct ProParams {
   const int32_t* ctx_len;     // cache mode: positions ctx_len[b] - seq + s
   const uint16_t* v_in;       // cache mode: raw values copied into v_out
   uint16_t* v_out;
+  int8_t* k_codes;            // int8 cache mode (k_scales set): codes [B,max_ctx,Hkv,D]
+  float* k_scales;            //   and scales [B,Hkv,max_ctx] replace k_out / v_out
+  int8_t* v_codes;
+  float* v_scales;
   int64_t tokens;
-  int32_t seq, hq, hkv, dim, rotary_dim, max_ctx;
+  int32_t seq, hq, hkv, dim, rotary_dim, max_ctx;   // max_ctx > 0: cache mode
   double theta;
   float eps, offset;
 };
@@ -80,18 +86,25 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
 
   // Row r of this workgroup: token tok0 + r / heads, head r % heads: the q
   // heads, then the k heads, then (cache mode) the v heads, which are copied
-  // unchanged.  In cache mode k and v rows go to cache row ctx - seq + s and
-  // are skipped when that row is outside the cache.
-  auto row_ptrs = [&](int32_t row, const uint16_t*& src, uint16_t*& dst, const float*& w, bool& copy) -> bool {
+  // unchanged.  In cache mode k and v rows go to cache row pos of their token
+  // and are skipped when that row is outside the cache; in int8 cache mode
+  // they go to the code row (cdst) and the scale slot (sdst) instead of dst.
+  struct RowDst {
+    uint16_t* dst;
+    int8_t* cdst;
+    float* sdst;
+  };
+  auto row_ptrs = [&](int32_t row, const uint16_t*& src, RowDst& out, const float*& w, bool& copy) -> bool {
     const int32_t tt = row / heads;
     const int32_t hh = row % heads;
     const int64_t token = tok0 + tt;
     copy = false;
+    out = RowDst{nullptr, nullptr, nullptr};
     if (row >= rows || token >= p.tokens) return false;
     if (hh < p.hq) {
       const int64_t off = (token * p.hq + hh) * dim + d0;
       src = p.q_in + off;
-      dst = p.q_out + off;
+      out.dst = p.q_out + off;
       w = p.qw;
       return true;
     }
@@ -100,13 +113,19 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
     src = (is_v ? p.v_in : p.k_in) + (token * p.hkv + kh) * dim + d0;
     w = is_v ? nullptr : p.kw;
     copy = is_v;
-    if (p.ctx_len) {
+    if (p.max_ctx > 0) {
       const int32_t b = static_cast<int32_t>(token / p.seq);
       const int64_t pos = token_pos(p, b, static_cast<int32_t>(token % p.seq));
       if (pos < 0 || pos >= p.max_ctx) return false;
-      dst = (is_v ? p.v_out : p.k_out) + ((static_cast<int64_t>(b) * p.max_ctx + pos) * p.hkv + kh) * dim + d0;
+      const int64_t crow = (static_cast<int64_t>(b) * p.max_ctx + pos) * p.hkv + kh;
+      if (p.k_scales) {
+        out.cdst = (is_v ? p.v_codes : p.k_codes) + crow * dim + d0;
+        out.sdst = (is_v ? p.v_scales : p.k_scales) + (static_cast<int64_t>(b) * p.hkv + kh) * p.max_ctx + pos;
+      } else {
+        out.dst = (is_v ? p.v_out : p.k_out) + crow * dim + d0;
+      }
     } else {
-      dst = p.k_out + (token * p.hkv + kh) * dim + d0;
+      out.dst = p.k_out + (token * p.hkv + kh) * dim + d0;
     }
     return true;
   };
@@ -115,10 +134,10 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
   u32x4 raw = u32x4{0u, 0u, 0u, 0u};
   {
     const uint16_t* src;
-    uint16_t* dst;
+    RowDst od;
     const float* w;
     bool cp;
-    if (row_ptrs(sub, src, dst, w, cp)) raw = *reinterpret_cast<const u32x4*>(src);
+    if (row_ptrs(sub, src, od, w, cp)) raw = *reinterpret_cast<const u32x4*>(src);
   }
 
   for (int32_t i = tid; i < half; i += kThreads) omega[i] = pow(p.theta, -2.0 * i / p.rotary_dim);
@@ -144,15 +163,15 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
   for (int32_t row0 = 0; row0 < rows; row0 += rows_per_pass) {
     const int32_t row = row0 + sub;
     const uint16_t* src = nullptr;
-    uint16_t* dst = nullptr;
+    RowDst od;
     const float* w = nullptr;
     bool copy = false;
-    const bool active = row_ptrs(row, src, dst, w, copy);
+    const bool active = row_ptrs(row, src, od, w, copy);
     // prefetch the next pass's row
     u32x4 next = u32x4{0u, 0u, 0u, 0u};
     if (row0 + rows_per_pass < rows) {
       const uint16_t* s2;
-      uint16_t* d2;
+      RowDst d2;
       const float* w2;
       bool c2;
       if (row_ptrs(row + rows_per_pass, s2, d2, w2, c2)) next = *reinterpret_cast<const u32x4*>(s2);
@@ -194,28 +213,51 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
       }
       __syncthreads();
     }
-    if (active) {
-      const int32_t tt = row / heads;
-      float y[8];
+    // Rows past the end take the last token's table (their results are dropped).
+    const int32_t tt = min(row / heads, kTok - 1);
+    float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int32_t d = d0 + e;
-        if (copy) {
-          y[e] = x[e];
-        } else if (d < half) {
-          const float2 c = cs_tab[tt][d];
-          y[e] = x[e] * c.x - partner[e] * c.y;
-        } else if (d < p.rotary_dim) {
-          const float2 c = cs_tab[tt][d - half];
-          y[e] = x[e] * c.x + partner[e] * c.y;
-        } else {
-          y[e] = x[e];
-        }
+    for (int e = 0; e < 8; ++e) {
+      const int32_t d = d0 + e;
+      if (copy) {
+        y[e] = x[e];
+      } else if (d < half) {
+        const float2 c = cs_tab[tt][d];
+        y[e] = x[e] * c.x - partner[e] * c.y;
+      } else if (d < p.rotary_dim) {
+        const float2 c = cs_tab[tt][d - half];
+        y[e] = x[e] * c.x + partner[e] * c.y;
+      } else {
+        y[e] = x[e];
       }
-      u32x4 o;
+    }
+    u32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
-      *reinterpret_cast<u32x4*>(dst) = o;
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+    if (p.k_scales) {
+      // int8 cache mode: every lane joins the row's max reduction.
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(o[e])), fabsf(hi_bf16(o[e]))));
+      for (int m = tpr >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+      if (active && od.cdst) {
+        const float sc = amax / 127.0f;
+        uint32_t cw[2] = {0u, 0u};
+        if (sc > 0.f) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = (e & 1) ? hi_bf16(o[e >> 1]) : lo_bf16(o[e >> 1]);
+            const int32_t c = static_cast<int32_t>(__builtin_rintf(v / sc));
+            cw[e >> 2] |= (static_cast<uint32_t>(c) & 0xffu) << (8 * (e & 3));
+          }
+        }
+        *reinterpret_cast<u32x2*>(od.cdst) = u32x2{cw[0], cw[1]};
+        if (lane == 0) *od.sdst = sc;
+      } else if (active) {
+        *reinterpret_cast<u32x4*>(od.dst) = o;
+      }
+    } else if (active) {
+      *reinterpret_cast<u32x4*>(od.dst) = o;
     }
     raw = next;
   }
@@ -237,6 +279,10 @@ hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream) {
   p.ctx_len = a.ctx_len;
   p.v_in = static_cast<const uint16_t*>(a.v_in);
   p.v_out = static_cast<uint16_t*>(a.v_out);
+  p.k_codes = static_cast<int8_t*>(a.k_codes);
+  p.k_scales = a.k_scales;
+  p.v_codes = static_cast<int8_t*>(a.v_codes);
+  p.v_scales = a.v_scales;
   p.max_ctx = a.max_ctx;
   p.tokens = tokens;
   p.seq = a.seq;

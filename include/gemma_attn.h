@@ -199,6 +199,53 @@ int gemma_qk_prologue_cache(const gemma_attn_config* cfg, int32_t layer_idx, int
                             void* k_cache, void* v_cache, const float* q_norm_w, const float* k_norm_w,
                             const int32_t* ctx_len, void* stream);
 
+/*
+ * int8 KV cache (the google-gemma-4 atlas summary, "Training" section: int8
+ * KV caching is offered; no format is given).  Reading adopted: symmetric
+ * absmax quantization of each (token, KV head) vector x of width D:
+ *   s = max|x| / 127 (fp32),  c = round-half-even(x / s) in [-127, 127]
+ * (fp32 division; s = 0 and c = 0 for an all-zero vector), dequantized as
+ * c * s.  Layouts: codes int8 [B,max_ctx,Hkv,D] (the bf16 cache's layout at
+ * one byte per element); scales fp32 [B,Hkv,max_ctx] (the scales of one head
+ * are contiguous over positions).  Keys are quantized after QK-norm and
+ * rotary and their bf16 rounding, values as given.
+ */
+
+/*
+ * gemma_attn_decode_multi against an int8 cache.  k_codes/k_scales hold the
+ * processed keys, v_codes/v_scales the values (both ignored, may be NULL, on
+ * keys-as-values layers, where the key codes serve as values).  Scores use
+ * s_j * (q . c_j); the value scale multiplies each probability before its
+ * bf16 rounding.  q, out, lse, ctx_len, workspace and errors as for
+ * gemma_attn_decode_multi, whose workspace size applies unchanged.  Pointers
+ * 16-byte aligned.
+ */
+int gemma_attn_decode_int8(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                           int32_t max_ctx, const void* q, const void* k_codes, const float* k_scales,
+                           const void* v_codes, const float* v_scales, const int32_t* ctx_len, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gemma_qk_prologue_cache appending to an int8 cache: the processed keys
+ * (bf16-rounded) and the raw values of the q_len new tokens are quantized
+ * into rows p = ctx_len[b] - q_len + s of the codes and scales (rows outside
+ * [0, max_ctx) skipped).  Value arguments are ignored, may be NULL, on
+ * keys-as-values layers.
+ */
+int gemma_qk_prologue_cache_int8(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                                 int32_t max_ctx, const void* q_in, const void* k_in, const void* v_in, void* q_out,
+                                 void* k_codes, float* k_scales, void* v_codes, float* v_scales,
+                                 const float* q_norm_w, const float* k_norm_w, const int32_t* ctx_len, void* stream);
+
+/*
+ * Quantize rows x [B,S,Hkv,D] bf16 (keys already processed, or values) into an
+ * int8 cache at rows pos0[b] + s (pos0: device int32 [B], NULL for zeros);
+ * rows outside [0, max_ctx) are skipped.  Fills a cache from a prefill's
+ * keys and values.  D a power of two in [8, 512].
+ */
+int gemma_kv_quantize_int8(int32_t batch, int32_t seq, int32_t num_kv_heads, int32_t head_dim, int32_t max_ctx,
+                           const void* x, const int32_t* pos0, void* codes, float* scales, void* stream);
+
 /* Static, human-readable text of an error code. */
 const char* gemma_attn_strerror(int code);
 

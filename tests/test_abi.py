@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol(ga):
     assert set(names) == {"gemma_attn_resolve_layer", "gemma_qk_prologue", "gemma_attn_prefill",
                           "gemma_attn_decode_workspace_size", "gemma_attn_decode", "gemma_attn_strerror",
                           "gemma_attn_decode_multi", "gemma_attn_decode_multi_workspace_size",
-                          "gemma_qk_prologue_cache"}
+                          "gemma_qk_prologue_cache", "gemma_attn_decode_int8", "gemma_qk_prologue_cache_int8",
+                          "gemma_kv_quantize_int8"}
     lib = ctypes.CDLL(ga.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -189,3 +190,30 @@ def test_decode_multi_workspace_covers_every_split(ga, W, max_ctx, B, q_len):
     span = min(W + q_len - 1, max_ctx) if W else max_ctx
     # one fp32 (o[D], m, l) record per (sequence, token, head, 4096-key chunk) of the longest span
     assert need >= B * q_len * 16 * (256 + 2) * 4 * -(-span // 4096)
+
+
+def test_int8_entry_points_reject_bad_arguments(ga):
+    lib, ref, fake = ga.load(), ctypes.byref, ctypes.c_void_p(1 << 20)
+    good = ga.Config(num_heads=8, num_kv_heads=4, head_dim=256).to_c()
+    keqv = ga.Config(num_heads=8, num_kv_heads=1, head_dim=512, k_eq_v=True).to_c()
+    need = lib.gemma_attn_decode_multi_workspace_size(ref(good), 0, 2, 3, 100)
+    D8 = lib.gemma_attn_decode_int8
+    assert D8(ref(good), 0, 2, 3, 100, fake, fake, None, fake, fake, fake, fake, None, fake, need,
+              None) == ga.GA_ERR_INVALID_ARG                                  # key scales missing
+    assert D8(ref(good), 0, 2, 3, 100, fake, fake, fake, fake, None, fake, fake, None, fake, need,
+              None) == ga.GA_ERR_INVALID_ARG                                  # value scales missing
+    assert D8(ref(good), 0, 2, 3, 100, fake, fake, fake, fake, fake, fake, fake, None, fake, need - 1,
+              None) == ga.GA_ERR_WORKSPACE
+    assert D8(ref(keqv), 0, 0, 3, 100, None, None, fake, None, None, None, None, None, None, 0, None) == ga.GA_OK
+    P8 = lib.gemma_qk_prologue_cache_int8
+    assert P8(ref(good), 0, 2, 4, 16, fake, fake, fake, fake, fake, None, fake, fake, None, None, fake,
+              None) == ga.GA_ERR_INVALID_ARG                                  # key scales missing
+    assert P8(ref(good), 0, 2, 4, 16, fake, fake, None, fake, fake, fake, fake, fake, None, None, fake,
+              None) == ga.GA_ERR_INVALID_ARG                                  # values missing
+    assert P8(ref(good), 0, 2, 17, 16, fake, fake, fake, fake, fake, fake, fake, fake, None, None, fake,
+              None) == ga.GA_ERR_INVALID_ARG                                  # q_len > max_ctx
+    Q = lib.gemma_kv_quantize_int8
+    assert Q(2, 4, 1, 96, 16, fake, None, fake, fake, None) == ga.GA_ERR_UNSUPPORTED
+    assert Q(2, 4, 0, 64, 16, fake, None, fake, fake, None) == ga.GA_ERR_INVALID_ARG
+    assert Q(2, 4, 1, 64, 16, fake, None, fake, None, None) == ga.GA_ERR_INVALID_ARG
+    assert Q(0, 4, 1, 64, 16, None, None, None, None, None) == ga.GA_OK
