@@ -16,7 +16,8 @@ The same JSON line also carries
   * ``decode``: the Gemma-4-12B-shaped decode step (64 sequences, contexts
     drawn from U[512, 65536]; local layer 16/8 heads D256 window 1024 and
     global layer 16/1 heads D512 keys-as-values), in GB/s of KV read against
-    8 TB/s HBM;
+    8 TB/s HBM; also 4 new tokens per sequence (``*_q4``) and the same cache
+    stored as int8 codes with per-(token, head) scales (``*_int8``);
   * ``prefill_configs``: the Gemma-3-1B-shaped 6-layer stack and the
     Gemma-4-12B-shaped global layer (TFLOP/s per layer);
   * ``cpu_baseline``: the fp64 oracle timed on the host's cores over a
@@ -248,6 +249,61 @@ def bench_decode(ga, reps=20):
         res[name] = dict(decode_ms=round(ms, 4), kv_bytes=nbytes, gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
                          frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          prologue_ms=round(float(np.median(timer.ms("prologue"))), 4))
+
+        # Several new tokens per sequence (draft verification, 4 tokens): the
+        # same cache rows plus the 3 extra rows the first token's window adds.
+        Lq = 4
+        qm = _dev_bf16(normal_bf16(seed_for(5, layer, "q") + 7, (B, Lq, 16, D)))
+        outm = torch.empty_like(qm)
+        wsm = torch.empty(ga.decode_multi_workspace_size(GEMMA4_12B, layer, B, Lq, Smax), dtype=torch.uint8,
+                          device="cuda")
+        for _ in range(2):
+            ga.attn_decode_multi(GEMMA4_12B, layer, qm, kc, vc, ctx_d, out=outm, workspace=wsm)
+        torch.cuda.synchronize()
+        tm = Timer()
+        for _ in range(reps):
+            tm.start("m")
+            ga.attn_decode_multi(GEMMA4_12B, layer, qm, kc, vc, ctx_d, out=outm, workspace=wsm)
+            tm.stop("m")
+        torch.cuda.synchronize()
+        span_m = np.minimum(ctx, W + Lq - 1) if W else ctx
+        nb_m = int(span_m.sum()) * Hkv * D * 2 * (1 if L["k_eq_v"] else 2)
+        ms_m = float(np.median(tm.ms("m")))
+        res[name + "_q4"] = dict(decode_ms=round(ms_m, 4), kv_bytes=nb_m, gbs=round(nb_m / (ms_m * 1e-3) / 1e9, 1),
+                                 frac=round(nb_m / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        del qm, outm, wsm
+
+        # int8 cache: the same rows quantized on the device (codes + one fp32
+        # scale per token and head); algorithmic bytes = codes + scales read.
+        codes, scales = [], []
+        for c in caches:
+            cc = torch.zeros((B, Smax, Hkv, D), dtype=torch.int8, device="cuda")
+            sc = torch.full((B, Hkv, Smax), float("nan"), dtype=torch.float32, device="cuda")
+            for b in range(B):
+                lo_b = max(0, int(ctx[b]) - W) if W else 0
+                p0 = torch.tensor([lo_b], dtype=torch.int32, device="cuda")
+                ga.kv_quantize_int8(c[b:b + 1, lo_b:int(ctx[b])], cc[b:b + 1], sc[b:b + 1], pos0=p0)
+            codes.append(cc)
+            scales.append(sc)
+        kq, ksq = codes[0], scales[0]
+        vq, vsq = (None, None) if L["k_eq_v"] else (codes[1], scales[1])
+        q1 = qt.view(B, 1, 16, D)
+        out1 = out.view(B, 1, 16, D)
+        for _ in range(3):
+            ga.attn_decode_int8(GEMMA4_12B, layer, q1, kq, ksq, vq, vsq, ctx_d, out=out1, workspace=ws)
+        torch.cuda.synchronize()
+        t8 = Timer()
+        for _ in range(reps):
+            t8.start("d8")
+            ga.attn_decode_int8(GEMMA4_12B, layer, q1, kq, ksq, vq, vsq, ctx_d, out=out1, workspace=ws)
+            t8.stop("d8")
+        torch.cuda.synchronize()
+        nb8 = int(span.sum()) * Hkv * (D + 4) * (1 if L["k_eq_v"] else 2)
+        ms8 = float(np.median(t8.ms("d8")))
+        res[name + "_int8"] = dict(decode_ms=round(ms8, 4), kv_bytes=nb8, gbs=round(nb8 / (ms8 * 1e-3) / 1e9, 1),
+                                   frac=round(nb8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   speedup_vs_bf16=round(ms / ms8, 3))
+        del codes, scales, kq, ksq, vq, vsq
         del caches, kc, vc
         torch.cuda.empty_cache()
     tot_bytes = 5 * res["local_w1024"]["kv_bytes"] + res["global_keqv"]["kv_bytes"]

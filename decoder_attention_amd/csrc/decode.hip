@@ -22,6 +22,8 @@
 // Sources: generate() decoding over cached keys and values (Gemma 4 page, API;
 // the atlas summary on KV caches bounded by the window on local layers), the
 // window, soft cap, scaling and keys-as-values as for prefill.
+#include <type_traits>
+
 #include "ga_device.h"
 #include "ga_kernels.h"
 
@@ -30,6 +32,14 @@ namespace ga {
 namespace {
 
 constexpr int kTK = 16;     // keys per wave tile
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: low 4 bits and bits 14-15), leaving the
+// export and LDS counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 struct DecodeParams {
   const uint16_t* q;
@@ -368,6 +378,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int kTeams = Sh::kTeams;
   constexpr int kDW = D / kTeam;     // D slice of one wave's accumulators
   constexpr int kDS = D / 64;        // 16-byte key chunks per lane per half (two MFMAs each)
+  constexpr int kDSW = kDS / kTeam;  // of them, this wave's share (a team splits the score product by D)
   constexpr int kDB = kDW / 16;      // 16-row blocks of this wave's O^T
   constexpr int kRowChunks = D / 16; // 16-byte chunks per cache row
   constexpr int kSlotBytes = kTK8 * D;
@@ -376,17 +387,32 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(G <= 16, "at most 16 query heads per KV head");
   static_assert(kOps % kTeam == 0, "tile must split into whole 1 KB ops");
   static_assert(kTeams == 1 || kSlotBytes * kTeams >= 16 * D * 4, "merge buffer reuses slot 0");
+  // Ring depth.  Two slots (one tile in flight while one is computed): the
+  // conversion work makes this kernel issue-bound, and a third 16 KB slot at
+  // head width 512 halves the workgroups per CU, which measured slower.
+  constexpr int kSlots = 2;
+  // Copy ops each wave issues per tile (codes, then scales): the wait for the
+  // oldest tile leaves the newer tile's ops outstanding.
+  constexpr int kCodeOps = kWaveOps * (KEQV ? 1 : 2);
+  constexpr int kOpsMember0 = kCodeOps + (kTeam == 1 ? (KEQV ? 1 : 2) : 1);
+  constexpr int kOpsMember1 = kCodeOps + (KEQV ? 0 : 1);
 
   __shared__ __attribute__((aligned(16))) uint8_t ks0[kTeams * kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ks1[kTeams * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ks2[kSlots > 2 ? kTeams * kSlotBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t vs0[KEQV ? 16 : kTeams * kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vs1[KEQV ? 16 : kTeams * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vs2[(KEQV || kSlots < 3) ? 16 : kTeams * kSlotBytes];
   __shared__ __attribute__((aligned(16))) float ksc0[kTeams * 64];
   __shared__ __attribute__((aligned(16))) float ksc1[kTeams * 64];
+  __shared__ __attribute__((aligned(16))) float ksc2[kSlots > 2 ? kTeams * 64 : 4];
   __shared__ __attribute__((aligned(16))) float vsc0[KEQV ? 4 : kTeams * 64];
   __shared__ __attribute__((aligned(16))) float vsc1[KEQV ? 4 : kTeams * 64];
+  __shared__ __attribute__((aligned(16))) float vsc2[(KEQV || kSlots < 3) ? 4 : kTeams * 64];
   __shared__ float m_w[2][16];
   __shared__ float l_w[2][16];
+  // Partial scores of a two-wave team: [member][half][lane].
+  __shared__ f32x4 sx[kTeam > 1 ? 2 * 2 * 64 : 1];
 
   const int32_t split = blockIdx.x;
   const int32_t kvh = static_cast<int32_t>(blockIdx.y) / p.n_cb;
@@ -415,14 +441,16 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int32_t key_lo = p.window > 0 ? key_hi - p.window + 1 : 0;
 
   // Q^T operand: step ds, MFMA m: lane holds d = (ds*4 + grp)*16 + m*8 + [0, 8),
-  // the d range of the key chunk (ds*4 + grp) that the K operand lane reads.
-  bf16x8 qf[kDS][2];
+  // the d range of the key chunk (ds*4 + grp) that the K operand lane reads;
+  // this wave's steps are ds = member*kDSW + [0, kDSW).
+  bf16x8 qf[kDSW][2];
   {
     const uint16_t* qrow = p.q + ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * D + grp * 16;
 #pragma unroll
-    for (int ds = 0; ds < kDS; ++ds) {
-      qf[ds][0] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 64) : bf16x8{};
-      qf[ds][1] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 64 + 8) : bf16x8{};
+    for (int i = 0; i < kDSW; ++i) {
+      const int ds = member * kDSW + i;
+      qf[i][0] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 64) : bf16x8{};
+      qf[i][1] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 64 + 8) : bf16x8{};
     }
   }
 
@@ -444,7 +472,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // tile's key scales and the last member its value scales (64 lanes, key
   // lane & 31, so the upper half repeats the lower).  Rows past s_hi repeat
   // row s_hi - 1.
-  auto copy_tile = [&](int32_t ti, uint8_t* kdst, uint8_t* vdst, float* kscd, float* vscd) {
+  auto copy_tile = [&](int32_t ti, uint8_t* kdst, uint8_t* vdst, float* kscd, float* vscd) __attribute__((always_inline)) {
     const int32_t k0 = s_lo + ti * kTK8;
     const int32_t last = s_hi - 1 - k0;
     const char* kb = kseq + static_cast<int64_t>(k0) * row_pitch;
@@ -475,12 +503,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  auto compute = [&](int32_t ti, const uint8_t* kb, const uint8_t* vb, const float* kscs, const float* vscs) {
+  auto compute = [&](int32_t ti, const uint8_t* kb, const uint8_t* vb, const float* kscs, const float* vscs) __attribute__((always_inline)) {
     const int32_t k0 = s_lo + ti * kTK8;
     const int32_t ln = lane_here();
     const int32_t li16 = ln & 15;
     const int32_t lgrp = ln >> 4;
-    // S^T[32 keys x 16 columns] in two 16-key halves.
+    // S^T[32 keys x 16 columns] in two 16-key halves (this wave's share of D).
     f32x4 sacc[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -488,12 +516,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int32_t row = h2 * 16 + li16;
       const int32_t sw = qswz<D>(row);
 #pragma unroll
-      for (int ds = 0; ds < kDS; ++ds) {
-        const int32_t c = ds * 4 + lgrp;
+      for (int i = 0; i < kDSW; ++i) {
+        const int32_t c = (member * kDSW + i) * 4 + lgrp;
         const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + row * D + ((c ^ sw) << 4));
-        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(raw[0], raw[1]), qf[ds][0], sacc[h2], 0, 0, 0);
-        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(raw[2], raw[3]), qf[ds][1], sacc[h2], 0, 0, 0);
+        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(raw[0], raw[1]), qf[i][0], sacc[h2], 0, 0, 0);
+        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(raw[2], raw[3]), qf[i][1], sacc[h2], 0, 0, 0);
       }
+    }
+    if constexpr (kTeam > 1) {
+      // Add the partner's half of D.  Both members form p0 + p1 (fp32 addition
+      // commutes), so they hold bit-identical scores.  The buffer is rewritten
+      // only after the next tile's team barrier, which follows this read.
+      sx[(member * 2 + 0) * 64 + ln] = sacc[0];
+      sx[(member * 2 + 1) * 64 + ln] = sacc[1];
+      __syncthreads();
+      sacc[0] += sx[((1 - member) * 2 + 0) * 64 + ln];
+      sacc[1] += sx[((1 - member) * 2 + 1) * 64 + ln];
     }
     // Lane holds keys k0 + h2*16 + grp*4 + r as x[h2*4 + r].
     const f32x4 ksa = *reinterpret_cast<const f32x4*>(kscs + grp * 4);
@@ -556,33 +594,72 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  uint8_t* k0s = ks0 + team * kSlotBytes;
-  uint8_t* k1s = ks1 + team * kSlotBytes;
-  uint8_t* v0s = KEQV ? k0s : vs0 + team * kSlotBytes;
-  uint8_t* v1s = KEQV ? k1s : vs1 + team * kSlotBytes;
-  float* kl0 = ksc0 + team * 64;
-  float* kl1 = ksc1 + team * 64;
-  float* vl0 = KEQV ? kl0 : vsc0 + team * 64;
-  float* vl1 = KEQV ? kl1 : vsc1 + team * 64;
+  // Slot I of this team (compile-time I, so each access names one LDS array).
+  auto kslot = [&](auto I) -> uint8_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return ks0 + team * kSlotBytes;
+    else if constexpr (i == 1) return ks1 + team * kSlotBytes;
+    else return ks2 + team * kSlotBytes;
+  };
+  auto vslot = [&](auto I) -> uint8_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (KEQV) return kslot(I);
+    else if constexpr (i == 0) return vs0 + team * kSlotBytes;
+    else if constexpr (i == 1) return vs1 + team * kSlotBytes;
+    else return vs2 + team * kSlotBytes;
+  };
+  auto kscl = [&](auto I) -> float* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return ksc0 + team * 64;
+    else if constexpr (i == 1) return ksc1 + team * 64;
+    else return ksc2 + team * 64;
+  };
+  auto vscl = [&](auto I) -> float* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (KEQV) return kscl(I);
+    else if constexpr (i == 0) return vsc0 + team * 64;
+    else if constexpr (i == 1) return vsc1 + team * 64;
+    else return vsc2 + team * 64;
+  };
   auto team_sync = [&]() {
     if constexpr (kTeam > 1) __syncthreads();
   };
+  // Wait for the oldest tile in flight: with a newer tile also in flight its
+  // ops stay outstanding.
+  auto wait_oldest = [&](bool newer_in_flight) __attribute__((always_inline)) {
+    if (kSlots > 2 && newer_in_flight) {
+      if (member == 0) wait_vmcnt<kOpsMember0>();
+      else wait_vmcnt<kOpsMember1>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  };
+  // The team's tiles are ti = team, team + kTeams, ...; tile k of the team
+  // sits in slot k % kSlots.
   int32_t ti = team;
-  if (ti < n_t) copy_tile(ti, k0s, v0s, kl0, vl0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (ti < n_t) copy_tile(ti, kslot(S0{}), vslot(S0{}), kscl(S0{}), vscl(S0{}));
+  if constexpr (kSlots > 2) {
+    if (ti + kTeams < n_t) copy_tile(ti + kTeams, kslot(S1{}), vslot(S1{}), kscl(S1{}), vscl(S1{}));
+  }
+  auto step = [&](auto I) __attribute__((always_inline)) -> bool {
+    constexpr int kCur = decltype(I)::value;
+    using Next = std::integral_constant<int, (kCur + kSlots - 1) % kSlots>;
+    wait_oldest(ti + kTeams < n_t);
+    team_sync();
+    const int32_t ta = ti + (kSlots - 1) * kTeams;
+    if (ta < n_t) copy_tile(ta, kslot(Next{}), vslot(Next{}), kscl(Next{}), vscl(Next{}));
+    compute(ti, kslot(I), vslot(I), kscl(I), vscl(I));
+    ti += kTeams;
+    return ti < n_t;
+  };
   while (ti < n_t) {
-    const int32_t tn = ti + kTeams;
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-    team_sync();
-    if (tn < n_t) copy_tile(tn, k1s, v1s, kl1, vl1);
-    compute(ti, k0s, v0s, kl0, vl0);
-    ti = tn;
-    if (ti >= n_t) break;
-    const int32_t tn2 = ti + kTeams;
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-    team_sync();
-    if (tn2 < n_t) copy_tile(tn2, k0s, v0s, kl0, vl0);
-    compute(ti, k1s, v1s, kl1, vl1);
-    ti = tn2;
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
+    if constexpr (kSlots > 2) {
+      if (!step(std::integral_constant<int, 2>{})) break;
+    }
   }
 
   l_run += __shfl_xor(l_run, 16, 64);
