@@ -53,9 +53,12 @@ def brute_layer(p: dict, layer_idx, q, k, v=None, q_norm_w=None, k_norm_w=None, 
     ``p`` uses the pages' knob names (same meaning as the oracle's config).
     """
     kind = layer_kind(p.get("sliding_window_pattern", 1), p.get("sliding_window", 0), layer_idx)
+    pos_div = 1.0
     if kind == "global":
         W = 0
         theta = p["rope_theta"]
+        if (p.get("rope_scaling_factor") or 0) > 0:
+            pos_div = float(p["rope_scaling_factor"])
         hkv = p.get("num_global_kv_heads") or p["num_kv_heads"]
         D = p.get("global_head_dim") or p["head_dim"]
         tied = bool(p.get("k_eq_v", False))
@@ -85,7 +88,7 @@ def brute_layer(p: dict, layer_idx, q, k, v=None, q_norm_w=None, k_norm_w=None, 
             vec = [float(x) for x in vec]
             if w is not None:
                 vec = _norm(vec, w, eps, off)
-            return _rope(vec, base + s, theta, r)
+            return _rope(vec, (base + s) / pos_div, theta, r)
 
         kk = [[prep(k[b][s][h], k_norm_w, s) for h in range(hkv)] for s in range(S)]
         vv = kk if tied else [[[float(x) for x in v[b][s][h]] for h in range(hkv)] for s in range(S)]

@@ -43,6 +43,7 @@ class GemmaAttnConfig:
     ``attn_logit_softcapping`` <= 0 disables the cap.
     ``query_pre_attn_scalar`` <= 0 means the layer's head width.
     ``norm_weight_offset`` 1 multiplies by (1 + w) (Gemma 1-3), 0 by w (Gemma 4).
+    ``rope_scaling_factor`` > 0: global layers divide positions by it; <= 0: off.
     """
 
     num_heads: int
@@ -60,6 +61,7 @@ class GemmaAttnConfig:
     k_eq_v: bool = False
     norm_eps: float = 1e-6
     norm_weight_offset: int = 0
+    rope_scaling_factor: float = 0.0
 
 
 def resolve_layer(cfg: GemmaAttnConfig, layer_idx: int) -> dict:
@@ -93,6 +95,8 @@ def resolve_layer(cfg: GemmaAttnConfig, layer_idx: int) -> dict:
     if hkv <= 0 or cfg.num_heads % hkv != 0:
         raise ValueError("num_heads must be a multiple of the KV-head count")
     rotary_dim = 2 * int(math.floor(float(cfg.partial_rotary_factor) * dim / 2.0))
+    factor = float(getattr(cfg, "rope_scaling_factor", 0.0) or 0.0)
+    pos_div = factor if (is_global and factor > 0) else 1.0
     qpas = float(cfg.query_pre_attn_scalar) if cfg.query_pre_attn_scalar > 0 else float(dim)
     return dict(
         is_global=bool(is_global),
@@ -105,6 +109,7 @@ def resolve_layer(cfg: GemmaAttnConfig, layer_idx: int) -> dict:
         k_eq_v=kv_eq,
         scale=qpas ** -0.5,
         softcap=float(cfg.attn_logit_softcapping) if cfg.attn_logit_softcapping > 0 else 0.0,
+        pos_div=pos_div,
     )
 
 
@@ -197,14 +202,17 @@ def allowed(i: np.ndarray, j: np.ndarray, window: int) -> np.ndarray:
 def prologue(cfg, layer_idx, q, k=None, q_norm_w=None, k_norm_w=None, pos0=None):
     """QK-norm then rotary on q [B,S,Hq,D] and k [B,S,Hkv,D]; returns fp64 arrays.
 
-    Positions are ``pos0[b] + s`` (``pos0`` defaults to zeros).  The norm is
-    applied only when its weight is given.  Values are never normed or rotated.
+    Positions are ``pos0[b] + s`` (``pos0`` defaults to zeros), divided by the
+    layer's ``pos_div`` (rope scaling).  The norm is applied only when its
+    weight is given.  Values are never normed or rotated.
     """
     L = resolve_layer(cfg, layer_idx)
     q = np.asarray(q, dtype=np.float64)
     B, S = q.shape[0], q.shape[1]
     p0 = np.zeros(B, dtype=np.int64) if pos0 is None else np.asarray(pos0, dtype=np.int64)
     positions = p0[:, None] + np.arange(S, dtype=np.int64)[None, :]
+    if L["pos_div"] != 1.0:
+        positions = positions.astype(np.float64) / L["pos_div"]
 
     def one(x, w):
         if w is not None:

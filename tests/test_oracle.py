@@ -312,3 +312,66 @@ def test_decode_multi_equals_prefill_tail_and_decode(W, tied):
     # more new tokens than context: early tokens see nothing
     oz, lz = R.decode_multi(cfg, 0, q[:, :3], kc, vc, [2, 2])
     assert np.all(oz[:, 0] == 0) and np.all(np.isneginf(lz[:, :, 0]))
+
+
+# --------------------------------------------------------------------------- rope scaling
+def _scaled_cfg(factor, **kw):
+    base = dict(num_heads=4, num_kv_heads=2, head_dim=8, num_global_kv_heads=1, global_head_dim=16,
+                sliding_window=4, sliding_window_pattern=3, rope_theta=1e4, rope_local_theta=1e3,
+                partial_rotary_factor=0.5, norm_weight_offset=0, rope_scaling_factor=factor)
+    base.update(kw)
+    return R.GemmaAttnConfig(**base)
+
+
+@pytest.mark.parametrize("layer", [0, 2])
+def test_rope_scaling_matches_brute_force(layer):
+    cfg = _scaled_cfg(4.0)
+    Lr = R.resolve_layer(cfg, layer)
+    assert Lr["pos_div"] == (4.0 if Lr["is_global"] else 1.0)
+    D, Hkv = Lr["head_dim"], Lr["num_kv_heads"]
+    q, k, v = _inputs(13, 2, 9, 4, Hkv, D, qscale=2.0)
+    pos0 = np.array([3, 1001])
+    qt, kt = R.prologue(cfg, layer, q, k, pos0=pos0)
+    o, l = R.prefill(cfg, layer, qt, kt, v)
+    ob, lb = brute_layer(_cfg_dict(cfg), layer, q.tolist(), k.tolist(), v.tolist(), pos0=pos0.tolist())
+    assert np.abs(o - np.array(ob)).max() < TOL
+    assert np.abs(l - np.array(lb)).max() < TOL
+
+
+def test_rope_scaling_divides_global_positions_only():
+    """Closed form: with factor f, global position f*m rotates like position m
+    without scaling (exactly, f a power of two); local layers ignore f."""
+    q, k, _ = _inputs(17, 2, 6, 4, 1, 16)
+    f = 8.0
+    m = np.array([5, 123])
+    qs, ks = R.prologue(_scaled_cfg(f), 2, q, k, pos0=(m * 8))
+    q0, k0 = R.prologue(_scaled_cfg(0.0), 2, q, k, pos0=m)
+    # positions (8m + s) / 8 = m + s/8: compare at s = 0 only, where they coincide
+    assert np.array_equal(qs[:, 0], q0[:, 0]) and np.array_equal(ks[:, 0], k0[:, 0])
+    ql, kl = _inputs(19, 2, 6, 4, 2, 8)[:2]
+    a = R.prologue(_scaled_cfg(f), 0, ql, kl, pos0=m)
+    b = R.prologue(_scaled_cfg(0.0), 0, ql, kl, pos0=m)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # and scaling changes the global rotation elsewhere
+    assert not np.allclose(qs[:, 1:], R.prologue(_scaled_cfg(0.0), 2, q, k, pos0=(m * 8))[0][:, 1:])
+
+
+def test_rope_scaling_mutants_are_caught(monkeypatch):
+    orig = R.resolve_layer
+
+    def on_local_layers_too(cfg, layer_idx):
+        L = dict(orig(cfg, layer_idx))
+        L["pos_div"] = float(cfg.rope_scaling_factor)
+        return L
+
+    def multiplied(cfg, layer_idx):
+        L = dict(orig(cfg, layer_idx))
+        if L["pos_div"] != 1.0:
+            L["pos_div"] = 1.0 / L["pos_div"]
+        return L
+
+    for mutant, layer in ((on_local_layers_too, 0), (multiplied, 2)):
+        monkeypatch.setattr(R, "resolve_layer", mutant)
+        with pytest.raises(AssertionError):
+            test_rope_scaling_matches_brute_force(layer)
+        monkeypatch.setattr(R, "resolve_layer", orig)
