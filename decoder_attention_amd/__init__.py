@@ -48,6 +48,7 @@ class CConfig(ctypes.Structure):
         ("attn_logit_softcapping", ctypes.c_double),
         ("query_pre_attn_scalar", ctypes.c_double),
         ("norm_eps", ctypes.c_double),
+        ("rope_scaling_factor", ctypes.c_double),
     ]
 
 
@@ -66,6 +67,7 @@ class CLayer(ctypes.Structure):
         ("theta", ctypes.c_double),
         ("scale", ctypes.c_double),
         ("softcap", ctypes.c_double),
+        ("pos_div", ctypes.c_double),
     ]
 
 
@@ -88,6 +90,7 @@ class Config:
     k_eq_v: bool = False
     norm_eps: float = 1e-6
     norm_weight_offset: int = 0
+    rope_scaling_factor: float = 0.0
 
     def to_c(self) -> CConfig:
         return CConfig(
@@ -99,7 +102,8 @@ class Config:
             rope_theta=float(self.rope_theta), rope_local_theta=float(self.rope_local_theta),
             partial_rotary_factor=float(self.partial_rotary_factor),
             attn_logit_softcapping=float(self.attn_logit_softcapping),
-            query_pre_attn_scalar=float(self.query_pre_attn_scalar), norm_eps=float(self.norm_eps))
+            query_pre_attn_scalar=float(self.query_pre_attn_scalar), norm_eps=float(self.norm_eps),
+            rope_scaling_factor=float(self.rope_scaling_factor or 0.0))
 
     @classmethod
     def from_any(cls, obj) -> "Config":

@@ -16,6 +16,7 @@ struct PrologueArgs {
   const float* k_norm_w;
   const int32_t* pos0;
   double theta;
+  double pos_div;             // rotary positions are divided by this (rope scaling)
   float eps, offset;
   // Cache mode (max_ctx > 0): token s of sequence b sits at position
   // ctx_len[b] - seq + s (pos0[b] + s when ctx_len is null); k_out and v_out

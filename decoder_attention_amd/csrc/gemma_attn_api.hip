@@ -117,6 +117,7 @@ int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
   a.k_norm_w = k_norm_w;
   a.pos0 = pos0;
   a.theta = L.theta;
+  a.pos_div = L.pos_div;
   a.eps = static_cast<float>(cfg->norm_eps);
   a.offset = static_cast<float>(cfg->norm_weight_offset);
   a.ctx_len = nullptr;
@@ -225,6 +226,7 @@ int gemma_qk_prologue_cache(const gemma_attn_config* cfg, int32_t layer_idx, int
   a.k_norm_w = k_norm_w;
   a.pos0 = nullptr;
   a.theta = L.theta;
+  a.pos_div = L.pos_div;
   a.eps = static_cast<float>(cfg->norm_eps);
   a.offset = static_cast<float>(cfg->norm_weight_offset);
   a.ctx_len = ctx_len;
@@ -262,6 +264,7 @@ int gemma_qk_prologue_cache_int8(const gemma_attn_config* cfg, int32_t layer_idx
   a.q_norm_w = q_norm_w;
   a.k_norm_w = k_norm_w;
   a.theta = L.theta;
+  a.pos_div = L.pos_div;
   a.eps = static_cast<float>(cfg->norm_eps);
   a.offset = static_cast<float>(cfg->norm_weight_offset);
   a.ctx_len = ctx_len;
@@ -294,6 +297,7 @@ int gemma_kv_quantize_int8(int32_t batch, int32_t seq, int32_t num_kv_heads, int
   a.k_in = x;
   a.pos0 = pos0;
   a.theta = 1.0;
+  a.pos_div = 1.0;
   a.max_ctx = max_ctx;
   a.k_codes = codes;
   a.k_scales = scales;

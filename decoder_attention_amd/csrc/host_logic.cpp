@@ -24,6 +24,7 @@ int validate_config(const gemma_attn_config* c) {
   if (!(c->partial_rotary_factor >= 0.0 && c->partial_rotary_factor <= 1.0)) return GA_ERR_INVALID_ARG;
   if (!finite(c->attn_logit_softcapping) || !finite(c->query_pre_attn_scalar)) return GA_ERR_INVALID_ARG;
   if (!finite(c->norm_eps) || !(c->norm_eps > 0.0)) return GA_ERR_INVALID_ARG;
+  if (!finite(c->rope_scaling_factor)) return GA_ERR_INVALID_ARG;
   if (c->num_heads % c->num_kv_heads != 0) return GA_ERR_INVALID_ARG;
   const int32_t hg = c->num_global_kv_heads > 0 ? c->num_global_kv_heads : c->num_kv_heads;
   if (c->num_heads % hg != 0) return GA_ERR_INVALID_ARG;
@@ -60,6 +61,8 @@ int resolve_layer(const gemma_attn_config* c, int32_t layer_idx, gemma_attn_laye
   const double qpas = c->query_pre_attn_scalar > 0.0 ? c->query_pre_attn_scalar : static_cast<double>(L.head_dim);
   L.scale = std::pow(qpas, -0.5);
   L.softcap = c->attn_logit_softcapping > 0.0 ? c->attn_logit_softcapping : 0.0;
+  // Long-context rope scaling, read as linear position division on the global layers.
+  L.pos_div = (is_global && c->rope_scaling_factor > 0.0) ? c->rope_scaling_factor : 1.0;
   *out = L;
   return GA_OK;
 }

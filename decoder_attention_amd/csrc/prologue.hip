@@ -52,6 +52,7 @@ struct ProParams {
   int64_t tokens;
   int32_t seq, hq, hkv, dim, rotary_dim, max_ctx;   // max_ctx > 0: cache mode
   double theta;
+  double pos_div;
   float eps, offset;
 };
 
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
     if (row_ptrs(sub, src, od, w, cp)) raw = *reinterpret_cast<const u32x4*>(src);
   }
 
-  for (int32_t i = tid; i < half; i += kThreads) omega[i] = pow(p.theta, -2.0 * i / p.rotary_dim);
+  // (p / pos_div) * w_i, formed as p * (w_i / pos_div).
+  for (int32_t i = tid; i < half; i += kThreads) omega[i] = pow(p.theta, -2.0 * i / p.rotary_dim) / p.pos_div;
   __syncthreads();
   for (int32_t e = tid; e < kTok * half; e += kThreads) {
     const int32_t tt = e / half;
@@ -291,6 +293,7 @@ hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream) {
   p.dim = a.dim;
   p.rotary_dim = a.rotary_dim;
   p.theta = a.theta;
+  p.pos_div = a.pos_div > 0.0 ? a.pos_div : 1.0;
   p.eps = a.eps;
   p.offset = a.offset;
   const int64_t blocks = (tokens + kTok - 1) / kTok;

@@ -65,6 +65,9 @@ typedef struct gemma_attn_config {
   double attn_logit_softcapping;  /* tanh cap on scaled logits; <= 0: off (Gemma 2: 50) */
   double query_pre_attn_scalar;   /* logits scale = this^-1/2; <= 0: the layer's D (Gemma 2/3: 256) */
   double norm_eps;                /* QK-norm epsilon inside the root (1e-6) */
+  double rope_scaling_factor;     /* > 0: global layers take position p / factor in the rotary
+                                     angle (Gemma 3 table, long-context scaling; read as linear);
+                                     <= 0: off */
 } gemma_attn_config;
 
 /* Values one layer resolves to (see gemma_attn_resolve_layer). */
@@ -80,6 +83,8 @@ typedef struct gemma_attn_layer {
   double theta;         /* rotary base of this layer */
   double scale;         /* query_pre_attn_scalar^-1/2 (or D^-1/2) */
   double softcap;       /* cap, or 0 when off */
+  double pos_div;       /* rotary positions are divided by this (rope_scaling_factor on
+                           global layers, else 1) */
 } gemma_attn_layer;
 
 /*
@@ -87,8 +92,9 @@ typedef struct gemma_attn_layer {
  * Local/global interleave: "one global layer every N" (Gemma 3 table,
  * sliding_window_pattern; Gemma 2 introduction: every other layer), read as
  * local layers first in each period.  Global layers take the global KV-head
- * count, global head width and keys-as-values flag (Gemma 4 table); local
- * layers take rope_local_theta (Gemma 3 "Dual RoPE bases").
+ * count, global head width and keys-as-values flag (Gemma 4 table) and the
+ * rope scaling factor; local layers take rope_local_theta (Gemma 3 "Dual RoPE
+ * bases").
  * Returns GA_ERR_INVALID_ARG for a null pointer, a negative layer, or a config
  * that fails validation (Hq not a multiple of Hkv, a non-positive D, a factor
  * outside [0, 1], a non-positive theta or eps).
@@ -101,7 +107,8 @@ int gemma_attn_resolve_layer(const gemma_attn_config* cfg, int32_t layer_idx, ge
  *   1. if a norm weight w is given: x <- x / sqrt(mean(x^2) + eps) * (w + offset)
  *      (RMSNorm; Gemma 4 "Plain-weight RMSNorm" uses offset 0);
  *   2. the first r dims rotate in pairs (i, i + r/2) by the angle
- *      p * theta^(-2i/r) with p = pos0[b] + s; dims [r, D) pass through
+ *      (p / pos_div) * theta^(-2i/r) with p = pos0[b] + s (pos_div: the
+ *      layer's rope scaling, 1 when off); dims [r, D) pass through
  *      (Gemma 4 "Zero-pad partial rope"; r from partial_rotary_factor).
  * q_in [B,S,Hq,D] -> q_out, k_in [B,S,Hkv,D] -> k_out; bf16.  Outputs may alias
  * their inputs exactly (in place) but must not partially overlap them.

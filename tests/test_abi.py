@@ -45,16 +45,18 @@ def test_exports_every_declared_symbol(ga):
 def test_struct_layout_matches_c(tmp_path):
     src = tmp_path / "sz.c"
     src.write_text('#include "gemma_attn.h"\n#include <stdio.h>\n#include <stddef.h>\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(gemma_attn_config), sizeof(gemma_attn_layer),'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(gemma_attn_config), sizeof(gemma_attn_layer),'
                    ' offsetof(gemma_attn_config, rope_theta), offsetof(gemma_attn_config, norm_eps),'
-                   ' offsetof(gemma_attn_layer, softcap)); return 0;}\n')
+                   ' offsetof(gemma_attn_layer, softcap), offsetof(gemma_attn_config, rope_scaling_factor),'
+                   ' offsetof(gemma_attn_layer, pos_div)); return 0;}\n')
     exe = tmp_path / "sz"
     subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
     got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
     import decoder_attention_amd as ga
 
     assert got == [ctypes.sizeof(ga.CConfig), ctypes.sizeof(ga.CLayer), ga.CConfig.rope_theta.offset,
-                   ga.CConfig.norm_eps.offset, ga.CLayer.softcap.offset]
+                   ga.CConfig.norm_eps.offset, ga.CLayer.softcap.offset, ga.CConfig.rope_scaling_factor.offset,
+                   ga.CLayer.pos_div.offset]
 
 
 CFGS = [
@@ -69,6 +71,8 @@ CFGS = [
          partial_rotary_factor=0.3),
     dict(num_heads=6, num_kv_heads=3, head_dim=96, sliding_window=7, sliding_window_pattern=1,
          partial_rotary_factor=0.7, query_pre_attn_scalar=10.0),
+    dict(num_heads=4, num_kv_heads=1, head_dim=256, sliding_window=512, sliding_window_pattern=6, rope_theta=1e6,
+         rope_local_theta=1e4, rope_scaling_factor=8.0),
 ]
 
 
@@ -79,7 +83,7 @@ def test_resolve_layer_matches_oracle(ga, kw):
         a = ga.resolve_layer(kw, layer)
         b = R.resolve_layer(cfg, layer)
         for key in ("is_global", "window", "num_kv_heads", "head_dim", "group", "rotary_dim", "k_eq_v", "theta",
-                    "scale", "softcap"):
+                    "scale", "softcap", "pos_div"):
             assert a[key] == b[key], (layer, key, a[key], b[key])
 
 
@@ -93,6 +97,7 @@ BAD = [
     dict(num_heads=8, num_kv_heads=4, head_dim=64, norm_eps=0.0),
     dict(num_heads=8, num_kv_heads=4, head_dim=64, norm_weight_offset=2),
     dict(num_heads=8, num_kv_heads=4, head_dim=64, attn_logit_softcapping=float("inf")),
+    dict(num_heads=8, num_kv_heads=4, head_dim=64, rope_scaling_factor=float("nan")),
 ]
 
 

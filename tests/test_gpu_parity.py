@@ -83,6 +83,9 @@ PRO = [
     ("d256_norm1", GEMMA3, 0, 1, [0, 70000]),
     ("d512_partial_norm0", GEMMA4, 5, 0, [3, 65535]),
     ("d256_partial_local", GEMMA4, 1, 0, [0, 12345]),
+    ("d256_global_rope_scaled8", GEMMA3 | dict(rope_scaling_factor=8.0), 5, 1, [5, 98765]),
+    ("d512_global_rope_scaled3", GEMMA4 | dict(rope_scaling_factor=3.0), 5, 0, [0, 200001]),
+    ("d256_local_ignores_scaling", GEMMA3 | dict(rope_scaling_factor=8.0), 0, 1, [7, 4321]),
 ]
 
 
