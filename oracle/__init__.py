@@ -38,6 +38,7 @@ from .gemma_ref import (  # noqa: F401
     prologue,
     prefill,
     prefill_rows,
+    prefill_ragged,
     decode,
     decode_multi,
     quantize_int8,

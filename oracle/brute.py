@@ -47,10 +47,12 @@ def _rope(vec, pos, theta, r):
     return out
 
 
-def brute_layer(p: dict, layer_idx, q, k, v=None, q_norm_w=None, k_norm_w=None, pos0=None):
+def brute_layer(p: dict, layer_idx, q, k, v=None, q_norm_w=None, k_norm_w=None, pos0=None, keep=None):
     """Whole layer (QK-norm, rotary, attention) for tiny shapes.
 
     ``p`` uses the pages' knob names (same meaning as the oracle's config).
+    ``keep`` (optional, [B][S] of 0/1) is an attention mask: a position with 0
+    is neither a query (its output row is 0, lse -inf) nor a key.
     """
     kind = layer_kind(p.get("sliding_window_pattern", 1), p.get("sliding_window", 0), layer_idx)
     pos_div = 1.0
@@ -93,8 +95,10 @@ def brute_layer(p: dict, layer_idx, q, k, v=None, q_norm_w=None, k_norm_w=None, 
         kk = [[prep(k[b][s][h], k_norm_w, s) for h in range(hkv)] for s in range(S)]
         vv = kk if tied else [[[float(x) for x in v[b][s][h]] for h in range(hkv)] for s in range(S)]
         for s in range(S):
+            if keep is not None and not keep[b][s]:
+                continue
             lo = 0 if W == 0 else max(0, s - W + 1)
-            visible = list(range(lo, s + 1))
+            visible = [j for j in range(lo, s + 1) if keep is None or keep[b][j]]
             for h in range(Hq):
                 qq = prep(q[b][s][h], q_norm_w, s)
                 kh = kv_of[h]

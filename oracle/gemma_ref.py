@@ -290,6 +290,34 @@ def prefill(cfg, layer_idx, q, k, v=None, block_rows: int = 256, threads: int | 
     return out, lse
 
 
+def prefill_ragged(cfg, layer_idx, q, k, v, seq_start, seq_end):
+    """Prefill of a padded batch: sequence b keeps rows [start_b, end_b).
+
+    The Gemma pages' generate() takes an attention_mask (batch, seq) with 1 =
+    keep and 0 = padding.  Reading: padding is contiguous at the ends (left
+    padding for batched generation, right padding for ragged lengths), so the
+    mask is the range [start_b, end_b); padded tokens are neither queries nor
+    keys.  The mask is positional (i - j), so attention over the kept rows is
+    the plain prefill of the slice; padded rows give out = 0, lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, S, Hq, D = q.shape
+    k = np.asarray(k, dtype=np.float64)
+    L = resolve_layer(cfg, layer_idx)
+    vv = k if L["k_eq_v"] else np.asarray(v, dtype=np.float64)
+    out = np.zeros((B, S, Hq, vv.shape[-1]))
+    lse = np.full((B, Hq, S), -np.inf)
+    for b in range(B):
+        lo = min(max(int(seq_start[b]), 0), S)
+        hi = min(max(int(seq_end[b]), lo), S)
+        if hi == lo:
+            continue
+        o, l = prefill(cfg, layer_idx, q[b:b + 1, lo:hi], k[b:b + 1, lo:hi], None if L["k_eq_v"] else vv[b:b + 1, lo:hi])
+        out[b, lo:hi] = o[0]
+        lse[b, :, lo:hi] = l[0]
+    return out, lse
+
+
 def prefill_rows(cfg, layer_idx, q_rows, k, v, rows):
     """Attention for a sample of query rows only.
 
@@ -345,15 +373,16 @@ def decode(cfg, layer_idx, q, k_cache, v_cache, ctx_len, batches=None):
     return out, lse
 
 
-def decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len):
+def decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len, kv_start=None):
     """Several new tokens per sequence against a contiguous cache.
 
     q [B,L,Hq,D] holds the processed queries of the tokens at positions
     ctx_b - L + t (reading: the cache already holds the new tokens, as in
     single-token decode).  Token t at position i sees cache rows j with
     0 <= j <= i and, on local layers, i - j < W -- the prefill mask.  A token
-    with i < 0 sees nothing (out 0, lse -inf).  Returns out [B,L,Hq,D] and
-    lse [B,Hq,L].
+    with i < 0 sees nothing (out 0, lse -inf).  ``kv_start`` [B] (optional)
+    drops the cache rows before it: the left padding of a padded prefill.
+    Returns out [B,L,Hq,D] and lse [B,Hq,L].
     """
     Lr = resolve_layer(cfg, layer_idx)
     q = np.asarray(q, dtype=np.float64)
@@ -363,11 +392,15 @@ def decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len):
     lse = np.full((B, Hq, Lq), -np.inf)
     for b in range(B):
         c = int(ctx_len[b])
+        first = 0 if kv_start is None else max(0, int(kv_start[b]))
         for t in range(Lq):
             i = c - Lq + t
             if i < 0:
                 continue
             lo = max(0, i - W + 1) if W > 0 else 0
+            lo = max(lo, first)
+            if lo > i:
+                continue
             for h in range(Lr["num_kv_heads"]):
                 keys = np.asarray(k_cache[b, lo:i + 1, h, :], dtype=np.float64)
                 vals = keys if Lr["k_eq_v"] else np.asarray(v_cache[b, lo:i + 1, h, :], dtype=np.float64)
@@ -404,7 +437,7 @@ def dequantize_int8(codes, scales):
     return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
 
 
-def decode_int8(cfg, layer_idx, q, k_codes, k_scales, v_codes, v_scales, ctx_len):
+def decode_int8(cfg, layer_idx, q, k_codes, k_scales, v_codes, v_scales, ctx_len, kv_start=None):
     """Decode (any number of new tokens) against an int8 cache.
 
     Cache codes [B,Smax,Hkv,D] int8 with scales [B,Hkv,Smax] fp32 (one per
@@ -415,7 +448,7 @@ def decode_int8(cfg, layer_idx, q, k_codes, k_scales, v_codes, v_scales, ctx_len
     L = resolve_layer(cfg, layer_idx)
     kd = dequantize_int8(k_codes, np.swapaxes(np.asarray(k_scales), 1, 2))
     vd = kd if L["k_eq_v"] else dequantize_int8(v_codes, np.swapaxes(np.asarray(v_scales), 1, 2))
-    return decode_multi(cfg, layer_idx, q, kd, vd, ctx_len)
+    return decode_multi(cfg, layer_idx, q, kd, vd, ctx_len, kv_start)
 
 
 def prefill_flops(cfg, layer_idx, batch: int, seq: int) -> int:

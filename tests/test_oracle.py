@@ -375,3 +375,75 @@ def test_rope_scaling_mutants_are_caught(monkeypatch):
         with pytest.raises(AssertionError):
             test_rope_scaling_matches_brute_force(layer)
         monkeypatch.setattr(R, "resolve_layer", orig)
+
+
+# --------------------------------------------------------------------------- padded (ragged) prefill
+_RAGGED_RANGES = [(3, 11), (0, 7), (2, 10), (5, 5), (0, 11)]     # left pad, right pad, both, empty, none
+
+
+@pytest.mark.parametrize("W,cap,tied", [(0, 0.0, False), (4, 3.0, False), (0, 0.0, True)])
+def test_prefill_ragged_matches_brute_force_mask(W, cap, tied):
+    cfg = R.GemmaAttnConfig(num_heads=4, num_kv_heads=2 if not tied else 1, head_dim=8, global_head_dim=8,
+                            sliding_window=W, sliding_window_pattern=0 if W else 1, attn_logit_softcapping=cap,
+                            k_eq_v=tied, rope_theta=1e4)
+    L = R.resolve_layer(cfg, 0)
+    B, S = len(_RAGGED_RANGES), 11
+    q, k, v = _inputs(23, B, S, 4, L["num_kv_heads"], 8, qscale=2.0)
+    start = np.array([a for a, _ in _RAGGED_RANGES])
+    end = np.array([b for _, b in _RAGGED_RANGES])
+    pos0 = -start                                     # kept tokens start at position 0
+    qt, kt = R.prologue(cfg, 0, q, k, pos0=pos0)
+    o, l = R.prefill_ragged(cfg, 0, qt, kt, v, start, end)
+    keep = [[1 if a <= s < b else 0 for s in range(S)] for a, b in _RAGGED_RANGES]
+    ob, lb = brute_layer(_cfg_dict(cfg), 0, q.tolist(), k.tolist(), v.tolist(), pos0=pos0.tolist(), keep=keep)
+    assert np.abs(o - np.array(ob)).max() < TOL
+    fin = np.isfinite(np.array(lb))
+    assert np.array_equal(np.isfinite(l), fin)
+    assert np.abs(l[fin] - np.array(lb)[fin]).max() < TOL
+    for bi, (a, b_) in enumerate(_RAGGED_RANGES):     # padded rows are exactly zero
+        assert np.all(o[bi, :a] == 0) and np.all(o[bi, b_:] == 0)
+
+
+def test_prefill_ragged_unpadded_is_prefill_and_left_pad_is_shift_invariant():
+    cfg = _small_cfg(sliding_window=5, attn_logit_softcapping=4.0)
+    q, k, v = _inputs(29, 2, 14, 4, 2, 16)
+    o, l = R.prefill(cfg, 0, q, k, v)
+    og, lg = R.prefill_ragged(cfg, 0, q, k, v, [0, 0], [14, 14])
+    assert np.array_equal(o, og) and np.array_equal(l, lg)
+    # left padding by 4: the kept rows equal the unpadded prefill of the same tokens
+    pad = np.zeros((2, 4) + q.shape[2:])
+    padk = np.zeros((2, 4) + k.shape[2:])
+    o2, _ = R.prefill_ragged(cfg, 0, np.concatenate([pad, q], 1), np.concatenate([padk, k], 1),
+                             np.concatenate([padk, v], 1), [4, 4], [18, 18])
+    assert np.array_equal(o2[:, 4:], o) and np.all(o2[:, :4] == 0)
+
+
+def test_decode_after_left_padded_prefill_uses_kv_start():
+    cfg = _small_cfg(sliding_window=0)
+    B, S = 2, 12
+    q, k, v = _inputs(31, B, S, 4, 2, 16, qscale=2.0)
+    start = np.array([3, 0])
+    o, l = R.prefill_ragged(cfg, 0, q, k, v, start, [S, S])
+    od, ld = R.decode_multi(cfg, 0, q[:, S - 2:], k, v, [S, S], kv_start=start)
+    assert np.abs(od - o[:, S - 2:]).max() < 1e-13 and np.abs(ld - l[:, :, S - 2:]).max() < 1e-13
+    # without kv_start the padded rows would be attended
+    ow, _ = R.decode_multi(cfg, 0, q[:, S - 2:], k, v, [S, S])
+    assert np.abs(ow[0] - o[0, S - 2:]).max() > 1e-6
+
+
+def test_ragged_mutant_is_caught(monkeypatch):
+    orig = R.prefill_ragged
+
+    def keys_not_masked(cfg, layer_idx, q, k, v, seq_start, seq_end):
+        out, lse = R.prefill(cfg, layer_idx, q, k, v)
+        for b in range(len(seq_start)):
+            out[b, :seq_start[b]] = 0
+            out[b, seq_end[b]:] = 0
+            lse[b, :, :seq_start[b]] = -np.inf
+            lse[b, :, seq_end[b]:] = -np.inf
+        return out, lse
+
+    monkeypatch.setattr(R, "prefill_ragged", keys_not_masked)
+    with pytest.raises(AssertionError):
+        test_prefill_ragged_matches_brute_force_mask(0, 0.0, False)
+    monkeypatch.setattr(R, "prefill_ragged", orig)
