@@ -140,7 +140,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gemma_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.gemma_attn_decode.argtypes = [cfgp, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
     lib.gemma_attn_decode.restype = ctypes.c_int
-    lib.gemma_attn_decode_multi.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+    lib.gemma_attn_decode_multi.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             ctypes.c_size_t, _VP]
     lib.gemma_attn_decode_multi.restype = ctypes.c_int
     lib.gemma_attn_decode_multi_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
@@ -148,7 +148,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gemma_qk_prologue_cache.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
     lib.gemma_qk_prologue_cache.restype = ctypes.c_int
     lib.gemma_attn_decode_int8.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                           ctypes.c_size_t, _VP]
+                                           _VP, ctypes.c_size_t, _VP]
+    lib.gemma_attn_prefill_ragged.argtypes = [cfgp, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.gemma_attn_prefill_ragged.restype = ctypes.c_int
     lib.gemma_attn_decode_int8.restype = ctypes.c_int
     lib.gemma_qk_prologue_cache_int8.argtypes = [cfgp, i32, i32, i32, i32] + [_VP] * 12
     lib.gemma_qk_prologue_cache_int8.restype = ctypes.c_int
@@ -240,8 +242,10 @@ def qk_prologue(cfg, layer_idx, q, k=None, q_out=None, k_out=None, q_norm_w=None
     return q_out, k_out
 
 
-def attn_prefill(cfg, layer_idx, q, k, v=None, out=None, lse=None, want_lse=False, stream=None):
-    """gemma_attn_prefill; returns out, or (out, lse) when an lse buffer is asked for."""
+def attn_prefill(cfg, layer_idx, q, k, v=None, out=None, lse=None, want_lse=False, stream=None, seq_start=None,
+                 seq_end=None):
+    """gemma_attn_prefill (gemma_attn_prefill_ragged when seq_start or seq_end [B] int32 is given: sequence b
+    keeps rows [start, end)); returns out, or (out, lse) when an lse buffer is asked for."""
     import torch
 
     cfg = Config.from_any(cfg)
@@ -259,11 +263,17 @@ def attn_prefill(cfg, layer_idx, q, k, v=None, out=None, lse=None, want_lse=Fals
     if lse is not None:
         _expect(lse, (B, cfg.num_heads, S), "lse")
     bf = torch.bfloat16
-    rc = load().gemma_attn_prefill(
-        ctypes.byref(cfg.to_c()), int(layer_idx), B, S, _ptr(q, bf, "q"), _ptr(k, bf, "k"),
-        None if L["k_eq_v"] else _ptr(v, bf, "v"), _ptr(out, bf, "out"),
-        _ptr(lse, torch.float32, "lse"), _stream(stream))
-    _check(rc, "gemma_attn_prefill")
+    args = (ctypes.byref(cfg.to_c()), int(layer_idx), B, S, _ptr(q, bf, "q"), _ptr(k, bf, "k"),
+            None if L["k_eq_v"] else _ptr(v, bf, "v"), _ptr(out, bf, "out"), _ptr(lse, torch.float32, "lse"))
+    if seq_start is None and seq_end is None:
+        _check(load().gemma_attn_prefill(*args, _stream(stream)), "gemma_attn_prefill")
+    else:
+        for t, n in ((seq_start, "seq_start"), (seq_end, "seq_end")):
+            if t is not None:
+                _expect(t, (B,), n)
+        rc = load().gemma_attn_prefill_ragged(*args, _ptr(seq_start, torch.int32, "seq_start"),
+                                              _ptr(seq_end, torch.int32, "seq_end"), _stream(stream))
+        _check(rc, "gemma_attn_prefill_ragged")
     return (out, lse) if lse is not None else out
 
 
@@ -310,7 +320,7 @@ def decode_multi_workspace_size(cfg, layer_idx, batch, q_len, max_ctx) -> int:
 
 
 def attn_decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len, out=None, lse=None, want_lse=False,
-                      workspace=None, stream=None):
+                      workspace=None, stream=None, kv_start=None):
     """gemma_attn_decode_multi; q [B,L,Hq,D]; returns out [B,L,Hq,D], or (out, lse [B,Hq,L])."""
     import torch
 
@@ -334,8 +344,8 @@ def attn_decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len, out=None, ls
     rc = load().gemma_attn_decode_multi(
         ctypes.byref(cfg.to_c()), int(layer_idx), B, Lq, Smax, _ptr(q, bf, "q"), _ptr(k_cache, bf, "k_cache"),
         None if L["k_eq_v"] else _ptr(v_cache, bf, "v_cache"), _ptr(ctx_len, torch.int32, "ctx_len"),
-        _ptr(out, bf, "out"), _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"),
-        workspace.numel() * workspace.element_size(), _stream(stream))
+        _ptr(kv_start, torch.int32, "kv_start"), _ptr(out, bf, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "gemma_attn_decode_multi")
     return (out, lse) if lse is not None else out
 
@@ -373,7 +383,7 @@ def qk_prologue_cache(cfg, layer_idx, q, k, v, k_cache, v_cache, ctx_len, q_out=
 # ----------------------------------------------------------------------------- int8 KV cache
 # codes [B,Smax,Hkv,D] torch.int8; scales [B,Hkv,Smax] torch.float32 (one per token and head).
 def attn_decode_int8(cfg, layer_idx, q, k_codes, k_scales, v_codes, v_scales, ctx_len, out=None, lse=None,
-                     want_lse=False, workspace=None, stream=None):
+                     want_lse=False, workspace=None, stream=None, kv_start=None):
     """gemma_attn_decode_int8; q [B,L,Hq,D]; returns out [B,L,Hq,D], or (out, lse [B,Hq,L])."""
     import torch
 
@@ -401,7 +411,8 @@ def attn_decode_int8(cfg, layer_idx, q, k_codes, k_scales, v_codes, v_scales, ct
         ctypes.byref(cfg.to_c()), int(layer_idx), B, Lq, Smax, _ptr(q, torch.bfloat16, "q"),
         _ptr(k_codes, torch.int8, "k_codes"), _ptr(k_scales, torch.float32, "k_scales"),
         _ptr(v_codes, torch.int8, "v_codes") if kv else None, _ptr(v_scales, torch.float32, "v_scales") if kv else None,
-        _ptr(ctx_len, torch.int32, "ctx_len"), _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(ctx_len, torch.int32, "ctx_len"), _ptr(kv_start, torch.int32, "kv_start"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
         _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "gemma_attn_decode_int8")
     return (out, lse) if lse is not None else out

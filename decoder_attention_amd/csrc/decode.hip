@@ -46,6 +46,7 @@ struct DecodeParams {
   const uint16_t* kc;
   const uint16_t* vc;
   const int32_t* ctx_len;
+  const int32_t* kv_start;    // first cache row each sequence may read (null: 0)
   uint16_t* out;
   float* lse;
   float* ws_o;
@@ -59,13 +60,15 @@ struct DecodeParams {
 };
 
 // Keys sequence b can read: [lo, ctx).  With q_len query tokens at positions
-// ctx - q_len .. ctx - 1, a local layer reads back to the window of the first.
+// ctx - q_len .. ctx - 1, a local layer reads back to the window of the first;
+// a left-padded cache starts at kv_start[b].
 __device__ __forceinline__ void seq_range(const DecodeParams& p, int32_t b, int32_t& lo, int32_t& ctx) {
   int32_t c = p.ctx_len[b];
   c = c < 0 ? 0 : (c > p.max_ctx ? p.max_ctx : c);
   const int32_t span = p.window > 0 ? min(c, p.window + p.q_len - 1) : c;
   ctx = c;
   lo = c - span;
+  if (p.kv_start) lo = min(max(lo, p.kv_start[b]), c);
 }
 
 // XOR pattern of the 16-byte chunks of LDS row r (a 16-lane ds_read_b128
@@ -754,6 +757,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.kc = static_cast<const uint16_t*>(a.k_cache);
   prm.vc = static_cast<const uint16_t*>(a.v_cache);
   prm.ctx_len = a.ctx_len;
+  prm.kv_start = a.kv_start;
   prm.out = static_cast<uint16_t*>(a.out);
   prm.lse = a.lse;
   prm.ws_o = a.ws_o;

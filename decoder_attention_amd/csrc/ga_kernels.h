@@ -42,6 +42,8 @@ struct PrefillArgs {
   const void* v;
   void* out;
   float* lse;
+  const int32_t* seq_start;   // padded batch (device [B], may be null): kept rows [start, end)
+  const int32_t* seq_end;
   double scale, softcap;
 };
 // Returns hipErrorInvalidValue for an unsupported (dim, group) pair.
@@ -54,6 +56,7 @@ struct DecodeArgs {
   const void* k_cache;
   const void* v_cache;
   const int32_t* ctx_len;
+  const int32_t* kv_start;    // device [B] or null: first cache row each sequence may read
   void* out;
   float* lse;
   float* ws_o;

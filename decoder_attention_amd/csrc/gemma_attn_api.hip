@@ -19,11 +19,45 @@ int hip_rc(hipError_t e) {
   return GA_ERR_HIP;
 }
 
+int prefill_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq, const void* q,
+                   const void* k, const void* v, void* out, float* lse, const int32_t* seq_start,
+                   const int32_t* seq_end, void* stream) {
+  gemma_attn_layer L;
+  const int rc = ga::resolve_layer(cfg, layer_idx, &L);
+  if (rc != GA_OK) return rc;
+  if (batch < 0 || seq < 0) return GA_ERR_INVALID_ARG;
+  if (!ga::attn_dim_supported(L.head_dim) || !ga::attn_group_supported(L.group)) return GA_ERR_UNSUPPORTED;
+  if (batch > 65535 || L.num_kv_heads > 65535) return GA_ERR_UNSUPPORTED;
+  if (batch == 0 || seq == 0) return GA_OK;
+  if (!dev_ok(q) || !dev_ok(k) || !dev_ok(out)) return GA_ERR_INVALID_ARG;
+  if (!L.k_eq_v && !dev_ok(v)) return GA_ERR_INVALID_ARG;
+  if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
+  ga::PrefillArgs a{};
+  a.batch = batch;
+  a.seq = seq;
+  a.hq = cfg->num_heads;
+  a.hkv = L.num_kv_heads;
+  a.dim = L.head_dim;
+  a.group = L.group;
+  a.window = L.window;
+  a.k_eq_v = L.k_eq_v;
+  a.q = q;
+  a.k = k;
+  a.v = L.k_eq_v ? k : v;
+  a.out = out;
+  a.lse = lse;
+  a.seq_start = seq_start;
+  a.seq_end = seq_end;
+  a.scale = L.scale;
+  a.softcap = L.softcap;
+  return hip_rc(ga::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 // Shared by the bf16 and int8 decode entry points (k_scales set: int8 caches).
 int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len, int32_t max_ctx,
                   const void* q, const void* k_cache, const float* k_scales, const void* v_cache,
-                  const float* v_scales, const int32_t* ctx_len, void* out, float* lse, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  const float* v_scales, const int32_t* ctx_len, const int32_t* kv_start, void* out, float* lse,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   gemma_attn_layer L;
   const int rc = ga::resolve_layer(cfg, layer_idx, &L);
   if (rc != GA_OK) return rc;
@@ -59,6 +93,7 @@ int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch
   a.k_scales = k_scales;
   a.v_scales = L.k_eq_v ? k_scales : v_scales;
   a.ctx_len = ctx_len;
+  a.kv_start = kv_start;
   a.out = out;
   a.lse = lse;
   a.ws_o = reinterpret_cast<float*>(wsb + ws.o_off);
@@ -129,33 +164,13 @@ int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
 
 int gemma_attn_prefill(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
                        const void* q, const void* k, const void* v, void* out, float* lse, void* stream) {
-  gemma_attn_layer L;
-  const int rc = ga::resolve_layer(cfg, layer_idx, &L);
-  if (rc != GA_OK) return rc;
-  if (batch < 0 || seq < 0) return GA_ERR_INVALID_ARG;
-  if (!ga::attn_dim_supported(L.head_dim) || !ga::attn_group_supported(L.group)) return GA_ERR_UNSUPPORTED;
-  if (batch > 65535 || L.num_kv_heads > 65535) return GA_ERR_UNSUPPORTED;
-  if (batch == 0 || seq == 0) return GA_OK;
-  if (!dev_ok(q) || !dev_ok(k) || !dev_ok(out)) return GA_ERR_INVALID_ARG;
-  if (!L.k_eq_v && !dev_ok(v)) return GA_ERR_INVALID_ARG;
-  if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
-  ga::PrefillArgs a{};
-  a.batch = batch;
-  a.seq = seq;
-  a.hq = cfg->num_heads;
-  a.hkv = L.num_kv_heads;
-  a.dim = L.head_dim;
-  a.group = L.group;
-  a.window = L.window;
-  a.k_eq_v = L.k_eq_v;
-  a.q = q;
-  a.k = k;
-  a.v = L.k_eq_v ? k : v;
-  a.out = out;
-  a.lse = lse;
-  a.scale = L.scale;
-  a.softcap = L.softcap;
-  return hip_rc(ga::launch_prefill(a, static_cast<hipStream_t>(stream)));
+  return prefill_common(cfg, layer_idx, batch, seq, q, k, v, out, lse, nullptr, nullptr, stream);
+}
+
+int gemma_attn_prefill_ragged(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
+                              const void* q, const void* k, const void* v, void* out, float* lse,
+                              const int32_t* seq_start, const int32_t* seq_end, void* stream) {
+  return prefill_common(cfg, layer_idx, batch, seq, q, k, v, out, lse, seq_start, seq_end, stream);
 }
 
 size_t gemma_attn_decode_multi_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
@@ -174,26 +189,27 @@ size_t gemma_attn_decode_workspace_size(const gemma_attn_config* cfg, int32_t la
 
 int gemma_attn_decode_multi(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
                             int32_t max_ctx, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* ctx_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                            void* stream) {
-  return decode_common(cfg, layer_idx, batch, q_len, max_ctx, q, k_cache, nullptr, v_cache, nullptr, ctx_len, out, lse,
-                       workspace, workspace_bytes, stream);
+                            const int32_t* ctx_len, const int32_t* kv_start, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_common(cfg, layer_idx, batch, q_len, max_ctx, q, k_cache, nullptr, v_cache, nullptr, ctx_len, kv_start,
+                       out, lse, workspace, workspace_bytes, stream);
 }
 
 int gemma_attn_decode_int8(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
                            int32_t max_ctx, const void* q, const void* k_codes, const float* k_scales,
-                           const void* v_codes, const float* v_scales, const int32_t* ctx_len, void* out, float* lse,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           const void* v_codes, const float* v_scales, const int32_t* ctx_len,
+                           const int32_t* kv_start, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   if (k_scales == nullptr) return GA_ERR_INVALID_ARG;
-  return decode_common(cfg, layer_idx, batch, q_len, max_ctx, q, k_codes, k_scales, v_codes, v_scales, ctx_len, out,
-                       lse, workspace, workspace_bytes, stream);
+  return decode_common(cfg, layer_idx, batch, q_len, max_ctx, q, k_codes, k_scales, v_codes, v_scales, ctx_len,
+                       kv_start, out, lse, workspace, workspace_bytes, stream);
 }
 
 int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t max_ctx,
                       const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_len,
                       void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return gemma_attn_decode_multi(cfg, layer_idx, batch, 1, max_ctx, q, k_cache, v_cache, ctx_len, out, lse, workspace,
-                                 workspace_bytes, stream);
+  return gemma_attn_decode_multi(cfg, layer_idx, batch, 1, max_ctx, q, k_cache, v_cache, ctx_len, nullptr, out, lse,
+                                 workspace, workspace_bytes, stream);
 }
 
 int gemma_qk_prologue_cache(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,

@@ -74,6 +74,8 @@ struct PrefillParams {
   const uint16_t* v;
   uint16_t* out;
   float* lse;
+  const int32_t* seq_start;   // padded batch: sequence b keeps rows [start, end) (null: 0, seq)
+  const int32_t* seq_end;
   int32_t seq, hq, hkv, window, n_qblocks, n_qblocks_pad, batch;
   float scale_log2;   // scale * log2(e)            (no cap)
   float cap_in2;      // 2 * scale * log2(e) / cap  (cap: exp2 argument of tanh)
@@ -222,14 +224,21 @@ void prefill_kernel(PrefillParams p) {
   const bool col_valid = pos < S;
   const int32_t pos_m = col_valid ? pos : S - 1;
   const int32_t W = p.window;
-  const int32_t key_lo = W > 0 ? pos_m - W + 1 : 0;   // first key this column may see
+  // Kept rows of this sequence (a padded batch keeps [r_lo, r_hi)); padded
+  // rows are neither queries nor keys.
+  int32_t r_lo = 0, r_hi = S;
+  if (p.seq_start) r_lo = min(max(p.seq_start[b], 0), S);
+  if (p.seq_end) r_hi = min(max(p.seq_end[b], r_lo), S);
+  const bool kept = pos >= r_lo && pos < r_hi;
+  const int32_t key_lo = max(W > 0 ? pos_m - W + 1 : 0, r_lo);   // first key this column may see
 
-  const int32_t w_lo = p0 + (cw * kCols) / G;                         // wave's first position
-  const int32_t w_hi = min(p0 + (cw * kCols + kCols - 1) / G, S - 1); // wave's last valid position
-  const int32_t kv_end = min(S, p0 + kP);
-  int32_t kv_begin = W > 0 ? max(0, p0 - W + 1) : 0;
+  // The wave's kept positions [w_lo, w_hi] (empty when w_lo > w_hi).
+  const int32_t w_lo = max(p0 + (cw * kCols) / G, r_lo);
+  const int32_t w_hi = min(min(p0 + (cw * kCols + kCols - 1) / G, S - 1), r_hi - 1);
+  const int32_t kv_end = min(min(S, p0 + kP), r_hi);
+  int32_t kv_begin = max(W > 0 ? max(0, p0 - W + 1) : 0, r_lo);
   kv_begin &= ~(kKeys - 1);
-  const int32_t n_tiles = (kv_end - kv_begin + kKeys - 1) / kKeys;
+  const int32_t n_tiles = max(0, (kv_end - kv_begin + kKeys - 1) / kKeys);
 
   // Issue the direct-to-LDS copies of the tile starting at key kt into ring
   // slot B.  Addresses are a wave-uniform tile base plus a 32-bit per-lane
@@ -251,7 +260,9 @@ void prefill_kernel(PrefillParams p) {
     const int64_t tile_off = (static_cast<int64_t>(kt) * p.hkv + kvh) * D * 2;
     const char* kt_base = kbase + tile_off;
     const char* vt_base = vbase + tile_off;
-    const bool tail = kt + kKeys > S;        // rows past the end repeat the last row (masked)
+    // Rows outside the kept range repeat its first or last row (masked), so
+    // no padded row is ever read.
+    const bool tail = kt < r_lo || kt + kKeys > r_hi;
     uint16_t* kdst = kslot(B);
     uint16_t* vdst = vslot(B);
 #pragma unroll
@@ -264,7 +275,8 @@ void prefill_kernel(PrefillParams p) {
         const int32_t pc = base + ln;
         const int32_t row = pc / kRowChunks;
         const int32_t lc = (pc % kRowChunks) ^ swz<D>(row);
-        off = static_cast<uint32_t>(min(row, S - 1 - kt)) * row_pitch + static_cast<uint32_t>(lc) * 16u;
+        off = static_cast<uint32_t>(min(max(row, r_lo - kt), r_hi - 1 - kt)) * row_pitch +
+              static_cast<uint32_t>(lc) * 16u;
       }
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt_base + off),
                                        (__attribute__((address_space(3))) void*)(kdst + base * 8), 16, 0, 0);
@@ -310,8 +322,8 @@ void prefill_kernel(PrefillParams p) {
 
     // Does this wave see any key of the tile?  (wave-uniform; equal for both
     // waves of a D-split pair)
-    const bool need = kt <= w_hi && (W == 0 || kt + kKeys - 1 >= w_lo - W + 1);
-    const bool full = kt + kKeys - 1 <= w_lo && (W == 0 || kt >= w_hi - W + 1);
+    const bool need = w_lo <= w_hi && kt <= w_hi && kt + kKeys - 1 >= max(r_lo, W > 0 ? w_lo - W + 1 : 0);
+    const bool full = kt >= r_lo && kt + kKeys - 1 <= w_lo && (W == 0 || kt >= w_hi - W + 1);
 
     // S^T = K . Q^T (partial over this wave's D slice when split)
     f32x16 sacc = f32x16{};
@@ -447,7 +459,10 @@ void prefill_kernel(PrefillParams p) {
 
   const float l_tot = xhalf_sum(l_run);
   if (col_valid) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // Padded rows are written as exact zeros (their accumulators are not
+    // meaningful: a padded query row may hold anything).
+    const bool live = kept && l_tot > 0.f;
+    const float inv = live ? 1.f / l_tot : 0.f;
     uint16_t* orow = p.out + ((static_cast<int64_t>(b) * S + pos) * p.hq + head) * D + dlo;
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
@@ -457,12 +472,12 @@ void prefill_kernel(PrefillParams p) {
         u32x2 w2;
         w2[0] = pack_bf16x2(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
         w2[1] = pack_bf16x2(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+        if (!kept) w2 = u32x2{0u, 0u};
         *reinterpret_cast<u32x2*>(orow + d) = w2;
       }
     }
     if (p.lse && h == 0 && dlo == 0) {
-      p.lse[(static_cast<int64_t>(b) * p.hq + head) * S + pos] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      p.lse[(static_cast<int64_t>(b) * p.hq + head) * S + pos] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -515,6 +530,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   prm.v = static_cast<const uint16_t*>(a.v);
   prm.out = static_cast<uint16_t*>(a.out);
   prm.lse = a.lse;
+  prm.seq_start = a.seq_start;
+  prm.seq_end = a.seq_end;
   prm.seq = a.seq;
   prm.hq = a.hq;
   prm.hkv = a.hkv;

@@ -143,6 +143,21 @@ int gemma_attn_prefill(const gemma_attn_config* cfg, int32_t layer_idx, int32_t 
                        void* stream);
 
 /*
+ * gemma_attn_prefill over a padded batch.  generate() on the Gemma, Gemma 2
+ * and Gemma 4 pages takes attention_mask (batch, seq) with 1 = keep and
+ * 0 = padding; read here as contiguous padding at the ends, so sequence b
+ * keeps rows [seq_start[b], seq_end[b]) (left padding: start > 0; ragged
+ * lengths: end < seq).  Padded rows are neither queries nor keys and are never
+ * read (they may hold anything); their output rows are 0 and their lse -inf.
+ * The causal and window masks stay positional (i - j).  seq_start / seq_end:
+ * device int32 [B], or NULL for 0 / seq; clamped on the device to
+ * 0 <= start <= end <= seq.  Other arguments as for gemma_attn_prefill.
+ */
+int gemma_attn_prefill_ragged(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
+                              const void* q, const void* k, const void* v, void* out, float* lse,
+                              const int32_t* seq_start, const int32_t* seq_end, void* stream);
+
+/*
  * Bytes of device workspace gemma_attn_decode needs for (layer, batch, max_ctx);
  * 0 when the arguments are invalid.
  */
@@ -176,16 +191,19 @@ int gemma_attn_decode(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
  * against the cache).  q [B,q_len,Hq,D] bf16 holds the processed queries; the
  * caches hold processed keys and values of positions 0..ctx-1, new tokens
  * included (see gemma_qk_prologue_cache); v_cache is ignored on keys-as-values
- * layers.  out [B,q_len,Hq,D] bf16; lse fp32 [B,Hq,q_len] or NULL.  Rows with
- * no visible key (i < 0) give out = 0, lse = -inf.  ctx_len entries are
- * clamped to [0, max_ctx] on the device; 1 <= q_len <= max_ctx.  workspace: at
- * least gemma_attn_decode_multi_workspace_size() bytes.  q_len = 1 is exactly
- * gemma_attn_decode.
+ * layers.  kv_start: device int32 [B] or NULL: cache rows before kv_start[b]
+ * are not read (the left padding of a padded prefill, see
+ * gemma_attn_prefill_ragged).  out [B,q_len,Hq,D] bf16; lse fp32
+ * [B,Hq,q_len] or NULL.  Rows with no visible key (i < 0, or i < kv_start[b])
+ * give out = 0, lse = -inf.  ctx_len entries are clamped to [0, max_ctx] on
+ * the device; 1 <= q_len <= max_ctx.  workspace: at least
+ * gemma_attn_decode_multi_workspace_size() bytes.  q_len = 1 with kv_start =
+ * NULL is exactly gemma_attn_decode.
  */
 int gemma_attn_decode_multi(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
                             int32_t max_ctx, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* ctx_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                            void* stream);
+                            const int32_t* ctx_len, const int32_t* kv_start, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of gemma_attn_decode_multi; 0 when the arguments are invalid. */
 size_t gemma_attn_decode_multi_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
@@ -223,14 +241,15 @@ int gemma_qk_prologue_cache(const gemma_attn_config* cfg, int32_t layer_idx, int
  * processed keys, v_codes/v_scales the values (both ignored, may be NULL, on
  * keys-as-values layers, where the key codes serve as values).  Scores use
  * s_j * (q . c_j); the value scale multiplies each probability before its
- * bf16 rounding.  q, out, lse, ctx_len, workspace and errors as for
- * gemma_attn_decode_multi, whose workspace size applies unchanged.  Pointers
- * 16-byte aligned.
+ * bf16 rounding.  q, out, lse, ctx_len, kv_start, workspace and errors as
+ * for gemma_attn_decode_multi, whose workspace size applies unchanged.
+ * Pointers 16-byte aligned.
  */
 int gemma_attn_decode_int8(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
                            int32_t max_ctx, const void* q, const void* k_codes, const float* k_scales,
-                           const void* v_codes, const float* v_scales, const int32_t* ctx_len, void* out, float* lse,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           const void* v_codes, const float* v_scales, const int32_t* ctx_len,
+                           const int32_t* kv_start, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * gemma_qk_prologue_cache appending to an int8 cache: the processed keys

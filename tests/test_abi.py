@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(ga):
                           "gemma_attn_decode_workspace_size", "gemma_attn_decode", "gemma_attn_strerror",
                           "gemma_attn_decode_multi", "gemma_attn_decode_multi_workspace_size",
                           "gemma_qk_prologue_cache", "gemma_attn_decode_int8", "gemma_qk_prologue_cache_int8",
-                          "gemma_kv_quantize_int8"}
+                          "gemma_kv_quantize_int8", "gemma_attn_prefill_ragged"}
     lib = ctypes.CDLL(ga.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -163,17 +163,17 @@ def test_multi_token_entry_points_reject_bad_arguments(ga):
         lib.gemma_attn_decode_workspace_size(ref(keqv), 0, 4, 1000)
     for q_len, max_ctx in [(0, 1000), (1001, 1000), (-1, 1000), (1, 0)]:
         assert lib.gemma_attn_decode_multi_workspace_size(ref(keqv), 0, 4, q_len, max_ctx) == 0
-        assert lib.gemma_attn_decode_multi(ref(keqv), 0, 4, q_len, max_ctx, fake, fake, None, fake, fake, None,
+        assert lib.gemma_attn_decode_multi(ref(keqv), 0, 4, q_len, max_ctx, fake, fake, None, fake, None, fake, None,
                                            fake, 1 << 30, None) == ga.GA_ERR_INVALID_ARG
-    assert lib.gemma_attn_decode_multi(ref(keqv), 0, 4, 5, 1000, fake, fake, None, fake, fake, None, fake,
+    assert lib.gemma_attn_decode_multi(ref(keqv), 0, 4, 5, 1000, fake, fake, None, fake, None, fake, None, fake,
                                        need - 1, None) == ga.GA_ERR_WORKSPACE
-    assert lib.gemma_attn_decode_multi(ref(good), 0, 4, 5, 1000, fake, fake, None, fake, fake, None, fake,
+    assert lib.gemma_attn_decode_multi(ref(good), 0, 4, 5, 1000, fake, fake, None, fake, None, fake, None, fake,
                                        1 << 30, None) == ga.GA_ERR_INVALID_ARG   # v_cache missing
-    assert lib.gemma_attn_decode_multi(ref(keqv), 0, 4, 5, 1000, fake, fake, None, None, fake, None, fake,
+    assert lib.gemma_attn_decode_multi(ref(keqv), 0, 4, 5, 1000, fake, fake, None, None, None, fake, None, fake,
                                        1 << 30, None) == ga.GA_ERR_INVALID_ARG   # ctx_len missing
     # too many 16-column blocks for the grid
     g16 = ga.Config(num_heads=16 * 4096, num_kv_heads=4096, head_dim=64).to_c()
-    assert lib.gemma_attn_decode_multi(ref(g16), 0, 1, 300, 1000, fake, fake, fake, fake, fake, None, fake,
+    assert lib.gemma_attn_decode_multi(ref(g16), 0, 1, 300, 1000, fake, fake, fake, fake, None, fake, None, fake,
                                        1 << 40, None) == ga.GA_ERR_UNSUPPORTED
     # prologue with cache append
     P = lib.gemma_qk_prologue_cache
@@ -203,13 +203,13 @@ def test_int8_entry_points_reject_bad_arguments(ga):
     keqv = ga.Config(num_heads=8, num_kv_heads=1, head_dim=512, k_eq_v=True).to_c()
     need = lib.gemma_attn_decode_multi_workspace_size(ref(good), 0, 2, 3, 100)
     D8 = lib.gemma_attn_decode_int8
-    assert D8(ref(good), 0, 2, 3, 100, fake, fake, None, fake, fake, fake, fake, None, fake, need,
+    assert D8(ref(good), 0, 2, 3, 100, fake, fake, None, fake, fake, fake, None, fake, None, fake, need,
               None) == ga.GA_ERR_INVALID_ARG                                  # key scales missing
-    assert D8(ref(good), 0, 2, 3, 100, fake, fake, fake, fake, None, fake, fake, None, fake, need,
+    assert D8(ref(good), 0, 2, 3, 100, fake, fake, fake, fake, None, fake, None, fake, None, fake, need,
               None) == ga.GA_ERR_INVALID_ARG                                  # value scales missing
-    assert D8(ref(good), 0, 2, 3, 100, fake, fake, fake, fake, fake, fake, fake, None, fake, need - 1,
+    assert D8(ref(good), 0, 2, 3, 100, fake, fake, fake, fake, fake, fake, None, fake, None, fake, need - 1,
               None) == ga.GA_ERR_WORKSPACE
-    assert D8(ref(keqv), 0, 0, 3, 100, None, None, fake, None, None, None, None, None, None, 0, None) == ga.GA_OK
+    assert D8(ref(keqv), 0, 0, 3, 100, None, None, fake, None, None, None, None, None, None, None, 0, None) == ga.GA_OK
     P8 = lib.gemma_qk_prologue_cache_int8
     assert P8(ref(good), 0, 2, 4, 16, fake, fake, fake, fake, fake, None, fake, fake, None, None, fake,
               None) == ga.GA_ERR_INVALID_ARG                                  # key scales missing
