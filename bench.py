@@ -56,6 +56,23 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel_source: str, summary: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+
+    try:
+        text = open(os.path.join(ROOT, "profiles", summary)).read()
+        block = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+        src = hashlib.sha256(open(os.path.join(ROOT, kernel_source), "rb").read()).hexdigest()
+    except (OSError, AttributeError, ValueError):
+        return None
+    if block.get("source_sha256") != src:
+        return None
+    return block
+
+
 def _flops(kw, layer, B, S) -> int:
     """4*D per allowed (query head, key) pair; window W sees exactly W keys."""
     import decoder_attention_amd as ga
@@ -137,6 +154,12 @@ def run_layer_step(ga, kw, layer, t, timer=None, tag=""):
         timer.stop(f"prefill{tag}")
 
 
+def _pair_traffic():
+    """Mean HBM bytes per launch of the pair's prefill kernel (counter summary), or None."""
+    t = measured_traffic("decoder_attention_amd/csrc/prefill.hip", "prefill_gemma2_pair_hbm_traffic.md")
+    return None if t is None else t["hbm_bytes_mean"]
+
+
 def bench_pair(ga, steps, warmup):
     import torch
 
@@ -170,7 +193,7 @@ def bench_pair(ga, steps, warmup):
         prologue_ms={"local_w4096": pro[0], "global": pro[1]},
         prefill_tflops={"local_w4096": flops[0] / (pre[0] * 1e-3) / 1e12, "global": flops[1] / (pre[1] * 1e-3) / 1e12},
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                      frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                      frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=_pair_traffic(),
                       kernel="prefill_kernel<256,2,false,true>",
                       flops_per_launch={"local_w4096": flops[0], "global": flops[1]},
                       avg_launch_ms={"local_w4096": round(pre[0], 4), "global": round(pre[1], 4)}),
