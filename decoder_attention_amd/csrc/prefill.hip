@@ -125,6 +125,10 @@ __device__ __forceinline__ float xhalf_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float xhalf_min(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float xhalf_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -325,17 +329,20 @@ void prefill_kernel(PrefillParams p) {
     const bool need = w_lo <= w_hi && kt <= w_hi && kt + kKeys - 1 >= max(r_lo, W > 0 ? w_lo - W + 1 : 0);
     const bool full = kt >= r_lo && kt + kKeys - 1 <= w_lo && (W == 0 || kt >= w_hi - W + 1);
 
-    // S^T = K . Q^T (partial over this wave's D slice when split)
+    // S^T = K . Q^T (partial over this wave's D slice when split).  Lane
+    // (jj, hh) reads chunk dlo/8 + 2*ds + hh of key row jj.  The chunk's bits
+    // (ds, hh, swizzle) sit in address bits 4-8, clear of the row and slice
+    // bits, so the address of step ds is one XOR: kaddr ^ (32 * ds).
     f32x16 sacc = f32x16{};
     if (need) {
       const int32_t ln = lane_id_here();
       const int32_t jj = ln & 31;
       const int32_t hh = ln >> 5;
-      const int32_t sw = swz<D>(jj);
+      const uint32_t kaddr = static_cast<uint32_t>(jj * D * 2 + dlo * 2 + ((hh ^ swz<D>(jj)) << 4));
+      const char* kbc = reinterpret_cast<const char*>(kb);
 #pragma unroll
       for (int ds = 0; ds < kDS; ++ds) {
-        const int32_t lc = (dlo >> 3) + ds * 2 + hh;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[jj * D + ((lc ^ sw) << 3)]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>(ds * 32)));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc, 0, 0, 0);
       }
     }
@@ -360,32 +367,43 @@ void prefill_kernel(PrefillParams p) {
     }
 
     if (need) {
-      // Logits: lane holds keys kt + (r/4)*8 + h*4 + r%4.  Without a cap the
-      // scale is folded into the exponent, exp2(s*scale*log2e - m), and the
-      // max is taken on the raw scores (the scale is positive).
+      // Lane holds keys kt + (r/4)*8 + h*4 + r%4.  Each score is kept in the
+      // form that needs the fewest instructions per element:
+      //  * with a cap, x = 1/(exp(2*s*scale/cap) + 1): the capped logit
+      //    cap*tanh(s*scale/cap) is cap*(1 - 2x) (log2 units below), which
+      //    falls as x rises, so the row max comes from the smallest x and a
+      //    masked key gets x = +inf;
+      //  * without a cap, x = s and the scale folds into the exponent,
+      //    exp2(s*scale*log2e - m); a masked key gets -inf.
       float x[16];
-      float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float t;
-        if (CAP) {
-          // cap * tanh(s*scale/cap) = cap - 2*cap / (exp(2*s*scale/cap) + 1), in log2 units
-          const float e = __builtin_amdgcn_exp2f(sacc[r] * p.cap_in2);
-          t = fmaf(-2.f * p.cap_log2, __builtin_amdgcn_rcpf(e + 1.f), p.cap_log2);
-        } else {
-          t = sacc[r];
-        }
-        if (!full) {
-          // allowed iff key_lo <= key <= pos (branch-free; key_lo from the window)
-          const int32_t key = kt + (r >> 2) * 8 + h * 4 + (r & 3);
-          const bool ok = (key <= pos_m) & (key >= key_lo);
-          t = ok ? t : -INFINITY;
-        }
-        x[r] = t;
-        mx = fmaxf(mx, t);
+        if (CAP) x[r] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sacc[r] * p.cap_in2) + 1.f);
+        else x[r] = sacc[r];
       }
-      mx = xhalf_max(mx);
-      if (!CAP) mx *= p.scale_log2;
+      if (__builtin_expect(!full, 0)) {
+        // boundary tile: allowed iff key_lo <= key <= pos
+        const int32_t kb0 = kt + h * 4;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t key = kb0 + (r >> 2) * 8 + (r & 3);
+          const bool ok = (key <= pos_m) & (key >= key_lo);
+          x[r] = ok ? x[r] : (CAP ? INFINITY : -INFINITY);
+        }
+      }
+      float mx;
+      if (CAP) {
+        float mr = x[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mr = fminf(mr, x[r]);
+        mr = xhalf_min(mr);
+        mx = fmaf(-2.f * p.cap_log2, mr, p.cap_log2);     // -inf when every key is masked
+      } else {
+        mx = x[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+        mx = xhalf_max(mx) * p.scale_log2;
+      }
       // The running max only moves when the tile exceeds it by more than
       // kTau (log2 units): probabilities then stay <= 2^kTau and the output
       // rescale, a pass over every accumulator, is rare.
@@ -404,12 +422,14 @@ void prefill_kernel(PrefillParams p) {
       // values (v_dot2_f32_bf16 against (1, 1)).
       uint32_t pk[8];
       const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+      const float cap_m = p.cap_log2 - m_use;
+      const float neg2cap = -2.f * p.cap_log2;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         float e0, e1;
         if (CAP) {
-          e0 = __builtin_amdgcn_exp2f(x[2 * r] - m_use);
-          e1 = __builtin_amdgcn_exp2f(x[2 * r + 1] - m_use);
+          e0 = __builtin_amdgcn_exp2f(fmaf(neg2cap, x[2 * r], cap_m));
+          e1 = __builtin_amdgcn_exp2f(fmaf(neg2cap, x[2 * r + 1], cap_m));
         } else {
           e0 = __builtin_amdgcn_exp2f(fmaf(x[2 * r], p.scale_log2, -m_use));
           e1 = __builtin_amdgcn_exp2f(fmaf(x[2 * r + 1], p.scale_log2, -m_use));
@@ -418,24 +438,28 @@ void prefill_kernel(PrefillParams p) {
         l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r]), ones, l_run, false);
       }
 
-      // O^T += V^T . P^T, two 16-key halves per tile.
+      // O^T += V^T . P^T, two 16-key halves per tile.  Lane (lgrp, li16)
+      // reads chunk dlo/8 + 4*db + 2*(lgrp&1) + (li16&3)/2 of rows r0 and
+      // r0 + 8; as for K, the chunk bits are clear of the row, slice and
+      // half-chunk bits, so block db's address is one XOR: base ^ (64 * db).
       const int32_t ln = lane_id_here();
       const int32_t lgrp = ln >> 4;
       const int32_t li16 = ln & 15;
+      const int32_t cl = 2 * (lgrp & 1) + ((li16 & 3) >> 1);
+      const char* vbc = reinterpret_cast<const char*>(vb);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const u32x4 pb = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
         const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
         const int32_t r0 = 16 * t + 4 * (ln >> 5) + (li16 >> 2);
         const int32_t r1 = r0 + 8;
-        const int32_t sw0 = swz<D>(r0);
-        const int32_t sw1 = swz<D>(r1);
-        const int32_t half8 = (li16 & 1) * 4;
+        const uint32_t rest = static_cast<uint32_t>(dlo * 2 + (li16 & 1) * 8);
+        const uint32_t va0 = static_cast<uint32_t>(r0 * D * 2 + ((cl ^ swz<D>(r0)) << 4)) + rest;
+        const uint32_t va1 = static_cast<uint32_t>(r1 * D * 2 + ((cl ^ swz<D>(r1)) << 4)) + rest;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
-          const int32_t lc = ((dlo + db * 32 + (lgrp & 1) * 16) >> 3) + ((li16 & 3) >> 1);
-          const i16x4 a0 = lds_read_tr16(&vb[r0 * D + ((lc ^ sw0) << 3) + half8]);
-          const i16x4 a1 = lds_read_tr16(&vb[r1 * D + ((lc ^ sw1) << 3) + half8]);
+          const i16x4 a0 = lds_read_tr16(vbc + (va0 ^ static_cast<uint32_t>(db * 64)));
+          const i16x4 a1 = lds_read_tr16(vbc + (va1 ^ static_cast<uint32_t>(db * 64)));
           const bf16x8 aop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, o[db], 0, 0, 0);
         }
