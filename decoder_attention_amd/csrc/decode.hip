@@ -169,12 +169,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(G <= 16, "at most 16 query heads per KV head");
   static_assert(kTK * kRowChunks % (64 * kTeam) == 0, "tile must split into whole 1 KB ops");
 
-  // Two slots per team, one LDS array per slot (so reads of one slot are not
-  // ordered behind the copies landing in the other).
+  // Ring of slots per team, one LDS array per slot (so reads of one slot are
+  // not ordered behind the copies landing in the others).  Two slots: one
+  // tile in flight while one is computed.  A third slot at head width 512
+  // (48 KB) leaves room for three workgroups per CU instead of four, which
+  // measured slower (3.9 against 4.6 TB/s on the global layer).
+  constexpr int kSlots = 2;
   __shared__ __attribute__((aligned(16))) uint16_t ks0[kTeams * kSlotElems];
   __shared__ __attribute__((aligned(16))) uint16_t ks1[kTeams * kSlotElems];
+  __shared__ __attribute__((aligned(16))) uint16_t ks2[kSlots > 2 ? kTeams * kSlotElems : 8];
   __shared__ __attribute__((aligned(16))) uint16_t vs0[KEQV ? 8 : kTeams * kSlotElems];
   __shared__ __attribute__((aligned(16))) uint16_t vs1[KEQV ? 8 : kTeams * kSlotElems];
+  __shared__ __attribute__((aligned(16))) uint16_t vs2[(KEQV || kSlots < 3) ? 8 : kTeams * kSlotElems];
   __shared__ float m_w[2][16];
   __shared__ float l_w[2][16];
   static_assert(kTeams == 1 || kSlotElems * kTeams * 2 >= 16 * D * 4, "merge buffer reuses slot 0");
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Copy this wave's share of tile ti (keys s_lo + 16*ti ...) into a slot.
   // Rows past s_hi repeat row s_hi - 1, so no row outside the sequence's
   // range is read.
-  auto copy_tile = [&](int32_t ti, uint16_t* kdst, uint16_t* vdst) {
+  auto copy_tile = [&](int32_t ti, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
     const int32_t k0 = s_lo + ti * kTK;
     const int32_t last = s_hi - 1 - k0;
     const char* kb = kseq + static_cast<int64_t>(k0) * row_pitch;
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // One tile from slot (kb, vb).
-  auto compute = [&](int32_t ti, const uint16_t* kb, const uint16_t* vb) {
+  auto compute = [&](int32_t ti, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
     const int32_t k0 = s_lo + ti * kTK;
     // S^T[16 keys x 16 heads] = K . Q^T; lane: key row li16, d chunk ds*4 + lgrp.
     f32x4 sacc = f32x4{};
@@ -315,32 +321,53 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  // The team's tiles: ti = team, team + kTeams, ...; alternate slots.
-  uint16_t* k0s = ks0 + team * kSlotElems;
-  uint16_t* k1s = ks1 + team * kSlotElems;
-  uint16_t* v0s = KEQV ? k0s : vs0 + team * kSlotElems;
-  uint16_t* v1s = KEQV ? k1s : vs1 + team * kSlotElems;
+  // Slot I of this team (compile-time I, so each access names one LDS array).
+  auto kslot = [&](auto I) -> uint16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return ks0 + team * kSlotElems;
+    else if constexpr (i == 1) return ks1 + team * kSlotElems;
+    else return ks2 + team * kSlotElems;
+  };
+  auto vslot = [&](auto I) -> uint16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (KEQV) return kslot(I);
+    else if constexpr (i == 0) return vs0 + team * kSlotElems;
+    else if constexpr (i == 1) return vs1 + team * kSlotElems;
+    else return vs2 + team * kSlotElems;
+  };
   // A team of two shares its slots: a barrier publishes both halves of a
   // tile and fences the slot being refilled (every wave runs the same trips).
   auto team_sync = [&]() {
     if constexpr (kTeam > 1) __syncthreads();
   };
+  // The team's tiles are ti = team, team + kTeams, ...; tile k of the team
+  // sits in slot k % kSlots.  Waiting for the oldest tile leaves a newer
+  // tile's copies (kOpsPerTile per wave) outstanding.
   int32_t ti = team;
-  if (ti < n_t) copy_tile(ti, k0s, v0s);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (ti < n_t) copy_tile(ti, kslot(S0{}), vslot(S0{}));
+  if constexpr (kSlots > 2) {
+    if (ti + kTeams < n_t) copy_tile(ti + kTeams, kslot(S1{}), vslot(S1{}));
+  }
+  auto step = [&](auto I) __attribute__((always_inline)) -> bool {
+    constexpr int kCur = decltype(I)::value;
+    using Next = std::integral_constant<int, (kCur + kSlots - 1) % kSlots>;
+    if (kSlots > 2 && ti + kTeams < n_t) wait_vmcnt<(kSlots > 2 ? kOpsPerTile : 0)>();
+    else wait_vmcnt<0>();
+    team_sync();
+    const int32_t ta = ti + (kSlots - 1) * kTeams;
+    if (ta < n_t) copy_tile(ta, kslot(Next{}), vslot(Next{}));
+    compute(ti, kslot(I), vslot(I));
+    ti += kTeams;
+    return ti < n_t;
+  };
   while (ti < n_t) {
-    const int32_t tn = ti + kTeams;
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));   // this wave's copies of tile ti
-    team_sync();
-    if (tn < n_t) copy_tile(tn, k1s, v1s);                 // in flight during compute
-    compute(ti, k0s, v0s);
-    ti = tn;
-    if (ti >= n_t) break;
-    const int32_t tn2 = ti + kTeams;
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-    team_sync();
-    if (tn2 < n_t) copy_tile(tn2, k0s, v0s);
-    compute(ti, k1s, v1s);
-    ti = tn2;
+    if (!step(S0{})) break;
+    if (!step(S1{})) break;
+    if constexpr (kSlots > 2) {
+      if (!step(std::integral_constant<int, 2>{})) break;
+    }
   }
   (void)kOpsPerTile;
 
