@@ -71,13 +71,18 @@ __device__ __forceinline__ void seq_range(const DecodeParams& p, int32_t b, int3
   if (p.kv_start) lo = min(max(lo, p.kv_start[b]), c);
 }
 
-// XOR pattern of the 16-byte chunks of LDS row r (a 16-lane ds_read_b128
-// phase reads 16 consecutive rows at one chunk; a transpose read reads 4
-// rows x 4 chunks per half-wave).  See the prefill kernel for the derivation.
+// XOR pattern f(r) of the 16-byte chunks of LDS row r in [0, 16).  The
+// score product's ds_read_b128 phase (16 lanes) reads rows 0-15 at one chunk:
+// f must take 16 distinct values (D >= 128: one row spans whole bank cycles),
+// or 8 distinct values within each row parity (D = 64: two rows per 256-byte
+// cycle).  The value transpose read's 32-lane phase reads rows 0-7 (or 8-15)
+// at an aligned chunk pair {c, c+1}: the pairs {c ^ f(r), (c+1) ^ f(r)} must
+// be disjoint, i.e. f(r) >> 1 distinct over those rows (within a parity at
+// D = 64).  Bits 1-3 from r & 7 and bit 0 from r >> 3 satisfy both.
 template <int D>
 __device__ __forceinline__ int32_t dswz(int32_t r) {
-  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  if constexpr (D >= 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 
 // The lane index, hidden from loop-invariant code motion, so lane-derived
@@ -132,15 +137,18 @@ __device__ __forceinline__ void write_partial(const DecodeParams& p, int64_t par
     const float m_all = fmaxf(m_w[0][col], m_w[1][col]);
     const float m_ref = m_all == -INFINITY ? 0.f : m_all;
     const float f = __builtin_amdgcn_exp2f(m_run - m_ref);
+    // Column col's 16-byte chunk q = db*4 + grp sits at chunk q ^ col of its
+    // row, so the 16 columns of a lane group hit 16 different bank groups.
     if (wave == 0) {
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) *reinterpret_cast<f32x4*>(merge_buf + col * D + db * 16 + grp * 4) = o[db] * f;
+      for (int db = 0; db < kDB; ++db)
+        *reinterpret_cast<f32x4*>(merge_buf + col * D + (((db * 4 + grp) ^ col) << 2)) = o[db] * f;
     }
     __syncthreads();
     if (wave == 1 && col_ok) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        const f32x4 prev = *reinterpret_cast<const f32x4*>(merge_buf + col * D + db * 16 + grp * 4);
+        const f32x4 prev = *reinterpret_cast<const f32x4*>(merge_buf + col * D + (((db * 4 + grp) ^ col) << 2));
         float* dst = p.ws_o + part * D + db * 16 + grp * 4;
         *reinterpret_cast<f32x4*>(dst) = prev + o[db] * f;
       }
