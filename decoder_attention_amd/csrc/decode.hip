@@ -32,6 +32,9 @@ namespace ga {
 namespace {
 
 constexpr int kTK = 16;     // keys per wave tile
+// Cache policy of the cache copies: non-temporal (each cache row is read once
+// per call; a plain streaming read measured ~8% slower than a non-temporal one).
+constexpr int kStreamAux = 2;
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: low 4 bits and bits 14-15), leaving the
 // export and LDS counters unconstrained.
@@ -257,10 +260,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int32_t lc = (pc % kRowChunks) ^ dswz<D>(row);
       const uint32_t off = static_cast<uint32_t>(min(row, last)) * row_pitch + static_cast<uint32_t>(lc) * 16u;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + off),
-                                       (__attribute__((address_space(3))) void*)(kdst + op * 512), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(kdst + op * 512), 16, 0, kStreamAux);
       if (!KEQV) {
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + off),
-                                         (__attribute__((address_space(3))) void*)(vdst + op * 512), 16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(vdst + op * 512), 16, 0, kStreamAux);
       }
     }
   };
@@ -524,20 +527,20 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int32_t lc = (pc % kRowChunks) ^ qswz<D>(row);
       const uint32_t off = static_cast<uint32_t>(min(row, last)) * row_pitch + static_cast<uint32_t>(lc) * 16u;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + off),
-                                       (__attribute__((address_space(3))) void*)(kdst + op * 1024), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(kdst + op * 1024), 16, 0, kStreamAux);
       if (!KEQV) {
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + off),
-                                         (__attribute__((address_space(3))) void*)(vdst + op * 1024), 16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(vdst + op * 1024), 16, 0, kStreamAux);
       }
     }
     const int32_t key = k0 + min(ln & 31, last);
     if (member == 0) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kscale + key),
-                                       (__attribute__((address_space(3))) void*)(kscd), 4, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(kscd), 4, 0, kStreamAux);
     }
     if (!KEQV && member == kTeam - 1) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vscale + key),
-                                       (__attribute__((address_space(3))) void*)(vscd), 4, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(vscd), 4, 0, kStreamAux);
     }
   };
 
