@@ -4,10 +4,14 @@
 // for chunked prefill or draft verification), at positions ctx - q_len ..
 // ctx - 1, each causal and windowed on its own position.  The keys a sequence
 // reads -- back to the window of its first query on local layers, [0, ctx) on
-// global layers -- are cut into chunks; one workgroup handles one (chunk,
-// KV head, block of 16 (token, head) columns, sequence) and produces an
-// unnormalised partial (m, l, o) per column; a second kernel merges the
-// partials of each (sequence, token, head) in a fixed order (log-sum-exp).
+// global layers -- are laid end to end over all sequences (a plan kernel
+// writes the prefix sums); the P workgroups of each (KV head, block of 16
+// (token, head) columns) take equal consecutive ranges of that line, so every
+// workgroup does the same work whatever the mix of context lengths.  A range
+// that crosses sequence boundaries yields one unnormalised partial (m, l, o)
+// per sequence it touches, stored at slot w + b (unique: along the monotone
+// path of (workgroup, sequence) pairs w + b increases at every step); a
+// combine kernel merges each (sequence, token, head)'s partials in order.
 //
 // Inside a workgroup (2 waves) tiles of 16 cache rows stream HBM -> LDS with
 // the direct-to-LDS loads into two slots per team (one tile in flight while
@@ -57,7 +61,10 @@ struct DecodeParams {
   float* ws_l;
   const float* ks;            // int8 caches: scales [B, Hkv, max_ctx] of keys and values
   const float* vs;
-  int32_t max_ctx, hq, hkv, window, chunk, n_split;
+  int64_t* prefix;            // workspace: [B + 1] prefix sums of the readable spans
+  int32_t* lo;                // workspace: [B] first readable key of each sequence
+  int32_t batch, max_ctx, hq, hkv, window, n_wg;   // n_wg: workgroups per (KV head, column block)
+  int32_t per_seq;            // workgroup w takes sequence w whole (n_wg = batch)
   int32_t q_len, n_cb;        // query tokens per sequence; 16-column blocks per KV head
   float scale_log2, cap_in2, cap_log2;
 };
@@ -72,6 +79,93 @@ __device__ __forceinline__ void seq_range(const DecodeParams& p, int32_t b, int3
   ctx = c;
   lo = c - span;
   if (p.kv_start) lo = min(max(lo, p.kv_start[b]), c);
+}
+
+// One workgroup: the readable span of every sequence and their exclusive
+// prefix sums (int64), written to the workspace.
+constexpr int kPlanThreads = 256;
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeParams p) {
+  __shared__ int64_t wsum[kPlanThreads / 64];
+  const int32_t t = threadIdx.x;
+  const int32_t per = (p.batch + kPlanThreads - 1) / kPlanThreads;
+  const int32_t b0 = min(p.batch, t * per), b1 = min(p.batch, b0 + per);
+  int64_t mine = 0;
+  for (int32_t b = b0; b < b1; ++b) {
+    int32_t lo, ctx;
+    seq_range(p, b, lo, ctx);
+    p.lo[b] = lo;
+    mine += ctx - lo;
+  }
+  // inclusive scan of the per-thread sums: within the wave, then across waves
+  int64_t inc = mine;
+  const int32_t lane = t & 63, wave = t >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t up = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += up;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int64_t base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  // exclusive prefix of this thread's first sequence; the spans are
+  // recomputed rather than held
+  int64_t run = base + inc - mine;
+  for (int32_t b = b0; b < b1; ++b) {
+    int32_t lo, ctx;
+    seq_range(p, b, lo, ctx);
+    p.prefix[b] = run;
+    run += ctx - lo;
+  }
+  if (t == kPlanThreads - 1) p.prefix[p.batch] = base + inc;
+}
+
+// Workgroup w of P covers keys [w*T/P, (w+1)*T/P) of the line (integer division).
+__device__ __forceinline__ int64_t wg_start(int64_t w, int64_t total, int64_t n_wg) { return (w * total) / n_wg; }
+
+// The workgroup whose range holds key x of the line (0 <= x < total).
+__device__ __forceinline__ int64_t wg_of(int64_t x, int64_t total, int64_t n_wg) {
+  int64_t w = (x * n_wg) / total;
+  while (w + 1 < n_wg && wg_start(w + 1, total, n_wg) <= x) ++w;
+  while (w > 0 && wg_start(w, total, n_wg) > x) --w;
+  return w;
+}
+
+// Calls f(b, s_lo, s_hi, ctx) for every sequence b that this workgroup's range
+// touches, with [s_lo, s_hi) the sequence's keys in the range; uniform across
+// the workgroup.  The caller separates consecutive calls with a barrier.
+template <class F>
+__device__ __forceinline__ void for_each_segment(const DecodeParams& p, F&& f) {
+  if (p.per_seq) {
+    const int32_t b = blockIdx.y;
+    int32_t lo, ctx;
+    seq_range(p, b, lo, ctx);
+    if (ctx > lo) f(b, lo, ctx, ctx);
+    return;
+  }
+  const int64_t total = p.prefix[p.batch];
+  const int64_t w = blockIdx.y;
+  const int64_t x0 = wg_start(w, total, p.n_wg);
+  const int64_t x1 = wg_start(w + 1, total, p.n_wg);
+  if (x0 >= x1) return;
+  // first sequence: the last b with prefix[b] <= x0
+  int32_t lo_b = 0, hi_b = p.batch - 1;
+  while (lo_b < hi_b) {
+    const int32_t mid = (lo_b + hi_b + 1) >> 1;
+    if (p.prefix[mid] <= x0) lo_b = mid;
+    else hi_b = mid - 1;
+  }
+  for (int32_t b = lo_b; b < p.batch; ++b) {
+    const int64_t pb = p.prefix[b], pe = p.prefix[b + 1];
+    const int64_t a = x0 > pb ? x0 : pb;
+    const int64_t e = x1 < pe ? x1 : pe;
+    if (a < e) {
+      const int32_t base = p.lo[b];
+      f(b, base + static_cast<int32_t>(a - pb), base + static_cast<int32_t>(e - pb),
+        base + static_cast<int32_t>(pe - pb));
+    }
+    if (pe >= x1) break;
+  }
 }
 
 // XOR pattern f(r) of the 16-byte chunks of LDS row r in [0, 16).  The
@@ -196,17 +290,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float l_w[2][16];
   static_assert(kTeams == 1 || kSlotElems * kTeams * 2 >= 16 * D * 4, "merge buffer reuses slot 0");
 
-  const int32_t split = blockIdx.x;
-  const int32_t kvh = static_cast<int32_t>(blockIdx.y) / p.n_cb;
-  const int32_t cb = static_cast<int32_t>(blockIdx.y) % p.n_cb;   // 16-column block
-  const int32_t b = blockIdx.z;
-  int32_t lo, ctx;
-  seq_range(p, b, lo, ctx);
-  const int32_t s_lo = lo + split * p.chunk;
-  if (s_lo >= ctx) return;   // this split is empty for the sequence (uniform)
-  const int32_t s_hi = min(ctx, s_lo + p.chunk);
-  const int32_t n_t = (s_hi - s_lo + kTK - 1) / kTK;
-
+  const int32_t kvh = static_cast<int32_t>(blockIdx.x) / p.n_cb;
+  const int32_t cb = static_cast<int32_t>(blockIdx.x) % p.n_cb;   // 16-column block
   const int32_t tid = threadIdx.x;
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t team = wave / kTeam;
@@ -219,10 +304,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool col_ok = gcol < G * p.q_len;
   const int32_t tok = col_ok ? gcol / G : 0;
   const int32_t head = kvh * G + (col_ok ? gcol % G : 0);
+
+
+  // Each sequence segment of this workgroup's key range: [s_lo, s_hi) of
+  // sequence b, whose context is ctx.
+  for_each_segment(p, [&](int32_t b, int32_t s_lo, int32_t s_hi, int32_t ctx) __attribute__((always_inline)) {
+  const int32_t n_t = (s_hi - s_lo + kTK - 1) / kTK;
   // Keys this column may see: [key_lo, key_hi] (its own position and the window).
   const int32_t key_hi = col_ok ? ctx - p.q_len + tok : -1;
   const int32_t key_lo = p.window > 0 ? key_hi - p.window + 1 : 0;
-
   // Q^T operand: lane holds d = ds*32 + grp*8 + [0, 8) of its (token, head).
   bf16x8 qf[kDS];
   {
@@ -385,9 +475,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   // Partial of (sequence b, token tok, head): row ((b*q_len + tok)*Hq + head).
-  const int64_t part = ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * p.n_split + split;
+  // Partial of (sequence b, token tok, head) from workgroup w: slot w + b.
+  const int64_t part = ((static_cast<int64_t>(blockIdx.y) + b) * p.q_len + tok) * p.hq + head;
   write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, member, dlo, grp, col,
                                 reinterpret_cast<float*>(ks0), m_w, l_w);
+  __syncthreads();   // LDS slots (and the merge buffer) are reused by the next segment
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -455,17 +548,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Partial scores of a two-wave team: [member][half][lane].
   __shared__ f32x4 sx[kTeam > 1 ? 2 * 2 * 64 : 1];
 
-  const int32_t split = blockIdx.x;
-  const int32_t kvh = static_cast<int32_t>(blockIdx.y) / p.n_cb;
-  const int32_t cb = static_cast<int32_t>(blockIdx.y) % p.n_cb;
-  const int32_t b = blockIdx.z;
-  int32_t lo, ctx;
-  seq_range(p, b, lo, ctx);
-  const int32_t s_lo = lo + split * p.chunk;
-  if (s_lo >= ctx) return;
-  const int32_t s_hi = min(ctx, s_lo + p.chunk);
-  const int32_t n_t = (s_hi - s_lo + kTK8 - 1) / kTK8;
-
+  const int32_t kvh = static_cast<int32_t>(blockIdx.x) / p.n_cb;
+  const int32_t cb = static_cast<int32_t>(blockIdx.x) % p.n_cb;   // 16-column block
   const int32_t tid = threadIdx.x;
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t team = wave / kTeam;
@@ -478,9 +562,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool col_ok = gcol < G * p.q_len;
   const int32_t tok = col_ok ? gcol / G : 0;
   const int32_t head = kvh * G + (col_ok ? gcol % G : 0);
+
+
+  // Each sequence segment of this workgroup's key range: [s_lo, s_hi) of
+  // sequence b, whose context is ctx.
+  for_each_segment(p, [&](int32_t b, int32_t s_lo, int32_t s_hi, int32_t ctx) __attribute__((always_inline)) {
+  const int32_t n_t = (s_hi - s_lo + kTK8 - 1) / kTK8;
+  // Keys this column may see: [key_lo, key_hi] (its own position and the window).
   const int32_t key_hi = col_ok ? ctx - p.q_len + tok : -1;
   const int32_t key_lo = p.window > 0 ? key_hi - p.window + 1 : 0;
-
   // Q^T operand: step ds, MFMA m: lane holds d = (ds*4 + grp)*16 + m*8 + [0, 8),
   // the d range of the key chunk (ds*4 + grp) that the K operand lane reads;
   // this wave's steps are ds = member*kDSW + [0, kDSW).
@@ -705,12 +795,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  const int64_t part = ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * p.n_split + split;
+  // Partial of (sequence b, token tok, head) from workgroup w: slot w + b.
+  const int64_t part = ((static_cast<int64_t>(blockIdx.y) + b) * p.q_len + tok) * p.hq + head;
   write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, member, dlo, grp, col,
                                 reinterpret_cast<float*>(ks0), m_w, l_w);
+  __syncthreads();   // LDS slots (and the merge buffer) are reused by the next segment
+  });
 }
 
-// Merge the split partials of one (sequence, query head) in split order.
+// Merge the partials of one (sequence, token, query head), in workgroup order.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
   constexpr int kPer = D / 64 > 0 ? D / 64 : 1;   // elements per lane
@@ -718,24 +811,43 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
   const int32_t head = static_cast<int32_t>(blockIdx.x) % p.hq;
   const int32_t b = blockIdx.y;
   const int32_t lane = threadIdx.x;
-  int32_t lo, ctx;
-  seq_range(p, b, lo, ctx);
-  const int32_t n_valid = ctx > lo ? (ctx - lo + p.chunk - 1) / p.chunk : 0;
+  // workgroups whose ranges hold this sequence's keys (none when it has none)
+  int64_t total = 0, wa = 1, wb = 0;
+  if (p.per_seq) {
+    int32_t lo, ctx;
+    seq_range(p, b, lo, ctx);
+    if (ctx > lo) wa = wb = b;
+  } else {
+    total = p.prefix[p.batch];
+    const int64_t pb = p.prefix[b], pe = p.prefix[b + 1];
+    if (pe > pb) {
+      wa = wg_of(pb, total, p.n_wg);
+      wb = wg_of(pe - 1, total, p.n_wg);
+    }
+  }
   const int64_t row = (static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head;
-  const int64_t part = row * p.n_split;
+  auto part_of = [&](int64_t w) { return ((w + b) * p.q_len + tok) * p.hq + head; };
+  // a workgroup with an empty range (fewer keys than workgroups) wrote nothing
+  auto empty = [&](int64_t w) {
+    return !p.per_seq && wg_start(w, total, p.n_wg) == wg_start(w + 1, total, p.n_wg);
+  };
   float m_all = -INFINITY;
-  for (int s = 0; s < n_valid; ++s) m_all = fmaxf(m_all, p.ws_m[part + s]);
+  for (int64_t w = wa; w <= wb; ++w) {
+    if (!empty(w)) m_all = fmaxf(m_all, p.ws_m[part_of(w)]);
+  }
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
   float l_all = 0.f;
   const int32_t d0 = lane * kPer;
-  for (int s = 0; s < n_valid; ++s) {
-    const float ms = p.ws_m[part + s];
+  for (int64_t w = wa; w <= wb; ++w) {
+    if (empty(w)) continue;
+    const int64_t part = part_of(w);
+    const float ms = p.ws_m[part];
     const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m_all);
-    l_all = fmaf(p.ws_l[part + s], f, l_all);
+    l_all = fmaf(p.ws_l[part], f, l_all);
     if (d0 < D) {
-      const float* src = p.ws_o + (part + s) * D + d0;
+      const float* src = p.ws_o + part * D + d0;
 #pragma unroll
       for (int e = 0; e < kPer; ++e) acc[e] = fmaf(src[e], f, acc[e]);
     }
@@ -754,7 +866,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
 
 template <int D, int G, bool KEQV, bool CAP>
 hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(a.n_split), static_cast<uint32_t>(a.hkv * prm.n_cb), static_cast<uint32_t>(a.batch));
+  if (!a.per_seq) {   // the balanced ranges need the prefix sums of the spans
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, prm);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
+  // rows (KV head, column block) fastest: the KV heads of one cache row are
+  // adjacent in memory and their workgroups run side by side
+  const dim3 grid(static_cast<uint32_t>(a.hkv * prm.n_cb), static_cast<uint32_t>(a.n_wg), 1u);
   if (prm.ks) {
     hipLaunchKernelGGL((decode_split_i8_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D>::kWaves * 64), 0, stream, prm);
   } else {
@@ -796,6 +915,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.vc = static_cast<const uint16_t*>(a.v_cache);
   prm.ctx_len = a.ctx_len;
   prm.kv_start = a.kv_start;
+  prm.prefix = a.ws_prefix;
+  prm.lo = a.ws_lo;
+  prm.batch = a.batch;
   prm.out = static_cast<uint16_t*>(a.out);
   prm.lse = a.lse;
   prm.ws_o = a.ws_o;
@@ -807,8 +929,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.hq = a.hq;
   prm.hkv = a.hkv;
   prm.window = a.window;
-  prm.chunk = a.chunk;
-  prm.n_split = a.n_split;
+  prm.n_wg = a.n_wg;
+  prm.per_seq = a.per_seq;
   prm.q_len = a.q_len;
   prm.n_cb = (a.group * a.q_len + 15) / 16;
   const double log2e = 1.4426950408889634;

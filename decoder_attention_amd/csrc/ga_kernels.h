@@ -51,7 +51,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   int32_t batch, max_ctx, hq, hkv, dim, group, window, k_eq_v;
-  int32_t chunk, n_split, q_len;
+  int32_t n_wg, q_len;        // workgroups per (KV head, column block); query tokens per sequence
+  int32_t per_seq;            // 1: workgroup w takes sequence w whole (n_wg = batch)
   const void* q;
   const void* k_cache;
   const void* v_cache;
@@ -62,6 +63,8 @@ struct DecodeArgs {
   float* ws_o;
   float* ws_m;
   float* ws_l;
+  int64_t* ws_prefix;         // [B + 1] prefix sums of the readable spans (written by the plan kernel)
+  int32_t* ws_lo;             // [B] first readable key of each sequence
   // int8 caches (k_scales set): k_cache / v_cache hold int8 codes and these
   // the fp32 scales, [B, Hkv, max_ctx].
   const float* k_scales;

@@ -84,8 +84,8 @@ int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch
   a.group = L.group;
   a.window = L.window;
   a.k_eq_v = L.k_eq_v;
-  a.chunk = plan.chunk;
-  a.n_split = plan.n_split;
+  a.n_wg = plan.n_wg;
+  a.per_seq = plan.per_seq ? 1 : 0;
   a.q_len = q_len;
   a.q = q;
   a.k_cache = k_cache;
@@ -99,6 +99,8 @@ int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch
   a.ws_o = reinterpret_cast<float*>(wsb + ws.o_off);
   a.ws_m = reinterpret_cast<float*>(wsb + ws.m_off);
   a.ws_l = reinterpret_cast<float*>(wsb + ws.l_off);
+  a.ws_prefix = reinterpret_cast<int64_t*>(wsb + ws.prefix_off);
+  a.ws_lo = reinterpret_cast<int32_t*>(wsb + ws.lo_off);
   a.scale = L.scale;
   a.softcap = L.softcap;
   return hip_rc(ga::launch_decode(a, static_cast<hipStream_t>(stream)));

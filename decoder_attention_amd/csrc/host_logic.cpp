@@ -82,34 +82,42 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
   const long long wspan = static_cast<long long>(L.window) + ql - 1;
   p.span_max = L.window > 0 ? static_cast<int32_t>(wspan < max_ctx ? wspan : max_ctx) : max_ctx;
   if (p.span_max < 1) p.span_max = 1;
-  // Aim for >= 2048 workgroups over (split, KV head x 16-column block,
-  // sequence) so that 256 CUs stay busy on ragged lengths; chunks are powers
-  // of two in [256, 4096] keys.
   const long long col_blocks = (static_cast<long long>(L.group) * ql + 15) / 16;
-  const long long units = static_cast<long long>(batch > 0 ? batch : 1) * L.num_kv_heads * col_blocks;
-  long long want = (2048 + units - 1) / units;
-  if (want < 1) want = 1;
-  long long chunk = 256;
-  while (chunk < 4096 && chunk * want < p.span_max) chunk *= 2;
-  // With enough units to fill the chip, longer chunks amortise each
-  // workgroup's start-up (first copy latency, merge, partial write-back).
-  if (units >= 256 && chunk < 1024) chunk = 1024;
-  p.chunk = static_cast<int32_t>(chunk);
-  // Splits are relative to the first key a sequence reads, so span/chunk
-  // chunks (rounded up) cover every sequence.
-  long long ns = (p.span_max + chunk - 1) / chunk;
-  if (ns < 1) ns = 1;
-  p.n_split = static_cast<int32_t>(ns);
+  const long long rows = static_cast<long long>(L.num_kv_heads) * col_blocks;
+  // One round of workgroups on 256 CUs: the split kernel's workgroups per CU
+  // follow from its LDS ring (two waves per workgroup, two waves per SIMD).
+  const long long team = L.head_dim > 256 ? 2 : 1;
+  const long long lds = (2 / team) * 2 * 16LL * L.head_dim * 2 * (L.k_eq_v ? 1 : 2);
+  long long per_cu = (160LL * 1024) / lds;
+  if (per_cu > 4) per_cu = 4;
+  if (per_cu < 1) per_cu = 1;
+  long long n = (256 * per_cu) / rows;
+  const long long line_max = static_cast<long long>(batch > 0 ? batch : 1) * p.span_max;
+  const long long at_least = (line_max + 16383) / 16384;   // at most 16K keys per workgroup
+  const long long at_most = (line_max + 255) / 256;        // at least 256 keys per workgroup
+  if (n < at_least) n = at_least;
+  if (n > at_most) n = at_most;
+  if (n > 65535) n = 65535;   // grid y
+  if (n < 1) n = 1;
+  p.n_wg = static_cast<int32_t>(n);
+  // Short spans (local windows) with enough sequences to fill the round: one
+  // workgroup per sequence.  Every span is then at most 8K keys, so no
+  // workgroup runs long, and none straddles two sequences.
+  p.per_seq = static_cast<long long>(batch) * rows >= 256 * per_cu && p.span_max <= 8192;
+  if (p.per_seq) p.n_wg = batch;
   return p;
 }
 
 DecodeWorkspace decode_workspace(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t q_len,
                                  const DecodePlan& p) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  const size_t rows = static_cast<size_t>(batch) * num_heads * static_cast<size_t>(q_len) * p.n_split;
+  const size_t b = static_cast<size_t>(batch > 0 ? batch : 0);
+  const size_t rows = (static_cast<size_t>(p.n_wg) + b) * static_cast<size_t>(q_len) * static_cast<size_t>(num_heads);
   DecodeWorkspace w;
-  w.o_off = 0;
-  w.m_off = up(rows * L.head_dim * sizeof(float));
+  w.prefix_off = 0;
+  w.lo_off = up((b + 1) * sizeof(int64_t));
+  w.o_off = w.lo_off + up(b * sizeof(int32_t) + 4);
+  w.m_off = w.o_off + up(rows * static_cast<size_t>(L.head_dim) * sizeof(float));
   w.l_off = w.m_off + up(rows * sizeof(float));
   w.total = w.l_off + up(rows * sizeof(float));
   return w;

@@ -23,22 +23,29 @@ bool prologue_dim_supported(int32_t d);
 bool attn_dim_supported(int32_t d);
 bool attn_group_supported(int32_t g);
 
-// Split-KV decode plan: keys of one (sequence, KV head) are cut into n_split
-// chunks of `chunk` keys (a power of two, >= 256), counted from the first key
-// the sequence reads.  `span_max` is the longest key range one sequence can
-// read: min(W + q_len - 1, max_ctx) on local layers (q_len query tokens at the
-// end of the context), max_ctx on global layers.
+// Split-KV decode plan.  The keys every sequence reads are laid end to end
+// (on the device, from ctx_len) and each (KV head, 16-column block) row of
+// the grid gets n_wg workgroups that take equal consecutive ranges of that
+// line.  n_wg targets one round of workgroups on 256 CUs (workgroups per CU
+// from the split kernel's LDS ring), within [line/16384, line/256] for the
+// longest possible line (B x span_max keys).  When every span is short and
+// the sequences alone fill the round, workgroup w takes sequence w instead.  `span_max` is
+// the longest key range one sequence can read: min(W + q_len - 1, max_ctx) on
+// local layers (q_len query tokens at the end of the context), max_ctx on
+// global layers.
 struct DecodePlan {
-  int32_t chunk;
-  int32_t n_split;
+  int32_t n_wg;
   int32_t span_max;
+  bool per_seq;   // workgroup w takes sequence w whole (n_wg = B); see decode_plan
 };
 DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t max_ctx, int32_t q_len);
 
-// Workspace layout: o partials fp32 [B, q_len, Hq, n_split, D], then m and l
-// fp32 [B, q_len, Hq, n_split] each; every region starts on a 256-byte boundary.
+// Workspace layout, every region on a 256-byte boundary: int64 prefix sums of
+// the spans [B + 1]; int32 first readable keys [B]; then fp32 partials for
+// n_wg + B slots (a workgroup's range touching sequence b stores at slot
+// w + b): o [slots, q_len, Hq, D], m and l [slots, q_len, Hq].
 struct DecodeWorkspace {
-  size_t o_off, m_off, l_off, total;
+  size_t prefix_off, lo_off, o_off, m_off, l_off, total;
 };
 DecodeWorkspace decode_workspace(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t q_len,
                                  const DecodePlan& p);

@@ -143,14 +143,25 @@ def test_argument_errors_before_any_launch(ga):
     assert ga.load().gemma_attn_strerror(ga.GA_ERR_WORKSPACE).decode().startswith("decode workspace")
 
 
+def _decode_ws_bytes(B, q_len, Hq, D, n_wg):
+    """The documented layout: int64 prefix [B+1], int32 lo [B], then fp32 o, m, l for n_wg + B slots."""
+    up = lambda x: (x + 255) // 256 * 256
+    rows = (n_wg + B) * q_len * Hq
+    return up((B + 1) * 8) + up(B * 4 + 4) + up(rows * D * 4) + 2 * up(rows * 4)
+
+
 @pytest.mark.parametrize("W,max_ctx,B", [(1024, 65536, 64), (0, 65536, 64), (0, 100, 1), (4096, 3000, 2), (0, 1, 1)])
 def test_decode_workspace_covers_every_split(ga, W, max_ctx, B):
     kw = dict(num_heads=16, num_kv_heads=8, head_dim=256, sliding_window=W, sliding_window_pattern=0)
     need = ga.decode_workspace_size(kw, 0, B, max_ctx)
-    L = R.resolve_layer(R.GemmaAttnConfig(**kw), 0)
+    # 8 KV heads x 1 column block = 8 grid rows; D = 256 with separate K and V: a 64 KB ring, two
+    # workgroups per CU -> 512 // 8 = 64 per row, kept within [line/16384, line/256] keys
     span = min(W, max_ctx) if W else max_ctx
-    # at least one fp32 (o[D], m, l) record per (sequence, head, 4096-key chunk) of the longest span
-    assert need >= B * 16 * (L["head_dim"] + 2) * 4 * -(-span // 4096)
+    line = B * span
+    n_wg = max(1, min(max(512 // 8, -(-line // 16384)), -(-line // 256)))
+    if B * 8 >= 512 and span <= 8192:
+        n_wg = B                                        # one workgroup per sequence and row
+    assert need == _decode_ws_bytes(B, 1, 16, 256, n_wg)
 
 
 def test_multi_token_entry_points_reject_bad_arguments(ga):
@@ -193,8 +204,12 @@ def test_decode_multi_workspace_covers_every_split(ga, W, max_ctx, B, q_len):
     kw = dict(num_heads=16, num_kv_heads=8, head_dim=256, sliding_window=W, sliding_window_pattern=0)
     need = ga.decode_multi_workspace_size(kw, 0, B, q_len, max_ctx)
     span = min(W + q_len - 1, max_ctx) if W else max_ctx
-    # one fp32 (o[D], m, l) record per (sequence, token, head, 4096-key chunk) of the longest span
-    assert need >= B * q_len * 16 * (256 + 2) * 4 * -(-span // 4096)
+    rows = 8 * -(-2 * q_len // 16)                      # KV heads x 16-column blocks (g = 2)
+    line = B * span
+    n_wg = max(1, min(max(512 // rows, -(-line // 16384)), -(-line // 256)))
+    if B * rows >= 512 and span <= 8192:
+        n_wg = B
+    assert need == _decode_ws_bytes(B, q_len, 16, 256, n_wg)
 
 
 def test_int8_entry_points_reject_bad_arguments(ga):
