@@ -8,21 +8,34 @@
 // (token, head) vector of the bf16-rounded result as codes
 // round-half-even(x / s) with s = max|x| / 127 (fp32 division), plus s.
 //
-// One workgroup per group of kTok consecutive tokens (flattened over batch and
-// sequence).  The rotary frequencies w_i = theta^(-2i/r) are formed once per
-// workgroup in fp64, then each token's cos/sin(p * w_i) table (angle reduced
-// modulo 2*pi in fp64, fp32 sincos) goes to LDS; the row loads are issued
-// before the tables are built so their latency overlaps it.  Each head row of
-// width D is handled by D/8 lanes holding 8 contiguous bf16 (one 16-byte
-// load); the RMS reduction is a butterfly inside those lanes.  The rotate-half
-// partner of element d (d +- r/2) sits r/16 lanes away at the same slot, so
-// when r/16 is a power of two it is one lane shuffle (lane ^ r/16); other
-// rotary widths go through an LDS copy of the normalised row.
+// The kernel streams rows (2 bytes read and 2 written per element), so it is
+// laid out to keep HBM busy while spending few VALU instructions per row (a
+// wave64 VALU instruction holds its SIMD for four cycles, and at 16-byte rows
+// per lane that budget is small):
+//  - persistent workgroups walk fixed-size items of consecutive (token, head)
+//    rows; the next item's 16-byte row loads are issued before the current
+//    item is worked on, so they stay in flight under its table build and row
+//    math;
+//  - the rotary frequencies w_i = theta^(-2i/r) (fp64) and the norm weights
+//    are formed once per workgroup; per item, each token's cos/sin(p * w_i)
+//    (angle reduced to [-pi, pi] in fp64 with a two-term 2*pi, fp32 sincos)
+//    goes to an LDS table laid out per element, with the rotate-half sign
+//    folded in, so every element is one multiply and one FMA;
+//  - each head row of width D is handled by D/8 lanes holding 8 contiguous
+//    bf16; the RMS (and int8 absmax) reductions run inside those lanes with
+//    DPP and lane swaps, and only on rows that have a norm weight.
+// The rotate-half partner of element d (d +- r/2) sits r/16 lanes away at the
+// same slot, so when r/16 is a power of two it is one lane shuffle (lane ^
+// r/16); other rotary widths go through an LDS copy of the normalised row.
 //
 // Sources: RMSNorm QK-norm (google-gemma-4 atlas summary; weight used as w on
 // Gemma 4, "Plain-weight RMSNorm", and as 1 + w on earlier Gemma), partial
 // rotary ("Zero-pad partial rope", Gemma 4 page) and dual bases (Gemma 3 page,
 // "Dual RoPE bases").
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
 #include "ga_device.h"
 #include "ga_kernels.h"
 
@@ -31,8 +44,15 @@ namespace ga {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTok = 4;                 // tokens per workgroup
-constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr int kLoads = 7;               // 16-byte row loads per lane per item
+// Tokens whose cos/sin tables (D entries of 8 bytes each) an item may touch:
+// 32 KB of LDS up to D = 256, 28 KB at D = 512, at most 64 tokens.
+constexpr int32_t tab_tokens(int32_t dim) {
+  return dim <= 256 ? (4096 / dim < 64 ? 4096 / dim : 64) : 3584 / dim;
+}
+constexpr double kInv2Pi = 0.15915494309189533577;
+constexpr double kTwoPiHi = 6.283185307179586232;          // 2*pi rounded to double
+constexpr double kTwoPiLo = 2.4492935982947064e-16;        // 2*pi - kTwoPiHi
 
 struct ProParams {
   const uint16_t* q_in;
@@ -49,220 +69,353 @@ struct ProParams {
   float* k_scales;            //   and scales [B,Hkv,max_ctx] replace k_out / v_out
   int8_t* v_codes;
   float* v_scales;
-  int64_t tokens;
-  int32_t seq, hq, hkv, dim, rotary_dim, max_ctx;   // max_ctx > 0: cache mode
+  int32_t tokens, rows_per_item;
+  int32_t seq, hq, hkv, rotary_dim, max_ctx;   // max_ctx > 0: cache mode
   double theta;
   double pos_div;
   float eps, offset;
 };
 
-// Position of token s of sequence b.
-__device__ __forceinline__ int64_t token_pos(const ProParams& p, int32_t b, int32_t s) {
-  if (p.ctx_len) {
-    int32_t c = p.ctx_len[b];
-    c = c < 0 ? 0 : (c > p.max_ctx ? p.max_ctx : c);
-    return static_cast<int64_t>(c) - p.seq + s;
+// Reduction of v over the TPR consecutive lanes of a row, every lane getting
+// the result: quad swaps, half-row and row mirrors (DPP), then the 16- and
+// 32-lane swaps.  Each step combines a value with one from the other half of
+// its group, so every lane forms the same operands and ends bitwise equal.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int TPR, typename Op>
+__device__ __forceinline__ float row_reduce(float v, Op op) {
+  if constexpr (TPR >= 2) v = op(v, dpp_mov<0xB1>(v));    // quad_perm [1,0,3,2]
+  if constexpr (TPR >= 4) v = op(v, dpp_mov<0x4E>(v));    // quad_perm [2,3,0,1]
+  if constexpr (TPR >= 8) v = op(v, dpp_mov<0x141>(v));   // row_half_mirror
+  if constexpr (TPR >= 16) v = op(v, dpp_mov<0x140>(v));  // row_mirror
+  if constexpr (TPR >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
-  return static_cast<int64_t>(p.pos0 ? p.pos0[b] : 0) + s;
+  if constexpr (TPR >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return v;
 }
 
 // SHFL: the partner is lane ^ (r/16) (r/16 a power of two, r <= D); else LDS.
-template <bool SHFL>
-__global__ __launch_bounds__(kThreads) void qk_prologue_kernel(ProParams p) {
+//
+// Persistent: rows are numbered token-major over the whole launch (row
+// t * heads + h is head h of token t: the q heads, then the k heads, then in
+// cache mode the v heads, copied unchanged), and item j is rows
+// [j * rpi, (j + 1) * rpi).  Workgroup w takes items w, w + G, w + 2G, ...
+// (G = grid size) and issues the next item's row loads before it builds the
+// current item's tables and processes its rows, so HBM always has the block's
+// next rows in flight.
+//
+// Per token the cos/sin table has one entry per element d of the head row:
+// (cos, -sin) of w_d for d < r/2, (cos, +sin) of w_{d-r/2} for r/2 <= d < r,
+// so element d's result is x_d cos + partner_d * entry.y in both halves.
+template <int TPR, bool SHFL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SHFL ? 4 : 3))) void qk_prologue_kernel(
+    ProParams p) {
+  constexpr int32_t tpr = TPR;                  // lanes per row
+  constexpr int32_t dim = TPR * 8;
+  constexpr int32_t rpp = kThreads / TPR;       // rows per pass
+  constexpr int32_t kTabTok = tab_tokens(dim);
   __shared__ double omega[256];
-  __shared__ float2 cs_tab[kTok][256];
+  __shared__ __attribute__((aligned(16))) float2 cs_tab[kTabTok * dim];
+  __shared__ __attribute__((aligned(16))) float wtab[2][dim];   // q and k weights + offset
+  __shared__ int64_t tok_pos[2][kTabTok];      // double-buffered: one item ahead
+  __shared__ int32_t tok_b[2][kTabTok];
   __shared__ float rowbuf[SHFL ? 1 : kThreads * 8];
 
   const int32_t tid = threadIdx.x;
   const int32_t half = p.rotary_dim >> 1;
-  const int32_t dim = p.dim;
-  const int32_t tpr = dim >> 3;                 // lanes per row (power of two <= 64)
-  const int32_t rows_per_pass = kThreads / tpr;
   const int32_t heads = p.hq + (p.k_in ? p.hkv : 0) + (p.v_in ? p.hkv : 0);
-  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kTok;
-  const int32_t rows = kTok * heads;
+  const int32_t rpi = p.rows_per_item;
+  const int64_t n_rows = static_cast<int64_t>(p.tokens) * heads;
+  const int64_t n_items = (n_rows + rpi - 1) / rpi;
   const int32_t sub = tid / tpr;
   const int32_t lane = tid % tpr;
   const int32_t d0 = lane * 8;
-
-  // Row r of this workgroup: token tok0 + r / heads, head r % heads: the q
-  // heads, then the k heads, then (cache mode) the v heads, which are copied
-  // unchanged.  In cache mode k and v rows go to cache row pos of their token
-  // and are skipped when that row is outside the cache; in int8 cache mode
-  // they go to the code row (cdst) and the scale slot (sdst) instead of dst.
-  struct RowDst {
-    uint16_t* dst;
-    int8_t* cdst;
-    float* sdst;
+  // Local row r (counted from the item's first token) is head r % heads of
+  // token r / heads; the quotient is taken in fp32 as (r + 1/2) / heads: the
+  // exact value is at least 1/(2 heads) from an integer and the two roundings
+  // move it by under r * 2^-23 / heads, so the truncation is exact for r < 2^22.
+  const float inv_heads = 1.0f / static_cast<float>(heads);
+  auto split = [&](int32_t row, int32_t& tt, int32_t& hh) __attribute__((always_inline)) {
+    tt = static_cast<int32_t>((static_cast<float>(row) + 0.5f) * inv_heads);
+    hh = row - tt * heads;
   };
-  auto row_ptrs = [&](int32_t row, const uint16_t*& src, RowDst& out, const float*& w, bool& copy) -> bool {
-    const int32_t tt = row / heads;
-    const int32_t hh = row % heads;
-    const int64_t token = tok0 + tt;
-    copy = false;
-    out = RowDst{nullptr, nullptr, nullptr};
-    if (row >= rows || token >= p.tokens) return false;
-    if (hh < p.hq) {
-      const int64_t off = (token * p.hq + hh) * dim + d0;
-      src = p.q_in + off;
-      out.dst = p.q_out + off;
-      w = p.qw;
-      return true;
+  // Element offset of head hh of token tok in its row-layout array.
+  auto row_off = [&](int32_t tok, int32_t hh) __attribute__((always_inline)) -> int64_t {
+    const int32_t hx = hh < p.hq ? p.hq : p.hkv;
+    const int32_t hk = hh - p.hq;
+    const int32_t hi = hh < p.hq ? hh : (hk < p.hkv ? hk : hk - p.hkv);
+    return (static_cast<int64_t>(tok) * hx + hi) * dim + d0;
+  };
+  // First token of item j and the item's first row counted from that token.
+  auto item_start = [&](int64_t j, int32_t& tok_first, int32_t& r0) __attribute__((always_inline)) {
+    const int64_t row0 = j * rpi;
+    tok_first = static_cast<int32_t>(row0 / heads);
+    r0 = static_cast<int32_t>(row0 - static_cast<int64_t>(tok_first) * heads);
+  };
+  auto load_item = [&](int64_t j, u32x4 (&buf)[kLoads]) __attribute__((always_inline)) {
+    int32_t tok_first = 0, r0 = 0, lim = 0;
+    if (j < n_items) {
+      item_start(j, tok_first, r0);
+      lim = static_cast<int32_t>(min<int64_t>(rpi, n_rows - j * rpi));
     }
-    const int32_t kh = (hh - p.hq) % p.hkv;
-    const bool is_v = hh >= p.hq + p.hkv;
-    src = (is_v ? p.v_in : p.k_in) + (token * p.hkv + kh) * dim + d0;
-    w = is_v ? nullptr : p.kw;
-    copy = is_v;
-    if (p.max_ctx > 0) {
-      const int32_t b = static_cast<int32_t>(token / p.seq);
-      const int64_t pos = token_pos(p, b, static_cast<int32_t>(token % p.seq));
-      if (pos < 0 || pos >= p.max_ctx) return false;
-      const int64_t crow = (static_cast<int64_t>(b) * p.max_ctx + pos) * p.hkv + kh;
-      if (p.k_scales) {
-        out.cdst = (is_v ? p.v_codes : p.k_codes) + crow * dim + d0;
-        out.sdst = (is_v ? p.v_scales : p.k_scales) + (static_cast<int64_t>(b) * p.hkv + kh) * p.max_ctx + pos;
-      } else {
-        out.dst = (is_v ? p.v_out : p.k_out) + crow * dim + d0;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      buf[i] = u32x4{0u, 0u, 0u, 0u};
+      const int32_t r = i * rpp + sub;
+      if (r < lim) {
+        int32_t tt, hh;
+        split(r + r0, tt, hh);
+        const uint16_t* base = hh < p.hq ? p.q_in : (hh < p.hq + p.hkv ? p.k_in : p.v_in);
+        buf[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + row_off(tok_first + tt, hh)));
       }
-    } else {
-      out.dst = p.k_out + (token * p.hkv + kh) * dim + d0;
     }
-    return true;
   };
 
-  // Issue the first pass's row load before building the tables.
-  u32x4 raw = u32x4{0u, 0u, 0u, 0u};
-  {
-    const uint16_t* src;
-    RowDst od;
-    const float* w;
-    bool cp;
-    if (row_ptrs(sub, src, od, w, cp)) raw = *reinterpret_cast<const u32x4*>(src);
-  }
-
-  // (p / pos_div) * w_i, formed as p * (w_i / pos_div).
-  for (int32_t i = tid; i < half; i += kThreads) omega[i] = pow(p.theta, -2.0 * i / p.rotary_dim) / p.pos_div;
-  __syncthreads();
-  for (int32_t e = tid; e < kTok * half; e += kThreads) {
-    const int32_t tt = e / half;
-    const int32_t i = e % half;
-    const int64_t token = tok0 + tt;
-    float sn = 0.f, cn = 1.f;
-    if (token < p.tokens) {
-      const int32_t b = static_cast<int32_t>(token / p.seq);
-      const int32_t s = static_cast<int32_t>(token % p.seq);
-      const int64_t pos = token_pos(p, b, s);
-      double ang = fmod(static_cast<double>(pos) * omega[i], kTwoPi);
-      if (ang < 0) ang += kTwoPi;
-      sincosf(static_cast<float>(ang), &sn, &cn);
+  // Sequence and position of token tid of item j: fetch_tok issues the
+  // position-array load early (so waiting for it does not wait for the row
+  // loads issued after it), commit_tok stores the result into buffer buf.
+  struct TokInfo {
+    int32_t t, b, s, raw;
+  };
+  auto fetch_tok = [&](int64_t j) __attribute__((always_inline)) -> TokInfo {
+    TokInfo ti{-1, 0, 0, 0};
+    if (j >= n_items) return ti;
+    int32_t tok_first, r0;
+    item_start(j, tok_first, r0);
+    const int32_t lim = static_cast<int32_t>(min<int64_t>(rpi, n_rows - j * rpi));
+    const int32_t ntok = (r0 + lim - 1) / heads + 1;        // <= kTabTok <= kThreads
+    if (tid < ntok) {
+      const int32_t token = tok_first + tid;
+      ti.t = tid;
+      ti.b = token / p.seq;
+      ti.s = token - ti.b * p.seq;
+      if (p.ctx_len) ti.raw = p.ctx_len[ti.b];
+      else if (p.pos0) ti.raw = p.pos0[ti.b];
     }
-    cs_tab[tt][i] = make_float2(cn, sn);
+    return ti;
+  };
+  auto commit_tok = [&](const TokInfo& ti, int buf) __attribute__((always_inline)) {
+    if (ti.t < 0) return;
+    int64_t pos;
+    if (p.ctx_len) {
+      const int32_t c = ti.raw < 0 ? 0 : (ti.raw > p.max_ctx ? p.max_ctx : ti.raw);
+      pos = static_cast<int64_t>(c) - p.seq + ti.s;
+    } else {
+      pos = static_cast<int64_t>(ti.raw) + ti.s;
+    }
+    tok_b[buf][ti.t] = ti.b;
+    tok_pos[buf][ti.t] = pos;
+  };
+
+  int64_t j = blockIdx.x;
+  u32x4 cur[kLoads];
+  TokInfo nt_cur = fetch_tok(j);
+  load_item(j, cur);
+  // Once per workgroup: (p / pos_div) * w_i, formed as p * (w_i / pos_div);
+  // the norm weights; the pass-through entries.
+  for (int32_t i = tid; i < half; i += kThreads) omega[i] = pow(p.theta, -2.0 * i / p.rotary_dim) / p.pos_div;
+  for (int32_t d = tid; d < dim; d += kThreads) {
+    wtab[0][d] = p.qw ? p.qw[d] + p.offset : 1.0f;
+    wtab[1][d] = p.kw ? p.kw[d] + p.offset : 1.0f;
   }
-  __syncthreads();
+  for (int32_t e = tid; e < kTabTok * dim; e += kThreads)
+    if (e % dim >= p.rotary_dim) cs_tab[e] = make_float2(1.0f, 0.0f);
+  const bool q_norm = p.qw != nullptr, k_norm = p.kw != nullptr;
 
   const int32_t pmask = p.rotary_dim >> 4;   // partner lane distance (SHFL)
-  for (int32_t row0 = 0; row0 < rows; row0 += rows_per_pass) {
-    const int32_t row = row0 + sub;
-    const uint16_t* src = nullptr;
-    RowDst od;
-    const float* w = nullptr;
-    bool copy = false;
-    const bool active = row_ptrs(row, src, od, w, copy);
-    // prefetch the next pass's row
-    u32x4 next = u32x4{0u, 0u, 0u, 0u};
-    if (row0 + rows_per_pass < rows) {
-      const uint16_t* s2;
-      RowDst d2;
-      const float* w2;
-      bool c2;
-      if (row_ptrs(row + rows_per_pass, s2, d2, w2, c2)) next = *reinterpret_cast<const u32x4*>(s2);
+  const bool any_keep = p.rotary_dim < dim || p.v_in != nullptr;
+  // One item: tables, then its rows from cur (token positions in buffer it).
+  auto step = [&](int64_t j, int it, const u32x4 (&cur)[kLoads]) __attribute__((always_inline)) {
+    int32_t tok_first, r0;
+    item_start(j, tok_first, r0);
+    const int32_t lim = static_cast<int32_t>(min<int64_t>(rpi, n_rows - j * rpi));
+    const int32_t ntok = (r0 + lim - 1) / heads + 1;
+
+    // The cos/sin tables of this item (the barrier first lets every wave
+    // finish reading the previous item's tables and makes this item's token
+    // positions visible).
+    __syncthreads();
+    for (int32_t e = tid; e < ntok * half; e += kThreads) {
+      const int32_t tt = e / half;
+      const int32_t i = e - tt * half;
+      const double ang = static_cast<double>(tok_pos[it][tt]) * omega[i];
+      const double k = rint(ang * kInv2Pi);
+      const double red = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
+      float sn, cn;
+      sincosf(static_cast<float>(red), &sn, &cn);
+      cs_tab[tt * dim + i] = make_float2(cn, -sn);
+      cs_tab[tt * dim + half + i] = make_float2(cn, sn);
     }
-    float x[8];
+    __syncthreads();
+
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = lo_bf16(raw[e]);
-      x[2 * e + 1] = hi_bf16(raw[e]);
-    }
-    // RMSNorm (only when this side has a weight).
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-    for (int m = tpr >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    if (active && w) {
-      const float inv = 1.0f / sqrtf(ss / static_cast<float>(dim) + p.eps);
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + d0);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + d0 + 4);
+    for (int i = 0; i < kLoads; ++i) {
+      const int32_t r = i * rpp + sub;
+      const bool in_range = r < lim;
+      int32_t tt, hh;
+      split(in_range ? r + r0 : 0, tt, hh);
+      const int32_t token = tok_first + tt;
+      const bool is_q = hh < p.hq;
+      const bool is_v = hh >= p.hq + p.hkv;
+      // Destination; k and v rows outside the cache are skipped.
+      uint16_t* dst = nullptr;
+      int8_t* cdst = nullptr;
+      float* sdst = nullptr;
+      bool active = in_range;
+      if (is_q) {
+        dst = p.q_out + row_off(token, hh);
+      } else if (p.max_ctx > 0) {
+        const int32_t kh = is_v ? hh - p.hq - p.hkv : hh - p.hq;
+        const int64_t pos = tok_pos[it][tt];
+        const int32_t b = tok_b[it][tt];
+        if (pos < 0 || pos >= p.max_ctx) active = false;
+        const int64_t crow = (static_cast<int64_t>(b) * p.max_ctx + pos) * p.hkv + kh;
+        if (p.k_scales) {
+          cdst = (is_v ? p.v_codes : p.k_codes) + crow * dim + d0;
+          sdst = (is_v ? p.v_scales : p.k_scales) + (static_cast<int64_t>(b) * p.hkv + kh) * p.max_ctx + pos;
+        } else {
+          dst = (is_v ? p.v_out : p.k_out) + crow * dim + d0;
+        }
+      } else {
+        dst = p.k_out + row_off(token, hh);
+      }
+
+      float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = x[e] * inv * (w0[e] + p.offset);
-        x[e + 4] = x[e + 4] * inv * (w1[e] + p.offset);
+        x[2 * e] = lo_bf16(cur[i][e]);
+        x[2 * e + 1] = hi_bf16(cur[i][e]);
       }
-    }
-    float partner[8];
-    if constexpr (SHFL) {
+      // RMSNorm where this side has a weight: x * rsqrt(mean x^2 + eps) * (w +
+      // offset).  All lanes of a row take the same branch, and the reduction
+      // stays inside the row.
+      const bool norm = is_q ? q_norm : (!is_v && k_norm);
+      if (norm) {
+        float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) partner[e] = __shfl_xor(x[e], pmask, 64);
-    } else {
-      float* rb = rowbuf + sub * dim;
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+        ss = row_reduce<TPR>(ss, [](float a, float b) { return a + b; });
+        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / static_cast<float>(dim)) + p.eps);
+        const float* wrow = wtab[is_q ? 0 : 1] + d0;
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wrow);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wrow + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rb[d0 + e] = x[e];
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int32_t d = d0 + e;
-        partner[e] = d < half ? rb[d + half] : (d < p.rotary_dim ? rb[d - half] : 0.f);
-      }
-      __syncthreads();
-    }
-    // Rows past the end take the last token's table (their results are dropped).
-    const int32_t tt = min(row / heads, kTok - 1);
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int32_t d = d0 + e;
-      if (copy) {
-        y[e] = x[e];
-      } else if (d < half) {
-        const float2 c = cs_tab[tt][d];
-        y[e] = x[e] * c.x - partner[e] * c.y;
-      } else if (d < p.rotary_dim) {
-        const float2 c = cs_tab[tt][d - half];
-        y[e] = x[e] * c.x + partner[e] * c.y;
-      } else {
-        y[e] = x[e];
-      }
-    }
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
-    if (p.k_scales) {
-      // int8 cache mode: every lane joins the row's max reduction.
-      float amax = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(o[e])), fabsf(hi_bf16(o[e]))));
-      for (int m = tpr >> 1; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-      if (active && od.cdst) {
-        const float sc = amax / 127.0f;
-        uint32_t cw[2] = {0u, 0u};
-        if (sc > 0.f) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = (e & 1) ? hi_bf16(o[e >> 1]) : lo_bf16(o[e >> 1]);
-            const int32_t c = static_cast<int32_t>(__builtin_rintf(v / sc));
-            cw[e >> 2] |= (static_cast<uint32_t>(c) & 0xffu) << (8 * (e & 3));
-          }
+        for (int e = 0; e < 4; ++e) {
+          x[e] = x[e] * inv * w0[e];
+          x[e + 4] = x[e + 4] * inv * w1[e];
         }
-        *reinterpret_cast<u32x2*>(od.cdst) = u32x2{cw[0], cw[1]};
-        if (lane == 0) *od.sdst = sc;
-      } else if (active) {
-        *reinterpret_cast<u32x4*>(od.dst) = o;
       }
-    } else if (active) {
-      *reinterpret_cast<u32x4*>(od.dst) = o;
+      float partner[8];
+      if constexpr (SHFL) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) partner[e] = __shfl_xor(x[e], pmask, 64);
+      } else {
+        float* rb = rowbuf + sub * dim;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rb[d0 + e] = x[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int32_t d = d0 + e;
+          partner[e] = d < half ? rb[d + half] : (d < p.rotary_dim ? rb[d - half] : 0.f);
+        }
+        __syncthreads();
+      }
+      const f32x4* cs = reinterpret_cast<const f32x4*>(cs_tab + tt * dim + d0);
+      float y[8];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const f32x4 c2 = cs[e2];                 // entries d0 + 2 e2 and d0 + 2 e2 + 1
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * e2 + h;
+          const float rot = x[e] * c2[2 * h] + partner[e] * c2[2 * h + 1];
+          y[e] = any_keep && (is_v || d0 + e >= p.rotary_dim) ? x[e] : rot;   // v rows, pass-through part
+        }
+      }
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+      if (p.k_scales) {
+        // int8 cache mode: every lane joins the row's max reduction.
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(lo_bf16(o[e])), fabsf(hi_bf16(o[e]))));
+        amax = row_reduce<TPR>(amax, [](float a, float b) { return fmaxf(a, b); });
+        if (active && cdst) {
+          const float sc = amax / 127.0f;
+          uint32_t cw[2] = {0u, 0u};
+          if (sc > 0.f) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = (e & 1) ? hi_bf16(o[e >> 1]) : lo_bf16(o[e >> 1]);
+              const int32_t q = static_cast<int32_t>(__builtin_rintf(v / sc));
+              cw[e >> 2] |= (static_cast<uint32_t>(q) & 0xffu) << (8 * (e & 3));
+            }
+          }
+          *reinterpret_cast<u32x2*>(cdst) = u32x2{cw[0], cw[1]};
+          if (lane == 0) *sdst = sc;
+        } else if (active) {
+          *reinterpret_cast<u32x4*>(dst) = o;
+        }
+      } else if (active) {
+        *reinterpret_cast<u32x4*>(dst) = o;
+      }
     }
-    raw = next;
+  };
+
+  // Two named buffers in turn.  Each item starts by waiting for all of its
+  // loads (issued during the previous item), then issues the next item's, so
+  // those stay in flight while this item's tables are built and its rows
+  // processed.  Token positions go to buffer it; the other buffer may still
+  // be read by waves processing the previous item, and this one was last
+  // read two items ago, before the previous item's first barrier.
+  constexpr int kWaitVm0 = 0x0F70;          // s_waitcnt vmcnt(0), other counters untouched
+  u32x4 alt[kLoads];
+  TokInfo nt_alt;
+  for (int it = 0;;) {
+    if (j >= n_items) break;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    commit_tok(nt_cur, it);
+    nt_alt = fetch_tok(j + gridDim.x);
+    load_item(j + gridDim.x, alt);
+    step(j, it, cur);
+    j += gridDim.x;
+    it ^= 1;
+    if (j >= n_items) break;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    commit_tok(nt_alt, it);
+    nt_cur = fetch_tok(j + gridDim.x);
+    load_item(j + gridDim.x, cur);
+    step(j, it, alt);
+    j += gridDim.x;
+    it ^= 1;
   }
+}
+
+// Resident workgroups per CU of one instantiation on the current device
+// (cached per device; the value is the same whichever thread computes it).
+template <int TPR, bool SHFL>
+int resident_grid() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, qk_prologue_kernel<TPR, SHFL>, kThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 || cus < 1)
+    return 0;
+  v = per_cu * cus;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 }  // namespace
@@ -286,24 +439,54 @@ hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream) {
   p.v_codes = static_cast<int8_t*>(a.v_codes);
   p.v_scales = a.v_scales;
   p.max_ctx = a.max_ctx;
-  p.tokens = tokens;
+  p.tokens = static_cast<int32_t>(tokens);
   p.seq = a.seq;
   p.hq = a.hq;
   p.hkv = a.hkv;
-  p.dim = a.dim;
   p.rotary_dim = a.rotary_dim;
   p.theta = a.theta;
   p.pos_div = a.pos_div > 0.0 ? a.pos_div : 1.0;
   p.eps = a.eps;
   p.offset = a.offset;
-  const int64_t blocks = (tokens + kTok - 1) / kTok;
+  // Rows per item: kLoads passes of the block, fewer when the tokens an item
+  // can touch would not fit the LDS tables.
+  const int32_t heads = a.hq + (a.k_in ? a.hkv : 0) + (a.v_in ? a.hkv : 0);
+  if (heads < 1) return hipErrorInvalidValue;
+  const int32_t rpp = kThreads / (a.dim >> 3);
+  const int32_t tab_tok = tab_tokens(a.dim);     // >= 7
+  // An item of n rows touches at most (n - 1) / heads + 2 tokens.
+  const int32_t rpi = std::max(1, std::min(kLoads * rpp, (tab_tok - 2) * heads + 1));
+  p.rows_per_item = rpi;
+  const int64_t items = (tokens * heads + rpi - 1) / rpi;
   const int32_t r16 = a.rotary_dim >> 4;
   const bool shfl = a.rotary_dim % 16 == 0 && r16 > 0 && (r16 & (r16 - 1)) == 0 && a.rotary_dim <= a.dim;
-  if (shfl || a.rotary_dim == 0) {
-    hipLaunchKernelGGL(qk_prologue_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(qk_prologue_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, p);
+  const bool use_shfl = shfl || a.rotary_dim == 0;
+  hipError_t err = hipSuccess;
+  auto go = [&](auto tpr_c) {
+    constexpr int T = decltype(tpr_c)::value;
+    const int resident = use_shfl ? resident_grid<T, true>() : resident_grid<T, false>();
+    if (resident < 1) {
+      err = hipErrorInvalidDeviceFunction;
+      return;
+    }
+    const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>(items, resident));
+    if (use_shfl) {
+      hipLaunchKernelGGL((qk_prologue_kernel<T, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((qk_prologue_kernel<T, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    }
+  };
+  switch (a.dim >> 3) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 8: go(std::integral_constant<int, 8>{}); break;
+    case 16: go(std::integral_constant<int, 16>{}); break;
+    case 32: go(std::integral_constant<int, 32>{}); break;
+    case 64: go(std::integral_constant<int, 64>{}); break;
+    default: return hipErrorInvalidValue;
   }
+  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 

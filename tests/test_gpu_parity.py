@@ -78,26 +78,38 @@ def test_end_to_end_layer(gpu, name, kw, layer, B, S, norm):
 
 
 # ----------------------------------------------------------------------------- prologue only
+_WIDE = dict(sliding_window=0, sliding_window_pattern=1, rope_theta=1e4)
 PRO = [
-    ("d64_full", TINY, 0, None, [0]),
-    ("d256_norm1", GEMMA3, 0, 1, [0, 70000]),
-    ("d512_partial_norm0", GEMMA4, 5, 0, [3, 65535]),
-    ("d256_partial_local", GEMMA4, 1, 0, [0, 12345]),
-    ("d256_global_rope_scaled8", GEMMA3 | dict(rope_scaling_factor=8.0), 5, 1, [5, 98765]),
-    ("d512_global_rope_scaled3", GEMMA4 | dict(rope_scaling_factor=3.0), 5, 0, [0, 200001]),
-    ("d256_local_ignores_scaling", GEMMA3 | dict(rope_scaling_factor=8.0), 0, 1, [7, 4321]),
+    ("d64_full", TINY, 0, None, [0], 67),
+    ("d256_norm1", GEMMA3, 0, 1, [0, 70000], 67),
+    ("d512_partial_norm0", GEMMA4, 5, 0, [3, 65535], 67),
+    ("d256_partial_local", GEMMA4, 1, 0, [0, 12345], 67),
+    ("d256_global_rope_scaled8", GEMMA3 | dict(rope_scaling_factor=8.0), 5, 1, [5, 98765], 67),
+    ("d512_global_rope_scaled3", GEMMA4 | dict(rope_scaling_factor=3.0), 5, 0, [0, 200001], 67),
+    ("d256_local_ignores_scaling", GEMMA3 | dict(rope_scaling_factor=8.0), 0, 1, [7, 4321], 67),
+    # rotary widths whose partner distance r/16 is not a power of two (LDS exchange), a
+    # half-width r/2 that is not a multiple of 8 (lanes straddling the rotary edge)
+    ("d128_rotary48_lds", dict(num_heads=6, num_kv_heads=2, head_dim=128, partial_rotary_factor=0.375) | _WIDE,
+     0, 0, [0, 9, 400], 67),
+    ("d64_rotary18_lds_nonorm", dict(num_heads=3, num_kv_heads=1, head_dim=64, partial_rotary_factor=0.3) | _WIDE,
+     0, None, [2, 0, 77, 5], 67),
+    # more (token, head) rows per token than one work item holds
+    ("d512_40heads", dict(num_heads=32, num_kv_heads=8, head_dim=512) | _WIDE, 0, 0, [0, 3000], 67),
+    # one new token per sequence (decode), many sequences per work item
+    ("d64_seq1", TINY, 0, None, list(range(0, 70 * 37, 37)), 1),
+    ("d256_seq3", GEMMA2, 0, None, list(range(11, 40 * 101, 101)), 3),
 ]
 
 
-@pytest.mark.parametrize("name,kw,layer,offset,pos0", PRO, ids=[p[0] for p in PRO])
-def test_prologue_within_one_ulp(gpu, name, kw, layer, offset, pos0):
+@pytest.mark.parametrize("name,kw,layer,offset,pos0,S", PRO, ids=[p[0] for p in PRO])
+def test_prologue_within_one_ulp(gpu, name, kw, layer, offset, pos0, S):
     ga = gpu
     kw = dict(kw)
     if offset is not None:
         kw["norm_weight_offset"] = offset
     B = len(pos0)
-    cfg, L, q, k, _, qw, kw_ = _layer_inputs(kw, layer, B, 67, seed=300, with_norm=offset is not None)
-    print(f"[prologue] {name}", flush=True)
+    cfg, L, q, k, _, qw, kw_ = _layer_inputs(kw, layer, B, S, seed=300, with_norm=offset is not None)
+    print(f"[prologue] {name} B={B} S={S} D={L['head_dim']} r={L['rotary_dim']}", flush=True)
     p0 = np.array(pos0, dtype=np.int32)
     qt, kt = ga.qk_prologue(kw, layer, to_dev_bf16(q), to_dev_bf16(k),
                             q_norm_w=None if qw is None else to_dev(qw),
