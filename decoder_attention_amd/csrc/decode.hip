@@ -27,6 +27,7 @@
 // the atlas summary on KV caches bounded by the window on local layers), the
 // window, soft cap, scaling and keys-as-values as for prefill.
 #include <type_traits>
+#include <utility>
 
 #include "ga_device.h"
 #include "ga_kernels.h"
@@ -131,20 +132,47 @@ __device__ __forceinline__ int64_t wg_of(int64_t x, int64_t total, int64_t n_wg)
   return w;
 }
 
+// Block placement.  Work item (KV head, key range w) is kvh + Hkv * w; its
+// n_cb column blocks take linear ids 8 apart, so they run on one XCD (linear
+// ids are dealt round-robin to the 8 XCDs) at about the same time, and that
+// XCD's L2 serves the cache rows they all read.  With one column block the
+// order is the item order: the KV heads of one range side by side.
+struct DecodeBlock {
+  int32_t kvh, cb, w;
+  bool valid;
+};
+__device__ __forceinline__ DecodeBlock decode_block(const DecodeParams& p) {
+  const int32_t L = static_cast<int32_t>(blockIdx.x);
+  const int32_t per = 8 * p.n_cb;
+  const int32_t g = L / per;
+  const int32_t r = L - g * per;
+  const int32_t item = g * 8 + (r & 7);
+  DecodeBlock d;
+  d.valid = item < p.hkv * p.n_wg;
+  d.kvh = item % p.hkv;
+  d.w = item / p.hkv;
+  d.cb = r >> 3;
+  return d;
+}
+inline int64_t decode_grid(int32_t hkv, int32_t n_wg, int32_t n_cb) {
+  const int64_t items = static_cast<int64_t>(hkv) * n_wg;
+  return n_cb == 1 ? items : (items + 7) / 8 * 8 * n_cb;
+}
+
 // Calls f(b, s_lo, s_hi, ctx) for every sequence b that this workgroup's range
 // touches, with [s_lo, s_hi) the sequence's keys in the range; uniform across
 // the workgroup.  The caller separates consecutive calls with a barrier.
 template <class F>
-__device__ __forceinline__ void for_each_segment(const DecodeParams& p, F&& f) {
+__device__ __forceinline__ void for_each_segment(const DecodeParams& p, int32_t wg, F&& f) {
   if (p.per_seq) {
-    const int32_t b = blockIdx.y;
+    const int32_t b = wg;
     int32_t lo, ctx;
     seq_range(p, b, lo, ctx);
     if (ctx > lo) f(b, lo, ctx, ctx);
     return;
   }
   const int64_t total = p.prefix[p.batch];
-  const int64_t w = blockIdx.y;
+  const int64_t w = wg;
   const int64_t x0 = wg_start(w, total, p.n_wg);
   const int64_t x1 = wg_start(w + 1, total, p.n_wg);
   if (x0 >= x1) return;
@@ -190,17 +218,47 @@ __device__ __forceinline__ int32_t lane_here() {
   return l & 63;
 }
 
-// Workgroup = 2 waves.  Head width 512: the two waves are one team that
-// streams the same tiles; both compute the full scores (QK^T is a third of the
-// matrix work) and each accumulates O^T for its half of D, so neither holds
-// more than 128 accumulator/query registers.  Narrower heads: each wave is a
-// team of its own and streams its own tiles.  Each team owns two LDS slots.
-template <int D>
+// Workgroup shape.  One 16-column block (CBW = 1): 2 waves.  Head width 512:
+// the two waves are one team that streams the same tiles; both compute the
+// full scores (QK^T is a third of the matrix work) and each accumulates O^T
+// for its half of D, so neither holds more than 128 accumulator/query
+// registers.  Narrower heads: each wave is a team of its own and streams its
+// own tiles.  CBW column blocks per workgroup (CBW > 1): one wave per block
+// (a D-split pair at width 512), all in one team that streams every tile once
+// for all the blocks, through a deeper ring.
+template <int D, int CBW>
 struct DecodeShape {
-  static constexpr int kWaves = 2;
-  static constexpr int kTeam = D > 256 ? 2 : 1;       // waves per team
+  static constexpr int kSplitD = D > 256 ? 2 : 1;          // waves per column block splitting D
+  static constexpr int kWaves = CBW == 1 ? 2 : CBW * kSplitD;
+  static constexpr int kTeam = CBW == 1 ? kSplitD : kWaves;  // waves streaming one tile sequence
   static constexpr int kTeams = kWaves / kTeam;
 };
+
+// f(integral_constant<int, I>) for I = 0, 1, ... in order; static_all stops
+// at the first call that returns false.
+template <class F, int... I>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <class F, int... I>
+__device__ __forceinline__ bool static_all(F&& f, std::integer_sequence<int, I...>) {
+  return (f(std::integral_constant<int, I>{}) && ...);
+}
+
+// s_waitcnt for tile copies: at most n tiles of K ops each still in flight
+// (n runtime, 0 <= n <= N).
+template <int N, int K>
+__device__ __forceinline__ void wait_tiles(int32_t n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vmcnt<N * K>();
+      return;
+    }
+    wait_tiles<N - 1, K>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
 
 // Write the partial (m, l, o) of this workgroup's 16 columns.  One team: both
 // waves hold the same (m, l) and disjoint slices of D.  Two teams (one wave
@@ -258,12 +316,13 @@ __device__ __forceinline__ void write_partial(const DecodeParams& p, int64_t par
   }
 }
 
-template <int D, int G, bool KEQV, bool CAP>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(DecodeParams p) {
-  using Sh = DecodeShape<D>;
+template <int D, int G, bool KEQV, bool CAP, int CBW>
+__global__ __launch_bounds__((DecodeShape<D, CBW>::kWaves * 64)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_split_kernel(DecodeParams p) {
+  using Sh = DecodeShape<D, CBW>;
   constexpr int kTeam = Sh::kTeam;
   constexpr int kTeams = Sh::kTeams;
-  constexpr int kDW = D / kTeam;     // D slice of one wave's accumulators
+  constexpr int kDW = D / Sh::kSplitD;   // D slice of one wave's accumulators
   constexpr int kDS = D / 32;        // k-steps of QK^T (16x16x32)
   constexpr int kDB = kDW / 16;      // 16-row blocks of this wave's O^T
   constexpr int kRowChunks = D / 8;  // 16-byte chunks per cache row
@@ -275,28 +334,44 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(kTK * kRowChunks % (64 * kTeam) == 0, "tile must split into whole 1 KB ops");
 
   // Ring of slots per team, one LDS array per slot (so reads of one slot are
-  // not ordered behind the copies landing in the others).  Two slots: one
-  // tile in flight while one is computed.  A third slot at head width 512
-  // (48 KB) leaves room for three workgroups per CU instead of four, which
-  // measured slower (3.9 against 4.6 TB/s on the global layer).
-  constexpr int kSlots = 2;
-  __shared__ __attribute__((aligned(16))) uint16_t ks0[kTeams * kSlotElems];
-  __shared__ __attribute__((aligned(16))) uint16_t ks1[kTeams * kSlotElems];
-  __shared__ __attribute__((aligned(16))) uint16_t ks2[kSlots > 2 ? kTeams * kSlotElems : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t vs0[KEQV ? 8 : kTeams * kSlotElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vs1[KEQV ? 8 : kTeams * kSlotElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vs2[(KEQV || kSlots < 3) ? 8 : kTeams * kSlotElems];
+  // not ordered behind the copies landing in the others).  One column block:
+  // two slots, one tile in flight while one is computed (a third slot at
+  // head width 512, 48 KB, leaves room for three workgroups per CU instead of
+  // four, which measured slower: 3.9 against 4.6 TB/s on the global layer).
+  // Several column blocks: one or two workgroups fill a CU (two waves per
+  // SIMD), so the ring deepens to keep as many tiles in flight per CU.
+  constexpr int kSlotBytes = kSlotElems * 2 * (KEQV ? 1 : 2);
+  constexpr int kWgPerCu = 8 / Sh::kWaves;
+  constexpr int kSlotsFit = (160 * 1024) / (kWgPerCu * kTeams * kSlotBytes);
+  constexpr int kSlots = CBW == 1 ? 2 : (kSlotsFit < 6 ? kSlotsFit : 6);
+  static_assert(kSlots >= 2 && kSlots <= 6, "ring depth");
+  constexpr int kKE = kTeams * kSlotElems;
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[kKE];
+  __shared__ __attribute__((aligned(16))) uint16_t ks1[kKE];
+  __shared__ __attribute__((aligned(16))) uint16_t ks2[kSlots > 2 ? kKE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t ks3[kSlots > 3 ? kKE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t ks4[kSlots > 4 ? kKE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t ks5[kSlots > 5 ? kKE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[KEQV ? 8 : kKE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs1[KEQV ? 8 : kKE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs2[(KEQV || kSlots < 3) ? 8 : kKE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs3[(KEQV || kSlots < 4) ? 8 : kKE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs4[(KEQV || kSlots < 5) ? 8 : kKE];
+  __shared__ __attribute__((aligned(16))) uint16_t vs5[(KEQV || kSlots < 6) ? 8 : kKE];
   __shared__ float m_w[2][16];
   __shared__ float l_w[2][16];
   static_assert(kTeams == 1 || kSlotElems * kTeams * 2 >= 16 * D * 4, "merge buffer reuses slot 0");
 
-  const int32_t kvh = static_cast<int32_t>(blockIdx.x) / p.n_cb;
-  const int32_t cb = static_cast<int32_t>(blockIdx.x) % p.n_cb;   // 16-column block
+  const DecodeBlock blk = decode_block(p);
+  if (!blk.valid) return;                                        // padding block (uniform)
+  const int32_t kvh = blk.kvh;
   const int32_t tid = threadIdx.x;
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t team = wave / kTeam;
-  const int32_t member = wave % kTeam;
-  const int32_t dlo = member * kDW;
+  const int32_t member = wave % kTeam;                           // copy share within the team
+  const int32_t dmem = wave % Sh::kSplitD;                       // D slice within the column block
+  const int32_t cb = blk.cb * CBW + (CBW == 1 ? 0 : wave / Sh::kSplitD);   // 16-column block
+  const int32_t dlo = dmem * kDW;
   const int32_t lane = tid & 63;
   const int32_t col = lane & 15;     // column of the block: (token, head) = divmod(cb*16 + col, g)
   const int32_t grp = lane >> 4;     // 16-lane group
@@ -308,7 +383,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // Each sequence segment of this workgroup's key range: [s_lo, s_hi) of
   // sequence b, whose context is ctx.
-  for_each_segment(p, [&](int32_t b, int32_t s_lo, int32_t s_hi, int32_t ctx) __attribute__((always_inline)) {
+  for_each_segment(p, blk.w, [&](int32_t b, int32_t s_lo, int32_t s_hi, int32_t ctx) __attribute__((always_inline)) {
   const int32_t n_t = (s_hi - s_lo + kTK - 1) / kTK;
   // Keys this column may see: [key_lo, key_hi] (its own position and the window).
   const int32_t key_hi = col_ok ? ctx - p.q_len + tok : -1;
@@ -362,15 +437,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto compute = [&](int32_t ti, const uint16_t* kb, const uint16_t* vb) __attribute__((always_inline)) {
     const int32_t k0 = s_lo + ti * kTK;
     // S^T[16 keys x 16 heads] = K . Q^T; lane: key row li16, d chunk ds*4 + lgrp.
+    // The chunk's bits (ds, lgrp, swizzle) sit in byte-address bits 4-9, clear
+    // of the row bits, and ds*4 + lgrp = (ds << 2) ^ lgrp, so step ds reads at
+    // one XOR of the lane's base: kaddr ^ (ds << 6).
     f32x4 sacc = f32x4{};
     const int32_t ln = lane_here();
     const int32_t li16 = ln & 15;
     const int32_t lgrp = ln >> 4;
-    const int32_t sw = dswz<D>(li16);
+    const uint32_t kaddr = static_cast<uint32_t>(li16 * D * 2 + ((lgrp ^ dswz<D>(li16)) << 4));
+    const char* kbc = reinterpret_cast<const char*>(kb);
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds) {
-      const int32_t lc = ds * 4 + lgrp;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[li16 * D + ((lc ^ sw) << 3)]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>(ds << 6)));
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ds], sacc, 0, 0, 0);
     }
     // Lane holds keys k0 + grp*4 + r for head `col`.
@@ -398,7 +476,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       l_run *= alpha;
-#pragma unroll
       for (int db = 0; db < kDB; ++db) o[db] *= alpha;
     }
     m_run = m_next;
@@ -407,18 +484,20 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
     l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk0), ones, l_run, false);
     l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk1), ones, l_run, false);
-    // P^T operand: slots 0-3 = keys grp*4 + [0,4), slots 4-7 empty.
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk0, pk1, 0u, 0u});
-    // V^T operand (transpose read of rows grp*4 + [0,4) at d = dlo + db*16 + li16).
+    // O^T += V^T . P^T with the 16-deep product (16 keys per tile).  P^T
+    // operand: lane group grp holds keys grp*4 + [0,4).  V^T operand: the
+    // transpose read of rows grp*4 + [0,4) at d = dlo + db*16 + li16.  The
+    // chunk (dlo/8 + 2*db + (li16&3)/2) ^ swizzle again has its db bits clear
+    // of the rest, so block db reads at vaddr ^ (db << 5).
+    const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{pk0, pk1});
     const int32_t r0 = lgrp * 4 + (li16 >> 2);
-    const int32_t sw0 = dswz<D>(r0);
-    const int32_t half8 = (li16 & 1) * 4;
+    const uint32_t vaddr = static_cast<uint32_t>(r0 * D * 2 + ((((dlo >> 3) + ((li16 & 3) >> 1)) ^ dswz<D>(r0)) << 4) +
+                                                 (li16 & 1) * 8);
+    const char* vbc = reinterpret_cast<const char*>(vb);
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
-      const int32_t lc = (dlo >> 3) + db * 2 + ((li16 & 3) >> 1);
-      const i16x4 a0 = lds_read_tr16(&vb[r0 * D + ((lc ^ sw0) << 3) + half8]);
-      const bf16x8 aop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, i16x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pb, o[db], 0, 0, 0);
+      const i16x4 a0 = lds_read_tr16(vbc + (vaddr ^ static_cast<uint32_t>(db << 5)));
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, pb, o[db], 0, 0, 0);
     }
   };
 
@@ -427,35 +506,41 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int i = decltype(I)::value;
     if constexpr (i == 0) return ks0 + team * kSlotElems;
     else if constexpr (i == 1) return ks1 + team * kSlotElems;
-    else return ks2 + team * kSlotElems;
+    else if constexpr (i == 2) return ks2 + team * kSlotElems;
+    else if constexpr (i == 3) return ks3 + team * kSlotElems;
+    else if constexpr (i == 4) return ks4 + team * kSlotElems;
+    else return ks5 + team * kSlotElems;
   };
   auto vslot = [&](auto I) -> uint16_t* {
     constexpr int i = decltype(I)::value;
     if constexpr (KEQV) return kslot(I);
     else if constexpr (i == 0) return vs0 + team * kSlotElems;
     else if constexpr (i == 1) return vs1 + team * kSlotElems;
-    else return vs2 + team * kSlotElems;
+    else if constexpr (i == 2) return vs2 + team * kSlotElems;
+    else if constexpr (i == 3) return vs3 + team * kSlotElems;
+    else if constexpr (i == 4) return vs4 + team * kSlotElems;
+    else return vs5 + team * kSlotElems;
   };
-  // A team of two shares its slots: a barrier publishes both halves of a
-  // tile and fences the slot being refilled (every wave runs the same trips).
+  // A team of several waves shares its slots: a barrier publishes every
+  // wave's part of a tile and fences the slot being refilled (every wave
+  // runs the same trips).
   auto team_sync = [&]() {
     if constexpr (kTeam > 1) __syncthreads();
   };
   // The team's tiles are ti = team, team + kTeams, ...; tile k of the team
-  // sits in slot k % kSlots.  Waiting for the oldest tile leaves a newer
-  // tile's copies (kOpsPerTile per wave) outstanding.
+  // sits in slot k % kSlots, and up to kSlots - 1 tiles are copied ahead.
+  // Before computing a tile, its copies must have landed; the newer tiles'
+  // copies (kOpsPerTile per wave each) may stay in flight.
   int32_t ti = team;
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  if (ti < n_t) copy_tile(ti, kslot(S0{}), vslot(S0{}));
-  if constexpr (kSlots > 2) {
-    if (ti + kTeams < n_t) copy_tile(ti + kTeams, kslot(S1{}), vslot(S1{}));
-  }
+  static_for([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    if (ti + i * kTeams < n_t) copy_tile(ti + i * kTeams, kslot(I), vslot(I));
+  }, std::make_integer_sequence<int, kSlots - 1>{});
   auto step = [&](auto I) __attribute__((always_inline)) -> bool {
     constexpr int kCur = decltype(I)::value;
     using Next = std::integral_constant<int, (kCur + kSlots - 1) % kSlots>;
-    if (kSlots > 2 && ti + kTeams < n_t) wait_vmcnt<(kSlots > 2 ? kOpsPerTile : 0)>();
-    else wait_vmcnt<0>();
+    const int32_t after = (n_t - 1 - ti) / kTeams;          // team tiles issued after this one, capped below
+    wait_tiles<kSlots - 2, kOpsPerTile>(after < kSlots - 2 ? after : kSlots - 2);
     team_sync();
     const int32_t ta = ti + (kSlots - 1) * kTeams;
     if (ta < n_t) copy_tile(ta, kslot(Next{}), vslot(Next{}));
@@ -464,11 +549,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return ti < n_t;
   };
   while (ti < n_t) {
-    if (!step(S0{})) break;
-    if (!step(S1{})) break;
-    if constexpr (kSlots > 2) {
-      if (!step(std::integral_constant<int, 2>{})) break;
-    }
+    if (!static_all(step, std::make_integer_sequence<int, kSlots>{})) break;
   }
   (void)kOpsPerTile;
 
@@ -476,8 +557,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   l_run += __shfl_xor(l_run, 32, 64);
   // Partial of (sequence b, token tok, head): row ((b*q_len + tok)*Hq + head).
   // Partial of (sequence b, token tok, head) from workgroup w: slot w + b.
-  const int64_t part = ((static_cast<int64_t>(blockIdx.y) + b) * p.q_len + tok) * p.hq + head;
-  write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, member, dlo, grp, col,
+  const int64_t part = ((static_cast<int64_t>(blk.w) + b) * p.q_len + tok) * p.hq + head;
+  write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, dmem, dlo, grp, col,
                                 reinterpret_cast<float*>(ks0), m_w, l_w);
   __syncthreads();   // LDS slots (and the merge buffer) are reused by the next segment
   });
@@ -507,7 +588,7 @@ __device__ __forceinline__ int32_t qswz(int32_t r) {
 
 template <int D, int G, bool KEQV, bool CAP>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_i8_kernel(DecodeParams p) {
-  using Sh = DecodeShape<D>;
+  using Sh = DecodeShape<D, 1>;
   constexpr int kTeam = Sh::kTeam;
   constexpr int kTeams = Sh::kTeams;
   constexpr int kDW = D / kTeam;     // D slice of one wave's accumulators
@@ -548,8 +629,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Partial scores of a two-wave team: [member][half][lane].
   __shared__ f32x4 sx[kTeam > 1 ? 2 * 2 * 64 : 1];
 
-  const int32_t kvh = static_cast<int32_t>(blockIdx.x) / p.n_cb;
-  const int32_t cb = static_cast<int32_t>(blockIdx.x) % p.n_cb;   // 16-column block
+  const DecodeBlock blk = decode_block(p);
+  if (!blk.valid) return;                                        // padding block (uniform)
+  const int32_t kvh = blk.kvh;
+  const int32_t cb = blk.cb;                                     // 16-column block
   const int32_t tid = threadIdx.x;
   const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t team = wave / kTeam;
@@ -566,7 +649,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // Each sequence segment of this workgroup's key range: [s_lo, s_hi) of
   // sequence b, whose context is ctx.
-  for_each_segment(p, [&](int32_t b, int32_t s_lo, int32_t s_hi, int32_t ctx) __attribute__((always_inline)) {
+  for_each_segment(p, blk.w, [&](int32_t b, int32_t s_lo, int32_t s_hi, int32_t ctx) __attribute__((always_inline)) {
   const int32_t n_t = (s_hi - s_lo + kTK8 - 1) / kTK8;
   // Keys this column may see: [key_lo, key_hi] (its own position and the window).
   const int32_t key_hi = col_ok ? ctx - p.q_len + tok : -1;
@@ -694,7 +777,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       l_run *= alpha;
-#pragma unroll
       for (int db = 0; db < kDB; ++db) o[db] *= alpha;
     }
     m_run = m_next;
@@ -796,7 +878,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   // Partial of (sequence b, token tok, head) from workgroup w: slot w + b.
-  const int64_t part = ((static_cast<int64_t>(blockIdx.y) + b) * p.q_len + tok) * p.hq + head;
+  const int64_t part = ((static_cast<int64_t>(blk.w) + b) * p.q_len + tok) * p.hq + head;
   write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, member, dlo, grp, col,
                                 reinterpret_cast<float*>(ks0), m_w, l_w);
   __syncthreads();   // LDS slots (and the merge buffer) are reused by the next segment
@@ -871,13 +953,27 @@ hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t st
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
-  // rows (KV head, column block) fastest: the KV heads of one cache row are
-  // adjacent in memory and their workgroups run side by side
-  const dim3 grid(static_cast<uint32_t>(a.hkv * prm.n_cb), static_cast<uint32_t>(a.n_wg), 1u);
+  // Three or more 16-column blocks per KV head (many query heads per KV
+  // head times several tokens): four blocks per workgroup share one stream
+  // of cache tiles (bf16 caches, head width 256 or 512).
+  constexpr int kCBW = 4;
+  const bool wide = !prm.ks && D >= 256 && prm.n_cb >= 3;
+  DecodeParams pp = prm;
+  if (wide) pp.n_cb = (prm.n_cb + kCBW - 1) / kCBW;
+  const int64_t nblocks = decode_grid(a.hkv, a.n_wg, pp.n_cb);
+  if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(nblocks), 1u, 1u);
   if (prm.ks) {
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D>::kWaves * 64), 0, stream, prm);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D, 1>::kWaves * 64), 0, stream,
+                       pp);
+  } else if (wide) {
+    if constexpr (D >= 256) {
+      hipLaunchKernelGGL((decode_split_kernel<D, G, KEQV, CAP, kCBW>), grid, dim3(DecodeShape<D, kCBW>::kWaves * 64), 0,
+                         stream, pp);
+    }
   } else {
-    hipLaunchKernelGGL((decode_split_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D>::kWaves * 64), 0, stream, prm);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, KEQV, CAP, 1>), grid, dim3(DecodeShape<D, 1>::kWaves * 64), 0, stream,
+                       pp);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -97,7 +97,7 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
   const long long at_most = (line_max + 255) / 256;        // at least 256 keys per workgroup
   if (n < at_least) n = at_least;
   if (n > at_most) n = at_most;
-  if (n > 65535) n = 65535;   // grid y
+  if (n > 65535) n = 65535;   // bounds the partial slots of the workspace
   if (n < 1) n = 1;
   p.n_wg = static_cast<int32_t>(n);
   // Short spans (local windows) with enough sequences to fill the round: one
