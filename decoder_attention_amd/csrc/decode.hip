@@ -568,11 +568,17 @@ void decode_split_kernel(DecodeParams p) {
 // int8 cache: codes [B, max_ctx, Hkv, D] int8 with one fp32 scale per (token,
 // KV head), scales laid out [B, Hkv, max_ctx] so a tile's scales are one
 // contiguous run.  Tiles hold 32 keys (the bytes of a 16-row bf16 tile).  The
-// codes convert to bf16 exactly in registers; the key scale multiplies the
-// score and the value scale folds into the probability before its bf16
-// rounding, so both products stay bf16 MFMA:
+// key scale multiplies the score and the value scale folds into the
+// probability, so both products run on the matrix cores:
 //   s_j = ks_j * (q . c_j),   o = sum_j (p_j * vs_j) c'_j,   l = sum_j p_j.
-// Value columns reach the PV operand with ds_read_b64_tr_b8.
+// The products are fp16: a code c enters as the exact fp16 value 1152 + c
+// (one XOR and one byte permute per two codes; bf16 needs a normalising
+// conversion per code), so each product carries 1152 times the sum of its
+// other operand, which is subtracted per column -- 1152 * sum(q') from the
+// scores (q' = q * 2^-e, scaled so every bf16 q converts to fp16 exactly) and
+// 1152 * sum(p * vs) from the outputs, summed over the same fp16-rounded
+// weights the product used.  Value columns reach the PV operand with
+// ds_read_b64_tr_b8.
 constexpr int kTK8 = 32;    // keys per int8 tile
 
 // XOR pattern of the 16-byte chunks of int8 LDS row r in [0, 32).  A 16-lane
@@ -656,16 +662,53 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int32_t key_lo = p.window > 0 ? key_hi - p.window + 1 : 0;
   // Q^T operand: step ds, MFMA m: lane holds d = (ds*4 + grp)*16 + m*8 + [0, 8),
   // the d range of the key chunk (ds*4 + grp) that the K operand lane reads;
-  // this wave's steps are ds = member*kDSW + [0, kDSW).
-  bf16x8 qf[kDSW][2];
+  // this wave's steps are ds = member*kDSW + [0, kDSW).  The products run in
+  // fp16 against offset-fp16 codes: q is scaled by 2^-e (e from the largest
+  // |q| of this wave's share of the column, so the scaled values stay below 2
+  // and every bf16 value converts exactly), and the offset term 1152 * sum(q')
+  // comes off each score before it is scaled back by 2^e.
+  f16x8 qh[kDSW][2];
+  float q_unscale, q_off;
   {
     const uint16_t* qrow = p.q + ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * D + grp * 16;
+    u32x4 qr[kDSW][2];
+    float qmax = 0.f;
 #pragma unroll
     for (int i = 0; i < kDSW; ++i) {
       const int ds = member * kDSW + i;
-      qf[i][0] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 64) : bf16x8{};
-      qf[i][1] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 64 + 8) : bf16x8{};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        qr[i][m] = col_ok ? *reinterpret_cast<const u32x4*>(qrow + ds * 64 + m * 8) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qmax = fmaxf(qmax, fmaxf(fabsf(lo_bf16(qr[i][m][e])), fabsf(hi_bf16(qr[i][m][e]))));
+      }
     }
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+    const int32_t qe = qmax > 0.f ? __builtin_amdgcn_frexp_expf(qmax) : 0;
+    const float qin = __builtin_ldexpf(1.f, -qe);
+    q_unscale = __builtin_ldexpf(1.f, qe);
+    float qsum = 0.f;
+    const f16x2 ones_h = f16x2{static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+#pragma unroll
+    for (int i = 0; i < kDSW; ++i) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        u32x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // (pack into a scalar first: the dot of a just-inserted vector
+          // element, bit-cast, was compiled as the dot of element 0)
+          const uint32_t w = pack_f16x2(lo_bf16(qr[i][m][e]) * qin, hi_bf16(qr[i][m][e]) * qin);
+          qsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones_h, qsum, false);
+          h[e] = w;
+        }
+        qh[i][m] = __builtin_bit_cast(f16x8, h);
+      }
+    }
+    qsum += __shfl_xor(qsum, 16, 64);
+    qsum += __shfl_xor(qsum, 32, 64);
+    q_off = kI8Offset * qsum;
   }
 
   f32x4 o[kDB];
@@ -673,6 +716,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int db = 0; db < kDB; ++db) o[db] = f32x4{};
   float m_run = -INFINITY;
   float l_run = 0.f;
+  float lp_run = 0.f;   // sum of the fp16 value-product weights p * vs (offset term of O)
 
   const uint32_t row_pitch = static_cast<uint32_t>(p.hkv) * D;     // bytes between cache rows
   const int64_t seq_off = (static_cast<int64_t>(b) * p.max_ctx * p.hkv + kvh) * D;
@@ -733,9 +777,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < kDSW; ++i) {
         const int32_t c = (member * kDSW + i) * 4 + lgrp;
         const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + row * D + ((c ^ sw) << 4));
-        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(raw[0], raw[1]), qf[i][0], sacc[h2], 0, 0, 0);
-        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16x8(raw[2], raw[3]), qf[i][1], sacc[h2], 0, 0, 0);
+        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i8x8_to_f16x8_off(raw[0], raw[1]), qh[i][0], sacc[h2], 0, 0, 0);
+        sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(i8x8_to_f16x8_off(raw[2], raw[3]), qh[i][1], sacc[h2], 0, 0, 0);
       }
+      sacc[h2] = (sacc[h2] - q_off) * q_unscale;   // this wave's share of q . c
     }
     if constexpr (kTeam > 1) {
       // Add the partner's half of D.  Both members form p0 + p1 (fp32 addition
@@ -777,21 +822,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       l_run *= alpha;
+      lp_run *= alpha;
       for (int db = 0; db < kDB; ++db) o[db] *= alpha;
     }
     m_run = m_next;
     float pe[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
-    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pack_bf16x2(pe[e], pe[e + 1])), ones, l_run, false);
+    for (int e = 0; e < 8; ++e) {
+      pe[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+      l_run += pe[e];
     }
-    // P^T operand: slot e = key (e/4)*16 + grp*4 + e%4, scaled by its value scale.
-    const bf16x8 pb = __builtin_bit_cast(
-        bf16x8, u32x4{pack_bf16x2(pe[0] * vsa[0], pe[1] * vsa[1]), pack_bf16x2(pe[2] * vsa[2], pe[3] * vsa[3]),
-                      pack_bf16x2(pe[4] * vsb[0], pe[5] * vsb[1]), pack_bf16x2(pe[6] * vsb[2], pe[7] * vsb[3])});
+    // P^T operand (fp16): slot e = key (e/4)*16 + grp*4 + e%4, scaled by its
+    // value scale; lp_run sums the same rounded weights for the offset term.
+    const uint32_t pw0 = pack_f16x2(pe[0] * vsa[0], pe[1] * vsa[1]);
+    const uint32_t pw1 = pack_f16x2(pe[2] * vsa[2], pe[3] * vsa[3]);
+    const uint32_t pw2 = pack_f16x2(pe[4] * vsb[0], pe[5] * vsb[1]);
+    const uint32_t pw3 = pack_f16x2(pe[6] * vsb[2], pe[7] * vsb[3]);
+    const f16x2 ones_h = f16x2{static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+    lp_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw0), ones_h, lp_run, false);
+    lp_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw1), ones_h, lp_run, false);
+    lp_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw2), ones_h, lp_run, false);
+    lp_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw3), ones_h, lp_run, false);
+    const f16x8 pb = __builtin_bit_cast(f16x8, u32x4{pw0, pw1, pw2, pw3});
     // V^T operand: lane j of group lgrp addresses key row of slot j/2 at
     // columns d0 + 8*(j%2); the transpose read hands lane i the 8 keys at d0 + i.
     const int32_t e2 = li16 >> 1;
@@ -802,8 +854,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int db = 0; db < kDB; ++db) {
       const int32_t c = (dlo >> 4) + db;
       const v2i32 raw = lds_read_tr8(vbase + ((c ^ vsw) << 4));
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          i8x8_to_bf16x8(static_cast<uint32_t>(raw[0]), static_cast<uint32_t>(raw[1])), pb, o[db], 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          i8x8_to_f16x8_off(static_cast<uint32_t>(raw[0]), static_cast<uint32_t>(raw[1])), pb, o[db], 0, 0, 0);
     }
   };
 
@@ -877,6 +929,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
+  // The value codes entered the products as 1152 + c: remove 1152 * sum(p * vs).
+  lp_run += __shfl_xor(lp_run, 16, 64);
+  lp_run += __shfl_xor(lp_run, 32, 64);
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) o[db] -= kI8Offset * lp_run;
   // Partial of (sequence b, token tok, head) from workgroup w: slot w + b.
   const int64_t part = ((static_cast<int64_t>(blk.w) + b) * p.q_len + tok) * p.hq + head;
   write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, member, dlo, grp, col,

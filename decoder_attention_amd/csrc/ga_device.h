@@ -79,6 +79,28 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
                                           i8pair_to_bf16x2<2>(w1)});
 }
 
+// int8 codes as offset fp16.  Flipping a code's sign bit gives u = c + 128
+// in [0, 255]; the fp16 bit pattern 0x64 : u is 1024 + u = 1152 + c exactly
+// (exponent 2^10, u in the low mantissa bits), so one byte permute per two
+// codes converts them (a product against these values carries an extra
+// 1152 * sum of the other operand, which the caller removes).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+constexpr float kI8Offset = 1152.f;
+__device__ __forceinline__ uint32_t i8pair_to_f16x2_off(uint32_t flipped, uint32_t sel) {
+  return __builtin_amdgcn_perm(0x64646464u, flipped, sel);
+}
+// Eight codes (w0 bytes 0-3, w1 bytes 0-3) as eight offset fp16 values.
+__device__ __forceinline__ f16x8 i8x8_to_f16x8_off(uint32_t w0, uint32_t w1) {
+  const uint32_t a = w0 ^ 0x80808080u, b = w1 ^ 0x80808080u;
+  return __builtin_bit_cast(f16x8, u32x4{i8pair_to_f16x2_off(a, 0x04010400u), i8pair_to_f16x2_off(a, 0x04030402u),
+                                         i8pair_to_f16x2_off(b, 0x04010400u), i8pair_to_f16x2_off(b, 0x04030402u)});
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2));
+}
+
 __device__ __forceinline__ float wave_max_xor32(float v) {
   return fmaxf(v, __shfl_xor(v, 32, 64));
 }

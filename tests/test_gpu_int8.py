@@ -142,6 +142,47 @@ def test_decode_int8_exact_cache_matches_bf16_decode(gpu, kw, layer):
     assert_close(from_dev_f64(o8), from_dev_f64(o16), max_abs=1e-2, mean_abs=1e-3, what="int8 vs bf16")
 
 
+@pytest.mark.parametrize("kw,layer", [(GEMMA2, 0), (GEMMA4, 0), (GEMMA3, 0), (TINY, 0)])
+def test_decode_int8_uniform_values_are_exact(gpu, kw, layer):
+    """The output is a convex combination of value rows, so whatever the scores:
+    value codes all equal to c with unit scales give c, and one value row
+    repeated over every key gives that row.  The kernel's value product carries
+    1152 * sum(p * vs), removed after the product; the product and the separate
+    sum round differently in fp32, which leaves at most a few 1152 * 2^-24 of
+    the value scale (1 here): within 2^-10, and nonzero codes round back to the
+    exact bf16 integer.  A wrong offset term misses by hundreds."""
+    ga = gpu
+    import torch
+
+    cfg = R.GemmaAttnConfig(**kw)
+    L = R.resolve_layer(cfg, layer)
+    B, Smax = 3, 300
+    D, Hkv, Hq = L["head_dim"], L["num_kv_heads"], cfg.num_heads
+    rng = np.random.default_rng(3450)
+    kc = to_dev(rng.integers(-127, 128, size=(B, Smax, Hkv, D)).astype(np.int8))
+    ks = to_dev(np.full((B, Hkv, Smax), 0.02, dtype=np.float32))
+    vs = to_dev(np.ones((B, Hkv, Smax), dtype=np.float32))
+    q = to_dev_bf16(normal_bf16(3451, (B, 1, Hq, D), scale=3.0))
+    for ctx_list in ([300, 1, 33], [2, 17, 299]):
+        ctx = to_dev(np.array(ctx_list, dtype=np.int32))
+        for c in (0, 1, -7, 127, -127):
+            vc = to_dev(np.full((B, Smax, Hkv, D), c, dtype=np.int8))
+            o = ga.attn_decode_int8(kw, layer, q, kc, ks, vc, vs, ctx)
+            torch.cuda.synchronize()
+            got = from_dev_f64(o)
+            assert np.all(np.abs(got - c) <= 2.0 ** -10), (ctx_list, c, np.max(np.abs(got - c)))
+            if c != 0:
+                assert np.all(got == c), (ctx_list, c)
+        row = rng.integers(-127, 128, size=(Hkv, D)).astype(np.int8)
+        vc = to_dev(np.ascontiguousarray(np.broadcast_to(row, (B, Smax, Hkv, D))))
+        o = from_dev_f64(ga.attn_decode_int8(kw, layer, q, kc, ks, vc, vs, ctx))
+        torch.cuda.synchronize()
+        for h in range(Hq):
+            want = row[h // L["group"]].astype(np.float64)
+            assert np.all(np.abs(o[:, :, h] - want) <= 2.0 ** -10), (ctx_list, h)
+            assert np.all((o[:, :, h] == want) | (want == 0)), (ctx_list, h)
+
+
 PRO8 = [("gemma2_local", GEMMA2, 0), ("gemma3_global", GEMMA3, 5), ("gemma4_local", GEMMA4, 0),
         ("gemma4_global_keqv", GEMMA4, 5)]
 
