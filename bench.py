@@ -333,7 +333,7 @@ def bench_decode(ga, reps=20):
     tot_ms = 5 * res["local_w1024"]["decode_ms"] + res["global_keqv"]["decode_ms"]
     res["stack_5local_1global"] = dict(ms=round(tot_ms, 4), gbs=round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1))
     res["roofline"] = dict(bound="hbm", achieved=res["global_keqv"]["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                           frac=res["global_keqv"]["frac"], traffic=None, kernel="decode_split_kernel<512,16,true,false>")
+                           frac=res["global_keqv"]["frac"], traffic=None, kernel="decode_split_kernel<512,16,true,false,1>")
     return res
 
 
