@@ -51,6 +51,13 @@ GEMMA4_12B = dict(num_heads=16, num_kv_heads=8, num_global_kv_heads=1, head_dim=
                   sliding_window=1024, sliding_window_pattern=6, rope_theta=1e6, rope_local_theta=1e4,
                   partial_rotary_factor=0.25, k_eq_v=True, norm_weight_offset=0)
 
+# Prefill workloads: name -> (seed family, config, timed layers, batch, sequence length, QK-norm).
+PREFILL_WORKLOADS = {
+    "gemma2_pair": (2, GEMMA2_PAIR, (0, 1), 2, 8192, False),
+    "gemma3_stack": (3, GEMMA3_STACK, (0, 5), 4, 16384, True),
+    "gemma4_global": (4, GEMMA4_12B, (5,), 1, 32768, True),
+}
+
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
@@ -89,23 +96,34 @@ def _dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def _layer_tensors(cfg_id, kw, layer, B, S, with_norm):
+def layer_inputs(cfg_id, kw, layer, B, S, with_norm):
+    """Host inputs of one prefill layer of a benchmark workload: raw bf16 bits
+    of q [B,S,Hq,D], k and v [B,S,Hkv,D] (v None with keys-as-values), and the
+    fp32 QK-norm weights [D] (None without QK-norm)."""
     import decoder_attention_amd as ga
     from synth import normal_bf16, norm_weight, seed_for
 
     L = ga.resolve_layer(kw, layer)
     D, Hkv, Hq = L["head_dim"], L["num_kv_heads"], kw["num_heads"]
-    t = dict(L=L)
-    t["q"] = _dev_bf16(normal_bf16(seed_for(cfg_id, layer, "q"), (B, S, Hq, D)))
-    t["k"] = _dev_bf16(normal_bf16(seed_for(cfg_id, layer, "k"), (B, S, Hkv, D)))
-    t["v"] = None if L["k_eq_v"] else _dev_bf16(normal_bf16(seed_for(cfg_id, layer, "v"), (B, S, Hkv, D)))
-    if with_norm:
-        import torch
+    h = dict(L=L)
+    h["q"] = normal_bf16(seed_for(cfg_id, layer, "q"), (B, S, Hq, D))
+    h["k"] = normal_bf16(seed_for(cfg_id, layer, "k"), (B, S, Hkv, D))
+    h["v"] = None if L["k_eq_v"] else normal_bf16(seed_for(cfg_id, layer, "v"), (B, S, Hkv, D))
+    h["qw"] = norm_weight(seed_for(cfg_id, layer, "q_norm_w"), D) if with_norm else None
+    h["kw"] = norm_weight(seed_for(cfg_id, layer, "k_norm_w"), D) if with_norm else None
+    return h
 
-        t["qw"] = torch.from_numpy(norm_weight(seed_for(cfg_id, layer, "q_norm_w"), D)).cuda()
-        t["kw"] = torch.from_numpy(norm_weight(seed_for(cfg_id, layer, "k_norm_w"), D)).cuda()
-    else:
-        t["qw"] = t["kw"] = None
+
+def _layer_tensors(cfg_id, kw, layer, B, S, with_norm, host=None):
+    """Device tensors of one prefill layer (from ``host``, else freshly drawn)."""
+    import torch
+
+    h = host if host is not None else layer_inputs(cfg_id, kw, layer, B, S, with_norm)
+    t = dict(L=h["L"])
+    for name in ("q", "k", "v"):
+        t[name] = None if h[name] is None else _dev_bf16(h[name])
+    for name in ("qw", "kw"):
+        t[name] = None if h[name] is None else torch.from_numpy(h[name]).cuda()
     t["qt"] = torch_empty_like(t["q"])
     t["kt"] = torch_empty_like(t["k"])
     t["out"] = torch_empty_like(t["q"])
@@ -163,12 +181,12 @@ def _pair_traffic():
 def bench_pair(ga, steps, warmup):
     import torch
 
-    B, S = 2, 8192
-    layers = {layer: _layer_tensors(2, GEMMA2_PAIR, layer, B, S, False) for layer in (0, 1)}
-    flops = {layer: _flops(GEMMA2_PAIR, layer, B, S) for layer in (0, 1)}
+    cfg_id, kw, _, B, S, norm = PREFILL_WORKLOADS["gemma2_pair"]
+    layers = {layer: _layer_tensors(cfg_id, kw, layer, B, S, norm) for layer in (0, 1)}
+    flops = {layer: _flops(kw, layer, B, S) for layer in (0, 1)}
     for _ in range(warmup):
         for layer in (0, 1):
-            run_layer_step(ga, GEMMA2_PAIR, layer, layers[layer])
+            run_layer_step(ga, kw, layer, layers[layer])
     torch.cuda.synchronize()
     timer = Timer()
     t0 = time.perf_counter()
@@ -177,7 +195,7 @@ def bench_pair(ga, steps, warmup):
     start.record()
     for _ in range(steps):
         for layer in (0, 1):
-            run_layer_step(ga, GEMMA2_PAIR, layer, layers[layer], timer, tag=str(layer))
+            run_layer_step(ga, kw, layer, layers[layer], timer, tag=str(layer))
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -201,9 +219,10 @@ def bench_pair(ga, steps, warmup):
     )
 
 
-def bench_prefill_layer(ga, cfg_id, kw, layer, B, S, with_norm, reps=10):
+def bench_prefill_layer(ga, workload, layer, reps=10):
     import torch
 
+    cfg_id, kw, _, B, S, with_norm = PREFILL_WORKLOADS[workload]
     t = _layer_tensors(cfg_id, kw, layer, B, S, with_norm)
     for _ in range(2):
         run_layer_step(ga, kw, layer, t)
@@ -220,44 +239,104 @@ def bench_prefill_layer(ga, cfg_id, kw, layer, B, S, with_norm, reps=10):
                 prologue_ms=round(float(np.median(timer.ms("prologue"))), 4), flops=f)
 
 
+DECODE_B, DECODE_SMAX, DECODE_MULTI = 64, 65536, 4
+
+
+def decode_contexts():
+    """The 64 ragged context lengths of the Gemma-4-12B decode workload."""
+    from synth import ctx_lengths, seed_for
+
+    return ctx_lengths(seed_for(5, 0, "ctx"), DECODE_B, 512, DECODE_SMAX)
+
+
+def decode_span(c, W):
+    """Cache rows [lo, c) that the decode steps of a sequence with context c
+    read: on a local layer the window of the first of the DECODE_MULTI new
+    tokens, on a global layer all c rows."""
+    return (max(0, int(c) - W - (DECODE_MULTI - 1)) if W else 0, int(c))
+
+
+def decode_caches(ga, layer, ctx):
+    """bf16 caches [B, Smax, Hkv, D] of one layer of the decode workload: the
+    rows of each sequence's span drawn from its own seeded stream, every other
+    row NaN.  Returns (k_cache, v_cache or None with keys-as-values)."""
+    import torch
+
+    from synth import BF16_NAN, normal_bf16_row, seed_for
+
+    B, Smax = DECODE_B, DECODE_SMAX
+    L = ga.resolve_layer(GEMMA4_12B, layer)
+    D, Hkv, W = L["head_dim"], L["num_kv_heads"], L["window"]
+    nan = torch.tensor(int(np.int16(BF16_NAN.view(np.int16))), dtype=torch.int16)
+    spans = [decode_span(ctx[b], W) for b in range(B)]
+    caches = []
+    for tensor in (("k",) if L["k_eq_v"] else ("k", "v")):
+        c = torch.full((B, Smax, Hkv, D), nan.item(), dtype=torch.int16, device="cuda")
+        seed = seed_for(5, layer, tensor)
+        with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+            rows = list(ex.map(lambda b: normal_bf16_row(seed, b, (spans[b][1] - spans[b][0], Hkv, D)), range(B)))
+        for b in range(B):
+            c[b, spans[b][0]:spans[b][1]] = torch.from_numpy(rows[b].view(np.int16)).cuda()
+        del rows
+        caches.append(c.view(torch.bfloat16))
+    return caches[0], (None if L["k_eq_v"] else caches[1])
+
+
+def decode_int8_caches(ga, layer, kc, vc, ctx):
+    """The same spans quantized on the device: (codes int8 [B, Smax, Hkv, D],
+    scales fp32 [B, Hkv, Smax]) per cache, zero codes and NaN scales elsewhere."""
+    import torch
+
+    B, Smax = DECODE_B, DECODE_SMAX
+    L = ga.resolve_layer(GEMMA4_12B, layer)
+    D, Hkv, W = L["head_dim"], L["num_kv_heads"], L["window"]
+    res = []
+    for c in ((kc,) if vc is None else (kc, vc)):
+        cc = torch.zeros((B, Smax, Hkv, D), dtype=torch.int8, device="cuda")
+        sc = torch.full((B, Hkv, Smax), float("nan"), dtype=torch.float32, device="cuda")
+        for b in range(B):
+            lo, hi = decode_span(ctx[b], W)
+            p0 = torch.tensor([lo], dtype=torch.int32, device="cuda")
+            ga.kv_quantize_int8(c[b:b + 1, lo:hi], cc[b:b + 1], sc[b:b + 1], pos0=p0)
+        res.append((cc, sc))
+    return res[0], (None, None) if vc is None else res[1]
+
+
+def decode_query(layer, multi=False):
+    """Raw bf16 bits of the decode workload's queries: [B, 1, 16, D] for the
+    one-token step (rotated by the prologue at position ctx - 1), else
+    [B, DECODE_MULTI, 16, D], taken as already processed."""
+    import decoder_attention_amd as ga
+    from synth import normal_bf16, seed_for
+
+    D = ga.resolve_layer(GEMMA4_12B, layer)["head_dim"]
+    if multi:
+        return normal_bf16(seed_for(5, layer, "q") + 7, (DECODE_B, DECODE_MULTI, 16, D))
+    return normal_bf16(seed_for(5, layer, "q"), (DECODE_B, 1, 16, D))
+
+
 def bench_decode(ga, reps=20):
     """Gemma-4-12B decode step: one local and one global layer over 64 ragged contexts."""
     import torch
 
-    from synth import BF16_NAN, ctx_lengths, normal_bf16_row, normal_bf16, seed_for
-
-    B, Smax = 64, 65536
-    ctx = ctx_lengths(seed_for(5, 0, "ctx"), B, 512, 65536)
+    B, Smax = DECODE_B, DECODE_SMAX
+    ctx = decode_contexts()
     ctx_d = torch.from_numpy(ctx).cuda()
-    pos = torch.from_numpy(ctx - 1).cuda()
+    p32 = torch.from_numpy(ctx - 1).to(torch.int32).cuda()
     res = {}
-    nan = torch.tensor(int(np.int16(BF16_NAN.view(np.int16))), dtype=torch.int16)
     for layer, name in ((0, "local_w1024"), (5, "global_keqv")):
         L = ga.resolve_layer(GEMMA4_12B, layer)
         D, Hkv, W = L["head_dim"], L["num_kv_heads"], L["window"]
-        caches = []
-        for tensor in (("k",) if L["k_eq_v"] else ("k", "v")):
-            c = torch.full((B, Smax, Hkv, D), nan.item(), dtype=torch.int16, device="cuda")
-            seed = seed_for(5, layer, tensor)
-            spans = [(max(0, int(ctx[b]) - W) if W else 0, int(ctx[b])) for b in range(B)]
-            with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
-                rows = list(ex.map(lambda b: normal_bf16_row(seed, b, (spans[b][1] - spans[b][0], Hkv, D)), range(B)))
-            for b in range(B):
-                c[b, spans[b][0]:spans[b][1]] = torch.from_numpy(rows[b].view(np.int16)).cuda()
-            del rows
-            caches.append(c.view(torch.bfloat16))
-        kc = caches[0]
-        vc = None if L["k_eq_v"] else caches[1]
-        q = _dev_bf16(normal_bf16(seed_for(5, layer, "q"), (B, 1, 16, D)))
+        kc, vc = decode_caches(ga, layer, ctx)
+        q = _dev_bf16(decode_query(layer))
         qt = torch.empty_like(q)
         out = torch.empty((B, 16, D), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(ga.decode_workspace_size(GEMMA4_12B, layer, B, Smax), dtype=torch.uint8, device="cuda")
         for _ in range(3):
-            ga.qk_prologue(GEMMA4_12B, layer, q, None, q_out=qt, pos0=pos.to(torch.int32))
+            ga.qk_prologue(GEMMA4_12B, layer, q, None, q_out=qt, pos0=p32)
             ga.attn_decode(GEMMA4_12B, layer, qt.view(B, 16, D), kc, vc, ctx_d, out=out, workspace=ws)
         torch.cuda.synchronize()
         timer = Timer()
-        p32 = pos.to(torch.int32)
         for _ in range(reps):
             timer.start("prologue")
             ga.qk_prologue(GEMMA4_12B, layer, q, None, q_out=qt, pos0=p32)
@@ -273,10 +352,10 @@ def bench_decode(ga, reps=20):
                          frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          prologue_ms=round(float(np.median(timer.ms("prologue"))), 4))
 
-        # Several new tokens per sequence (draft verification, 4 tokens): the
-        # same cache rows plus the 3 extra rows the first token's window adds.
-        Lq = 4
-        qm = _dev_bf16(normal_bf16(seed_for(5, layer, "q") + 7, (B, Lq, 16, D)))
+        # Several new tokens per sequence (draft verification): the same cache
+        # rows plus the DECODE_MULTI - 1 extra rows the first token's window adds.
+        Lq = DECODE_MULTI
+        qm = _dev_bf16(decode_query(layer, multi=True))
         outm = torch.empty_like(qm)
         wsm = torch.empty(ga.decode_multi_workspace_size(GEMMA4_12B, layer, B, Lq, Smax), dtype=torch.uint8,
                           device="cuda")
@@ -298,18 +377,7 @@ def bench_decode(ga, reps=20):
 
         # int8 cache: the same rows quantized on the device (codes + one fp32
         # scale per token and head); algorithmic bytes = codes + scales read.
-        codes, scales = [], []
-        for c in caches:
-            cc = torch.zeros((B, Smax, Hkv, D), dtype=torch.int8, device="cuda")
-            sc = torch.full((B, Hkv, Smax), float("nan"), dtype=torch.float32, device="cuda")
-            for b in range(B):
-                lo_b = max(0, int(ctx[b]) - W) if W else 0
-                p0 = torch.tensor([lo_b], dtype=torch.int32, device="cuda")
-                ga.kv_quantize_int8(c[b:b + 1, lo_b:int(ctx[b])], cc[b:b + 1], sc[b:b + 1], pos0=p0)
-            codes.append(cc)
-            scales.append(sc)
-        kq, ksq = codes[0], scales[0]
-        vq, vsq = (None, None) if L["k_eq_v"] else (codes[1], scales[1])
+        (kq, ksq), (vq, vsq) = decode_int8_caches(ga, layer, kc, vc, ctx)
         q1 = qt.view(B, 1, 16, D)
         out1 = out.view(B, 1, 16, D)
         for _ in range(3):
@@ -326,8 +394,7 @@ def bench_decode(ga, reps=20):
         res[name + "_int8"] = dict(decode_ms=round(ms8, 4), kv_bytes=nb8, gbs=round(nb8 / (ms8 * 1e-3) / 1e9, 1),
                                    frac=round(nb8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                    speedup_vs_bf16=round(ms / ms8, 3))
-        del codes, scales, kq, ksq, vq, vsq
-        del caches, kc, vc
+        del kq, ksq, vq, vsq, kc, vc
         torch.cuda.empty_cache()
     tot_bytes = 5 * res["local_w1024"]["kv_bytes"] + res["global_keqv"]["kv_bytes"]
     tot_ms = 5 * res["local_w1024"]["decode_ms"] + res["global_keqv"]["decode_ms"]
@@ -397,9 +464,9 @@ def main():
         out = {}
         if a.workload == "gemma3":
             for layer, name in ((0, "gemma3_1b_local_w512"), (5, "gemma3_1b_global")):
-                out[name] = bench_prefill_layer(ga, 3, GEMMA3_STACK, layer, 4, 16384, True, reps=a.steps)
+                out[name] = bench_prefill_layer(ga, "gemma3_stack", layer, reps=a.steps)
         elif a.workload == "gemma4":
-            out["gemma4_12b_global_keqv_d512"] = bench_prefill_layer(ga, 4, GEMMA4_12B, 5, 1, 32768, True, reps=a.steps)
+            out["gemma4_12b_global_keqv_d512"] = bench_prefill_layer(ga, "gemma4_global", 5, reps=a.steps)
         else:
             out["decode"] = bench_decode(ga, reps=a.steps)
         print(json.dumps({"workload": a.workload, **out}), flush=True)
@@ -442,14 +509,14 @@ def main():
         log("[bench] gemma3 stack / gemma4 global prefill")
         cfgs = {}
         for layer, name in ((0, "gemma3_1b_local_w512"), (5, "gemma3_1b_global")):
-            cfgs[name] = bench_prefill_layer(ga, 3, GEMMA3_STACK, layer, 4, 16384, True)
+            cfgs[name] = bench_prefill_layer(ga, "gemma3_stack", layer)
         s3 = cfgs["gemma3_1b_local_w512"]
         g3 = cfgs["gemma3_1b_global"]
         stack_f = 5 * s3["flops"] + g3["flops"]
         stack_ms = 5 * s3["prefill_ms"] + g3["prefill_ms"]
         cfgs["gemma3_1b_stack_5local_1global"] = dict(prefill_ms=round(stack_ms, 4),
                                                        tflops=round(stack_f / (stack_ms * 1e-3) / 1e12, 2))
-        cfgs["gemma4_12b_global_keqv_d512"] = bench_prefill_layer(ga, 4, GEMMA4_12B, 5, 1, 32768, True, reps=5)
+        cfgs["gemma4_12b_global_keqv_d512"] = bench_prefill_layer(ga, "gemma4_global", 5, reps=5)
         line["prefill_configs"] = cfgs
         log(f"[bench] prefill configs: {json.dumps(cfgs)}")
         log("[bench] gemma4 decode: building caches")

@@ -47,3 +47,18 @@ def assert_close(got: np.ndarray, ref: np.ndarray, max_abs=2e-2, mean_abs=2e-3, 
     mx, mn = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
     assert mx <= max_abs and mn <= mean_abs, f"{what}: max-abs {mx:.3e} (<= {max_abs}), mean-abs {mn:.3e} (<= {mean_abs})"
     return mx, mn
+
+
+def assert_within_one_ulp(got: np.ndarray, ref: np.ndarray, what=""):
+    """Prologue outputs: one bf16 ulp of the exact value, plus the fp32 rounding
+    of the rotation a*cos - b*sin, which is relative to the row's magnitude and
+    shows where the two products nearly cancel; 99% within half an ulp."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    row_scale = np.max(np.abs(ref), axis=-1, keepdims=True)
+    tol = bf16_ulp(ref) + 2.0 ** -20 * row_scale
+    err = np.abs(got - ref)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} beyond tolerance, max err/ulp {np.max(err / bf16_ulp(ref)):.3f}"
+    assert np.mean(err <= bf16_ulp(ref) * 0.5 + 2.0 ** -20 * row_scale) > 0.99, what

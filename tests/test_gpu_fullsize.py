@@ -1,0 +1,200 @@
+"""GPU parity at the benchmark's own sizes and launches, on sampled outputs.
+
+The inputs are the benchmark's seeded tensors (bench.py builds them, the
+same calls launch the kernels), so every launch shape timed there is also
+checked here:
+  * prefill: the Gemma-2-2B-shaped pair (B2 S8192), the Gemma-3-1B-shaped
+    local (window 512) and global layers (B4 S16384, QK-norm 1+w) and the
+    Gemma-4-12B-shaped global layer (B1 S32768, D512, keys as values);
+  * decode: the Gemma-4-12B-shaped step over 64 ragged contexts of up to
+    65536 rows (local layer window 1024, global layer D512), one new token,
+    four new tokens, and the int8 cache.
+The oracle computes the sampled query rows one by one: each row's processed
+query from its raw bits at its own position, all keys of the layer, then the
+row's attention.  Outputs and lse are held to the attention tolerance
+(max-abs 2e-2, mean-abs 2e-3), prologue outputs to one bf16 ulp, int8 codes
+and scales bit for bit.  Decode caches are NaN outside the rows a sequence
+may read, so a stray read shows as a non-finite output anywhere in the batch.
+"""
+import numpy as np
+import pytest
+
+import bench
+from oracle import gemma_ref as R
+from synth import bf16_bits_to_f64, normal_bf16_row, seed_for
+from tests.gpu_util import assert_close, assert_within_one_ulp, from_dev_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+PREFILL = [(f"{name}_layer{layer}", name, layer)
+           for name, (_, _, layers, _, _, _) in bench.PREFILL_WORKLOADS.items() for layer in layers]
+
+
+def _sample_rows(B, S, Hq, W, seed, n_random=8):
+    """(b, head, i) rows: the first positions, tile edges, both sides of the
+    window edge, the last positions, and seeded random ones; heads and
+    sequences cycle so every GQA group member and sequence appears."""
+    rng = np.random.default_rng(seed)
+    pos = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, S // 2, S - 2, S - 1}
+    if W:
+        pos |= {W - 2, W - 1, W, W + 1}
+    pos |= set(int(x) for x in rng.integers(0, S, n_random))
+    pos = sorted(p for p in pos if 0 <= p < S)
+    return [(j % B, int((j * 5 + rng.integers(0, Hq)) % Hq), p) for j, p in enumerate(pos)]
+
+
+@pytest.mark.parametrize("case,workload,layer", PREFILL, ids=[p[0] for p in PREFILL])
+def test_prefill_full_size_sampled(gpu, case, workload, layer):
+    ga = gpu
+    import torch
+
+    cfg_id, kw, _, B, S, norm = bench.PREFILL_WORKLOADS[workload]
+    cfg = R.GemmaAttnConfig(**kw)
+    L = R.resolve_layer(cfg, layer)
+    Hq, W = cfg.num_heads, L["window"]
+    print(f"[fullsize] {case}: B={B} S={S} D={L['head_dim']} window={W}", flush=True)
+    h = bench.layer_inputs(cfg_id, kw, layer, B, S, norm)
+    t = bench._layer_tensors(cfg_id, kw, layer, B, S, norm, host=h)
+    bench.run_layer_step(ga, kw, layer, t)                 # the timed launch: prologue, then prefill
+    out2, lse = ga.attn_prefill(kw, layer, t["qt"], t["kt"], t["v"], want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), t["out"].view(torch.int16)), "lse request changed the output"
+
+    rows = _sample_rows(B, S, Hq, W, seed=cfg_id * 100 + layer)
+    bi = torch.tensor([r[0] for r in rows], device="cuda")
+    hi = torch.tensor([r[1] for r in rows], device="cuda")
+    ii = torch.tensor([r[2] for r in rows], device="cuda")
+    got_q = from_dev_f64(t["qt"][bi, ii, hi])
+    got_o = from_dev_f64(t["out"][bi, ii, hi])
+    got_l = from_dev_f64(lse[bi, hi, ii])
+    got_k = from_dev_f64(t["kt"])
+    del t, out2, lse
+    torch.cuda.empty_cache()
+
+    # oracle: each sampled query row processed alone at its own position
+    ref_q = np.stack([R.prologue(cfg, layer, bf16_bits_to_f64(h["q"][b, i][None, None]), None, h["qw"], None,
+                                 pos0=[i])[0][0, 0, hq] for b, hq, i in rows])
+    # keys: the prologue of the whole key tensor (its norm weight, positions 0..S-1)
+    ref_k = R.prologue(cfg, layer, bf16_bits_to_f64(h["k"]), None, h["kw"], None)[0]
+    assert_within_one_ulp(got_q, ref_q, what=case + " q rows")
+    assert_within_one_ulp(got_k, ref_k, what=case + " k")
+    del got_k
+    v = None if L["k_eq_v"] else bf16_bits_to_f64(h["v"])
+    # the processed q and k cross the library boundary as bf16
+    ro, rl = R.prefill_rows(cfg, layer, R.round_bf16(ref_q), R.round_bf16(ref_k), v, rows)
+    mx, mn = assert_close(got_o, ro, what=case)
+    assert_close(got_l, rl, what=case + " lse")
+    print(f"[fullsize] {case}: {len(rows)} rows, max-abs {mx:.2e} mean-abs {mn:.2e}", flush=True)
+
+
+class _Spans:
+    """Read-only stand-in for a [B', Smax, Hkv, D] cache of which only the
+    rows [lo_b, hi_b) of each sequence exist (the rows the decode step may
+    read); reading any other row fails."""
+
+    def __init__(self, spans, rows):
+        self.spans, self.rows = spans, rows
+
+    def __getitem__(self, idx):
+        b, s, h, d = idx
+        lo, hi = self.spans[b]
+        assert s.step is None and lo <= s.start <= s.stop <= hi, (b, s, (lo, hi))
+        return self.rows[b][s.start - lo:s.stop - lo, h, d]
+
+
+def _decode_oracle_caches(layer, ctx, sel):
+    """The sampled sequences' cache rows, drawn on the host from the same
+    seeded streams that fill the device caches: (spans, bf16 bits per tensor)."""
+    L = R.resolve_layer(R.GemmaAttnConfig(**bench.GEMMA4_12B), layer)
+    Hkv, D, W = L["num_kv_heads"], L["head_dim"], L["window"]
+    spans = [bench.decode_span(ctx[b], W) for b in sel]
+    bits = {}
+    for tensor in (("k",) if L["k_eq_v"] else ("k", "v")):
+        seed = seed_for(5, layer, tensor)
+        bits[tensor] = [normal_bf16_row(seed, int(b), (hi - lo, Hkv, D)) for b, (lo, hi) in zip(sel, spans)]
+    return spans, bits
+
+
+@pytest.mark.parametrize("layer", [0, 5], ids=["local_w1024", "global_keqv_d512"])
+def test_decode_full_size_sampled(gpu, layer):
+    ga = gpu
+    import torch
+
+    kw = bench.GEMMA4_12B
+    cfg = R.GemmaAttnConfig(**kw)
+    L = R.resolve_layer(cfg, layer)
+    B, Smax, D, Lq = bench.DECODE_B, bench.DECODE_SMAX, L["head_dim"], bench.DECODE_MULTI
+    ctx = bench.decode_contexts()
+    rng = np.random.default_rng(50 + layer)
+    sel = sorted({int(np.argmin(ctx)), int(np.argmax(ctx))} | set(int(x) for x in rng.choice(B, 4, replace=False)))
+    print(f"[fullsize] decode layer {layer}: B={B} Smax={Smax} D={D} sampled {sel} ctx {ctx[sel].tolist()}",
+          flush=True)
+
+    # the timed launches, in the timed configuration
+    kc, vc = bench.decode_caches(ga, layer, ctx)
+    ctx_d = torch.from_numpy(ctx).cuda()
+    q_bits = bench.decode_query(layer)
+    q = to_dev(q_bits.view(np.int16)).view(torch.bfloat16)
+    qt = torch.empty_like(q)
+    out = torch.empty((B, 16, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ga.decode_workspace_size(kw, layer, B, Smax), dtype=torch.uint8, device="cuda")
+    ga.qk_prologue(kw, layer, q, None, q_out=qt, pos0=to_dev((ctx - 1).astype(np.int32)))
+    ga.attn_decode(kw, layer, qt.view(B, 16, D), kc, vc, ctx_d, out=out, workspace=ws)
+    out_l, lse = ga.attn_decode(kw, layer, qt.view(B, 16, D), kc, vc, ctx_d, want_lse=True, workspace=ws)
+    qm_bits = bench.decode_query(layer, multi=True)
+    qm = to_dev(qm_bits.view(np.int16)).view(torch.bfloat16)
+    wsm = torch.empty(ga.decode_multi_workspace_size(kw, layer, B, Lq, Smax), dtype=torch.uint8, device="cuda")
+    outm = ga.attn_decode_multi(kw, layer, qm, kc, vc, ctx_d, workspace=wsm)
+    (kq, ksq), (vq, vsq) = bench.decode_int8_caches(ga, layer, kc, vc, ctx)
+    out8 = ga.attn_decode_int8(kw, layer, qt.view(B, 1, 16, D), kq, ksq, vq, vsq, ctx_d, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_l.view(torch.int16), out.view(torch.int16)), "lse request changed the output"
+    for name, o in (("q1", out), ("q4", outm), ("int8", out8)):
+        assert bool(torch.isfinite(o.float()).all()), f"decode {name}: non-finite output (a row outside a span was read)"
+    sel_d = torch.tensor(sel, device="cuda")
+    got = dict(q=from_dev_f64(qt[sel_d]), q1=from_dev_f64(out[sel_d]), lse=from_dev_f64(lse[sel_d]),
+               q4=from_dev_f64(outm[sel_d]), int8=from_dev_f64(out8[sel_d]))
+    spans = [bench.decode_span(ctx[b], L["window"]) for b in sel]
+    got_codes = [([c[b, lo:hi].cpu().numpy() for b, (lo, hi) in zip(sel, spans)],
+                  [np.ascontiguousarray(s[b, :, lo:hi].cpu().numpy().T) for b, (lo, hi) in zip(sel, spans)])
+                 for c, s in ((kq, ksq), (vq, vsq)) if c is not None]
+    del kc, vc, kq, ksq, vq, vsq, out, out_l, outm, out8, ws, wsm
+    torch.cuda.empty_cache()
+
+    assert _decode_oracle_caches(layer, ctx, sel)[0] == spans
+    bits = _decode_oracle_caches(layer, ctx, sel)[1]
+    f64 = {t: [bf16_bits_to_f64(x) for x in xs] for t, xs in bits.items()}
+    kc_o = _Spans(spans, f64["k"])
+    vc_o = None if L["k_eq_v"] else _Spans(spans, f64["v"])
+    ctx_s = ctx[sel]
+
+    # one new token: the prologue rotates q at position ctx - 1
+    rq = R.prologue(cfg, layer, bf16_bits_to_f64(q_bits[sel]), pos0=ctx_s - 1)[0]       # [n,1,16,D]
+    assert_within_one_ulp(got["q"], rq, what=f"decode layer {layer} q")
+    rq = R.round_bf16(rq)
+    ro, rl = R.decode(cfg, layer, rq[:, 0], kc_o, vc_o, ctx_s)
+    mx, mn = assert_close(got["q1"], ro, what=f"decode layer {layer} q1")
+    assert_close(got["lse"], rl, what=f"decode layer {layer} lse")
+    print(f"[fullsize] decode layer {layer} q1: max-abs {mx:.2e} mean-abs {mn:.2e}", flush=True)
+
+    # four new tokens at positions ctx - 4 .. ctx - 1 (queries taken as processed)
+    rm, _ = R.decode_multi(cfg, layer, bf16_bits_to_f64(qm_bits[sel]), kc_o, vc_o, ctx_s)
+    mx, mn = assert_close(got["q4"], rm, what=f"decode layer {layer} q4")
+    print(f"[fullsize] decode layer {layer} q4: max-abs {mx:.2e} mean-abs {mn:.2e}", flush=True)
+
+    # int8 cache: codes and scales bit for bit over each span, then attention
+    # over the oracle's own dequantized codes
+    deq = {}
+    for (codes, scales), t in zip(got_codes, ("k", "v")):
+        deq[t] = []
+        for j, (lo, hi) in enumerate(spans):
+            rc, rs = R.quantize_int8(f64[t][j].astype(np.float32))        # bf16 values are exact in fp32
+            assert np.array_equal(codes[j], rc), f"int8 codes, layer {layer} {t} seq {sel[j]}"
+            assert np.array_equal(scales[j].view(np.uint32), rs.view(np.uint32)), \
+                f"int8 scales, layer {layer} {t} seq {sel[j]}"
+            deq[t].append(R.dequantize_int8(rc, rs))
+    k8 = _Spans(spans, deq["k"])
+    v8 = None if L["k_eq_v"] else _Spans(spans, deq["v"])
+    r8, _ = R.decode_multi(cfg, layer, rq, k8, v8, ctx_s)
+    mx, mn = assert_close(got["int8"], r8, what=f"decode layer {layer} int8")
+    print(f"[fullsize] decode layer {layer} int8: max-abs {mx:.2e} mean-abs {mn:.2e}", flush=True)

@@ -12,7 +12,8 @@ import pytest
 
 from oracle import gemma_ref as R
 from synth import BF16_NAN, bf16_bits_to_f64, ctx_lengths, normal_bf16, norm_weight
-from tests.gpu_util import assert_close, bf16_ulp, from_dev_bf16_bits, from_dev_f64, to_dev, to_dev_bf16
+from tests.gpu_util import (assert_close, assert_within_one_ulp, from_dev_bf16_bits, from_dev_f64, to_dev,
+                            to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -115,16 +116,8 @@ def test_prologue_within_one_ulp(gpu, name, kw, layer, offset, pos0, S):
                             q_norm_w=None if qw is None else to_dev(qw),
                             k_norm_w=None if kw_ is None else to_dev(kw_), pos0=to_dev(p0))
     rq, rk = R.prologue(cfg, layer, bf16_bits_to_f64(q), bf16_bits_to_f64(k), qw, kw_, p0)
-    for got, ref in ((from_dev_f64(qt), rq), (from_dev_f64(kt), rk)):
-        # one bf16 ulp of the exact value, plus the fp32 rounding of the
-        # rotation a*cos - b*sin, which is relative to the row's magnitude and
-        # shows where the two products nearly cancel
-        row_scale = np.max(np.abs(ref), axis=-1, keepdims=True)
-        tol = bf16_ulp(ref) + 2.0 ** -20 * row_scale
-        err = np.abs(got - ref)
-        bad = err > tol
-        assert not bad.any(), f"{name}: {bad.sum()} of {bad.size} beyond tolerance, max err/ulp {np.max(err / bf16_ulp(ref)):.3f}"
-        assert np.mean(err <= bf16_ulp(ref) * 0.5 + 2.0 ** -20 * row_scale) > 0.99
+    assert_within_one_ulp(from_dev_f64(qt), rq, what=name + " q")
+    assert_within_one_ulp(from_dev_f64(kt), rk, what=name + " k")
 
 
 def test_prologue_in_place_and_queries_only(gpu):
