@@ -414,8 +414,8 @@ void decode_split_kernel(DecodeParams p) {
   auto copy_tile = [&](int32_t ti, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
     const int32_t k0 = s_lo + ti * kTK;
     const int32_t last = s_hi - 1 - k0;
-    const char* kb = kseq + static_cast<int64_t>(k0) * row_pitch;
-    const char* vb = vseq + static_cast<int64_t>(k0) * row_pitch;
+    const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kseq + static_cast<int64_t>(k0) * row_pitch, kTK * row_pitch);
+    const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vseq + static_cast<int64_t>(k0) * row_pitch, kTK * row_pitch);
     const int32_t ln = lane_here();
 #pragma unroll
     for (int i = 0; i < kWaveOps; ++i) {
@@ -424,12 +424,8 @@ void decode_split_kernel(DecodeParams p) {
       const int32_t row = pc / kRowChunks;
       const int32_t lc = (pc % kRowChunks) ^ dswz<D>(row);
       const uint32_t off = static_cast<uint32_t>(min(row, last)) * row_pitch + static_cast<uint32_t>(lc) * 16u;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + off),
-                                       (__attribute__((address_space(3))) void*)(kdst + op * 512), 16, 0, kStreamAux);
-      if (!KEQV) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + off),
-                                         (__attribute__((address_space(3))) void*)(vdst + op * 512), 16, 0, kStreamAux);
-      }
+      copy_to_lds<16, kStreamAux>(krs, off, kdst + op * 512);
+      if (!KEQV) copy_to_lds<16, kStreamAux>(vrs, off, vdst + op * 512);
     }
   };
 
@@ -733,8 +729,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto copy_tile = [&](int32_t ti, uint8_t* kdst, uint8_t* vdst, float* kscd, float* vscd) __attribute__((always_inline)) {
     const int32_t k0 = s_lo + ti * kTK8;
     const int32_t last = s_hi - 1 - k0;
-    const char* kb = kseq + static_cast<int64_t>(k0) * row_pitch;
-    const char* vb = vseq + static_cast<int64_t>(k0) * row_pitch;
+    const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kseq + static_cast<int64_t>(k0) * row_pitch, kTK8 * row_pitch);
+    const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vseq + static_cast<int64_t>(k0) * row_pitch, kTK8 * row_pitch);
     const int32_t ln = lane_here();
 #pragma unroll
     for (int i = 0; i < kWaveOps; ++i) {
@@ -743,22 +739,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int32_t row = pc / kRowChunks;
       const int32_t lc = (pc % kRowChunks) ^ qswz<D>(row);
       const uint32_t off = static_cast<uint32_t>(min(row, last)) * row_pitch + static_cast<uint32_t>(lc) * 16u;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + off),
-                                       (__attribute__((address_space(3))) void*)(kdst + op * 1024), 16, 0, kStreamAux);
-      if (!KEQV) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + off),
-                                         (__attribute__((address_space(3))) void*)(vdst + op * 1024), 16, 0, kStreamAux);
-      }
+      copy_to_lds<16, kStreamAux>(krs, off, kdst + op * 1024);
+      if (!KEQV) copy_to_lds<16, kStreamAux>(vrs, off, vdst + op * 1024);
     }
-    const int32_t key = k0 + min(ln & 31, last);
-    if (member == 0) {
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kscale + key),
-                                       (__attribute__((address_space(3))) void*)(kscd), 4, 0, kStreamAux);
-    }
-    if (!KEQV && member == kTeam - 1) {
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vscale + key),
-                                       (__attribute__((address_space(3))) void*)(vscd), 4, 0, kStreamAux);
-    }
+    const uint32_t koff = static_cast<uint32_t>(min(ln & 31, last)) * 4u;
+    if (member == 0) copy_to_lds<4, kStreamAux>(raw_rsrc(kscale + k0, kTK8 * 4), koff, kscd);
+    if (!KEQV && member == kTeam - 1) copy_to_lds<4, kStreamAux>(raw_rsrc(vscale + k0, kTK8 * 4), koff, vscd);
   };
 
   auto compute = [&](int32_t ti, const uint8_t* kb, const uint8_t* vb, const float* kscs, const float* vscs) __attribute__((always_inline)) {

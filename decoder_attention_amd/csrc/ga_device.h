@@ -47,6 +47,28 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // of the 8-byte chunks addressed by lanes 4e + i/4, e = 0..3.  Pointing lane j
 // of a group at row (r0 + j/4), column (c0 + 4*(j%4)) of a row-major bf16 tile
 // therefore gives lane i the four rows r0..r0+3 at column c0 + i.
+// Direct-to-LDS copy, buffer form: every lane copies Bytes (4 or 16) from
+// rsrc base + voff to lds + Bytes * lane, with cache-policy bits Aux.  Unlike
+// the global-segment form, the compiler counts this copy on the vector-memory
+// counter only, so the LDS reads issued around it keep partial waits instead
+// of waiting for every outstanding LDS read.  Offsets past the resource's
+// byte range read zeros.
+// (The builtin takes its size and policy only as literal constants.)
+template <int Bytes = 16, int Aux = 0>
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds) {
+  auto* dst = (__attribute__((address_space(3))) void*)(lds);
+  static_assert((Bytes == 16 || Bytes == 4) && (Aux == 0 || Aux == 2), "copy size / policy");
+  if constexpr (Bytes == 16 && Aux == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 0);
+  else if constexpr (Bytes == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 2);
+  else if constexpr (Aux == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, voff, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, voff, 0, 0, 2);
+}
+
+// Buffer resource over nbytes from base (raw addressing, 32-bit offsets).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int32_t>(nbytes), 0x00020000);
+}
+
 __device__ __forceinline__ i16x4 lds_read_tr16(const void* lds_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_addr));
 }

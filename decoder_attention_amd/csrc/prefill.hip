@@ -21,7 +21,7 @@
 //
 // K/V staging
 //   Tiles of 32 keys are copied HBM -> LDS by the gfx950 direct-to-LDS loads
-//   (global_load_lds_dwordx4, no register round trip) into a ring of three
+//   (buffer_load_dwordx4 ... lds, no register round trip) into a ring of three
 //   buffers (two when three do not fit), up to two tiles ahead of the one
 //   being computed; one barrier per tile.
 //   Rows are unpadded and their 16-byte chunks are XOR-swizzled (chunk c of
@@ -254,8 +254,11 @@ void prefill_kernel(PrefillParams p) {
   const int32_t n_tiles = max(0, (kv_end - kv_begin + kKeys - 1) / kKeys);
 
   // Issue the direct-to-LDS copies of the tile starting at key kt into ring
-  // slot B.  Addresses are a wave-uniform tile base plus a 32-bit per-lane
-  // byte offset (row * row pitch + chunk), so they need no 64-bit registers.
+  // slot B.  Addresses are a wave-uniform tile base (a buffer resource over
+  // the tile's 32 rows) plus a 32-bit per-lane byte offset (row * row pitch +
+  // chunk), so they need no 64-bit registers.  The buffer form keeps the
+  // compiler's LDS-read waits partial (the global-segment form made every
+  // consumer of an LDS read wait for all of them).
   const char* kbase = reinterpret_cast<const char*>(p.k) + static_cast<int64_t>(b) * S * p.hkv * D * 2;
   const char* vbase = reinterpret_cast<const char*>(KEQV ? p.k : p.v) + static_cast<int64_t>(b) * S * p.hkv * D * 2;
   const uint32_t row_pitch = static_cast<uint32_t>(p.hkv) * D * 2;
@@ -278,6 +281,8 @@ void prefill_kernel(PrefillParams p) {
     const bool tail = kt < r_lo || kt + kKeys > r_hi;
     uint16_t* kdst = kslot(B);
     uint16_t* vdst = vslot(B);
+    const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kt_base, kKeys * row_pitch);
+    const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vt_base, kKeys * row_pitch);
 #pragma unroll
     for (int i = 0; i < kWaveLoads; ++i) {
       if (kOps % kWaves != 0 && wave * kWaveLoads + i >= kOps) break;   // uniform per wave
@@ -291,12 +296,8 @@ void prefill_kernel(PrefillParams p) {
         off = static_cast<uint32_t>(min(max(row, r_lo - kt), r_hi - 1 - kt)) * row_pitch +
               static_cast<uint32_t>(lc) * 16u;
       }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt_base + off),
-                                       (__attribute__((address_space(3))) void*)(kdst + base * 8), 16, 0, 0);
-      if (!KEQV) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt_base + off),
-                                         (__attribute__((address_space(3))) void*)(vdst + base * 8), 16, 0, 0);
-      }
+      copy_to_lds(krs, off, kdst + base * 8);
+      if (!KEQV) copy_to_lds(vrs, off, vdst + base * 8);
     }
   };
 
