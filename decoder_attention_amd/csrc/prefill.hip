@@ -350,10 +350,19 @@ void prefill_kernel(PrefillParams p) {
       const int32_t hh = ln >> 5;
       const uint32_t kaddr = static_cast<uint32_t>(jj * D * 2 + dlo * 2 + ((hh ^ swz<D>(jj)) << 4));
       const char* kbc = reinterpret_cast<const char*>(kb);
+      // kLA operand reads in flight ahead of the matrix instruction that
+      // consumes them (fenced, so the order holds): the LDS latency is several
+      // matrix instructions long.
+      constexpr int kLA = kDS < 4 ? kDS : 4;
+      bf16x8 a[kLA];
+#pragma unroll
+      for (int ds = 0; ds < kLA; ++ds) a[ds] = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>(ds * 32)));
 #pragma unroll
       for (int ds = 0; ds < kDS; ++ds) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>(ds * 32)));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds % kLA], qf[ds], sacc, 0, 0, 0);
+        if (ds + kLA < kDS)
+          a[ds % kLA] = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>((ds + kLA) * 32)));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (kSplit > 1) {
@@ -429,13 +438,12 @@ void prefill_kernel(PrefillParams p) {
       m_run = m_next;
 
       // Probabilities rounded to bf16; the row sum adds the same rounded
-      // values (v_dot2_f32_bf16 against (1, 1)).
+      // values (v_dot2_f32_bf16 against (1, 1)), in key order.
       uint32_t pk[8];
       const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
       const float cap_m = p.cap_log2 - m_use;
       const float neg2cap = -2.f * p.cap_log2;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
+      auto prob_pair = [&](int r) {
         float e0, e1;
         if (CAP) {
           e0 = __builtin_amdgcn_exp2f(fmaf(neg2cap, x[2 * r], cap_m));
@@ -446,33 +454,52 @@ void prefill_kernel(PrefillParams p) {
         }
         pk[r] = pack_bf16x2(e0, e1);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r]), ones, l_run, false);
-      }
+      };
+#pragma unroll
+      for (int r = 0; r < 4; ++r) prob_pair(r);   // keys 0-15: the first half's operand
 
-      // O^T += V^T . P^T, two 16-key halves per tile.  Lane (lgrp, li16)
-      // reads chunk dlo/8 + 4*db + 2*(lgrp&1) + (li16&3)/2 of rows r0 and
-      // r0 + 8; as for K, the chunk bits are clear of the row, slice and
-      // half-chunk bits, so block db's address is one XOR: base ^ (64 * db).
+      // O^T += V^T . P^T, two 16-key halves per tile (product v: half
+      // v / kDB, 32-row block v % kDB).  Lane (lgrp, li16) reads chunk
+      // dlo/8 + 4*db + 2*(lgrp&1) + (li16&3)/2 of rows r0 and r0 + 8; as for
+      // K, the chunk bits are clear of the row, slice and half-chunk bits, so
+      // block db's address is one XOR: base ^ (64 * db).  The operands of
+      // kLV products are read ahead (fenced), and the second half's
+      // probabilities are computed during the first half's products.
       const int32_t ln = lane_id_here();
       const int32_t lgrp = ln >> 4;
       const int32_t li16 = ln & 15;
       const int32_t cl = 2 * (lgrp & 1) + ((li16 & 3) >> 1);
       const char* vbc = reinterpret_cast<const char*>(vb);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 pb = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
-        const bf16x8 bop = __builtin_bit_cast(bf16x8, pb);
+      const uint32_t rest = static_cast<uint32_t>(dlo * 2 + (li16 & 1) * 8);
+      auto vread = [&](int v) -> bf16x8 {
+        const int t = v / kDB;
+        const int db = v % kDB;
         const int32_t r0 = 16 * t + 4 * (ln >> 5) + (li16 >> 2);
         const int32_t r1 = r0 + 8;
-        const uint32_t rest = static_cast<uint32_t>(dlo * 2 + (li16 & 1) * 8);
         const uint32_t va0 = static_cast<uint32_t>(r0 * D * 2 + ((cl ^ swz<D>(r0)) << 4)) + rest;
         const uint32_t va1 = static_cast<uint32_t>(r1 * D * 2 + ((cl ^ swz<D>(r1)) << 4)) + rest;
+        const i16x4 a0 = lds_read_tr16(vbc + (va0 ^ static_cast<uint32_t>(db * 64)));
+        const i16x4 a1 = lds_read_tr16(vbc + (va1 ^ static_cast<uint32_t>(db * 64)));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int kV = 2 * kDB;
+      constexpr int kLV = 3;
+      bf16x8 va[kLV];
 #pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const i16x4 a0 = lds_read_tr16(vbc + (va0 ^ static_cast<uint32_t>(db * 64)));
-          const i16x4 a1 = lds_read_tr16(vbc + (va1 ^ static_cast<uint32_t>(db * 64)));
-          const bf16x8 aop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, o[db], 0, 0, 0);
+      for (int v = 0; v < kLV; ++v) va[v] = vread(v);
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int t = v / kDB;
+        const int db = v % kDB;
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]});
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[v % kLV], bop, o[db], 0, 0, 0);
+        if (v + kLV < kV) va[v % kLV] = vread(v + kLV);
+        if (t == 0) {
+#pragma unroll
+          for (int r = 4; r < 8; ++r)
+            if ((r - 4) * kDB / 4 == db) prob_pair(r);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // The next tile's copies must have landed before anyone reads them; the
