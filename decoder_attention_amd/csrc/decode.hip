@@ -442,10 +442,18 @@ void decode_split_kernel(DecodeParams p) {
     const int32_t lgrp = ln >> 4;
     const uint32_t kaddr = static_cast<uint32_t>(li16 * D * 2 + ((lgrp ^ dswz<D>(li16)) << 4));
     const char* kbc = reinterpret_cast<const char*>(kb);
+    // kLA operand reads in flight ahead of the product that consumes them
+    // (fenced, so the order holds): the LDS latency spans several products.
+    constexpr int kLA = kDS < 4 ? kDS : 4;
+    bf16x8 ka[kLA];
+#pragma unroll
+    for (int ds = 0; ds < kLA; ++ds) ka[ds] = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>(ds << 6)));
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>(ds << 6)));
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ds], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ds % kLA], qf[ds], sacc, 0, 0, 0);
+      if (ds + kLA < kDS)
+        ka[ds % kLA] = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>((ds + kLA) << 6)));
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Lane holds keys k0 + grp*4 + r for head `col`.
     float x[4];
