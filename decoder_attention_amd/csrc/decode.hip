@@ -964,25 +964,51 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
   auto empty = [&](int64_t w) {
     return !p.per_seq && wg_start(w, total, p.n_wg) == wg_start(w + 1, total, p.n_wg);
   };
+  // The largest partial max: the lanes take the partials in turn (their
+  // loads independent), then a reduction across the wave.
   float m_all = -INFINITY;
-  for (int64_t w = wa; w <= wb; ++w) {
+  for (int64_t w = wa + lane; w <= wb; w += 64) {
     if (!empty(w)) m_all = fmaxf(m_all, p.ws_m[part_of(w)]);
   }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) m_all = fmaxf(m_all, __shfl_xor(m_all, sh, 64));
+  // The weighted sum, in partial order; kAhead partials are loaded before
+  // the first of them is used, so their loads are in flight together.
+  constexpr int kAhead = 4;
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
   float l_all = 0.f;
   const int32_t d0 = lane * kPer;
-  for (int64_t w = wa; w <= wb; ++w) {
-    if (empty(w)) continue;
-    const int64_t part = part_of(w);
-    const float ms = p.ws_m[part];
-    const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m_all);
-    l_all = fmaf(p.ws_l[part], f, l_all);
-    if (d0 < D) {
-      const float* src = p.ws_o + part * D + d0;
+  for (int64_t w0 = wa; w0 <= wb; w0 += kAhead) {
+    bool use[kAhead];
+    float ms[kAhead], ls[kAhead], os[kAhead][kPer];
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) acc[e] = fmaf(src[e], f, acc[e]);
+    for (int i = 0; i < kAhead; ++i) {
+      const int64_t w = w0 + i;
+      use[i] = w <= wb && !empty(w);
+      ms[i] = -INFINITY;
+      ls[i] = 0.f;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) os[i][e] = 0.f;
+      if (use[i]) {
+        const int64_t part = part_of(w);
+        ms[i] = p.ws_m[part];
+        ls[i] = p.ws_l[part];
+        if (d0 < D) {
+          const float* src = p.ws_o + part * D + d0;
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) os[i][e] = src[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      if (!use[i]) continue;
+      const float f = ms[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[i] - m_all);
+      l_all = fmaf(ls[i], f, l_all);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc[e] = fmaf(os[i][e], f, acc[e]);
     }
   }
   const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
