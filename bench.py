@@ -114,7 +114,7 @@ def layer_inputs(cfg_id, kw, layer, B, S, with_norm):
     return h
 
 
-def _layer_tensors(cfg_id, kw, layer, B, S, with_norm, host=None):
+def layer_tensors(cfg_id, kw, layer, B, S, with_norm, host=None):
     """Device tensors of one prefill layer (from ``host``, else freshly drawn)."""
     import torch
 
@@ -182,7 +182,7 @@ def bench_pair(ga, steps, warmup):
     import torch
 
     cfg_id, kw, _, B, S, norm = PREFILL_WORKLOADS["gemma2_pair"]
-    layers = {layer: _layer_tensors(cfg_id, kw, layer, B, S, norm) for layer in (0, 1)}
+    layers = {layer: layer_tensors(cfg_id, kw, layer, B, S, norm) for layer in (0, 1)}
     flops = {layer: _flops(kw, layer, B, S) for layer in (0, 1)}
     for _ in range(warmup):
         for layer in (0, 1):
@@ -223,7 +223,7 @@ def bench_prefill_layer(ga, workload, layer, reps=10):
     import torch
 
     cfg_id, kw, _, B, S, with_norm = PREFILL_WORKLOADS[workload]
-    t = _layer_tensors(cfg_id, kw, layer, B, S, with_norm)
+    t = layer_tensors(cfg_id, kw, layer, B, S, with_norm)
     for _ in range(2):
         run_layer_step(ga, kw, layer, t)
     torch.cuda.synchronize()

@@ -54,7 +54,7 @@ def test_prefill_full_size_sampled(gpu, case, workload, layer):
     Hq, W = cfg.num_heads, L["window"]
     print(f"[fullsize] {case}: B={B} S={S} D={L['head_dim']} window={W}", flush=True)
     h = bench.layer_inputs(cfg_id, kw, layer, B, S, norm)
-    t = bench._layer_tensors(cfg_id, kw, layer, B, S, norm, host=h)
+    t = bench.layer_tensors(cfg_id, kw, layer, B, S, norm, host=h)
     bench.run_layer_step(ga, kw, layer, t)                 # the timed launch: prologue, then prefill
     out2, lse = ga.attn_prefill(kw, layer, t["qt"], t["kt"], t["v"], want_lse=True)
     torch.cuda.synchronize()
