@@ -1023,6 +1023,300 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many query columns per KV head at head width 512 with keys as values (the
+// query heads of an MQA global layer times several new tokens): dense enough
+// for the prefill's tile structure.  A workgroup is four waves, two D-split
+// pairs of 32 columns, so 64 columns, (token, head) = divmod(cg*64 + c, g).
+// Each wave holds half of Q^T and O^T.  Per 32-key tile of the cache:
+//   * S^T over the wave's half of D (v_mfma_f32_32x32x16_bf16, K operands
+//     read four products ahead);
+//   * the partial scores exchanged through LDS, so both waves of a pair hold
+//     the same fp32 sums (a + b == b + a);
+//   * the softmax (masked on boundary tiles only, lazily updated running max);
+//   * O^T += V^T . P^T over the wave's half (V operands read two ahead;
+//     with keys as values the same LDS tile is both).
+// Work items, key ranges, the partial layout and the combine are those of
+// the split kernel above.
+namespace tile {
+constexpr int kD = 512;
+constexpr int kKeys = 32;
+constexpr int kDW = kD / 2;                     // D half per wave
+constexpr int kDS = kDW / 16;                   // k-steps of S^T
+constexpr int kDB = kDW / 32;                   // 32-row blocks of O^T
+constexpr int kRowChunks = kD / 8;              // 16-byte chunks per cache row
+constexpr int kTileElems = kKeys * kD;
+constexpr int kOps = kKeys * kRowChunks / 64;   // 1 KB copy ops per tile
+constexpr int kWaveOps = kOps / 4;
+constexpr float kTau = 8.f;                     // lazy-rescale threshold (log2 units)
+
+// XOR pattern of LDS row r's 16-byte chunks (a 4-bit rotate of r): the S^T
+// reads (16 rows at one chunk per ds_read_b128 phase) and the V^T transpose
+// reads (4 rows x 4 chunks per half-wave) are free of bank conflicts.
+__device__ __forceinline__ int32_t swz(int32_t r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_min(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+}  // namespace tile
+
+template <int G, bool CAP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_tile_kernel(DecodeParams p) {
+  using namespace tile;
+  __shared__ __attribute__((aligned(16))) uint16_t ts0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t ts1[kTileElems];
+  __shared__ __attribute__((aligned(16))) f32x4 sx[4 * 4 * 64];   // [wave][r/4][lane] partial scores
+
+  const DecodeBlock blk = decode_block(p);
+  if (!blk.valid) return;                                        // padding block (uniform)
+  const int32_t kvh = blk.kvh;
+  const int32_t tid = threadIdx.x;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t lane = tid & 63;
+  const int32_t j = lane & 31;       // column within the pair
+  const int32_t h = lane >> 5;       // half of the wave
+  const int32_t dlo = (wave & 1) * kDW;
+  const int32_t ncols = G * p.q_len;
+  const int32_t g0 = blk.cb * 64 + (wave >> 1) * 32;                // the pair's first column
+  const int32_t gcol = g0 + j;
+  const bool col_ok = gcol < ncols;
+  const int32_t tok = col_ok ? gcol / G : 0;
+  const int32_t head = kvh * G + (col_ok ? gcol % G : 0);
+  // First and last token among the pair's columns (for the unmasked-tile test).
+  const int32_t tok_first = g0 / G;
+  const int32_t tok_last = (min(g0 + 31, ncols - 1)) / G;
+  const uint32_t row_pitch = static_cast<uint32_t>(p.hkv) * kD * 2;
+
+  for_each_segment(p, blk.w, [&](int32_t b, int32_t s_lo, int32_t s_hi, int32_t ctx) __attribute__((always_inline)) {
+  const int32_t n_t = (s_hi - s_lo + kKeys - 1) / kKeys;
+  // Keys this column may see: [key_lo, key_hi] (its own position and the window).
+  const int32_t key_hi = col_ok ? ctx - p.q_len + tok : -1;
+  const int32_t key_lo = p.window > 0 ? key_hi - p.window + 1 : 0;
+  const int32_t first_hi = ctx - p.q_len + tok_first;
+  const int32_t last_lo = ctx - p.q_len + tok_last - p.window + 1;
+  const char* kseq = reinterpret_cast<const char*>(p.kc) + (static_cast<int64_t>(b) * p.max_ctx * p.hkv + kvh) * kD * 2;
+
+  // Copy tile ti (keys s_lo + 32*ti ...) into dst.  Rows past s_hi repeat
+  // row s_hi - 1 (masked), so no row outside the sequence's range is read.
+  auto issue = [&](int32_t ti, uint16_t* dst) __attribute__((always_inline)) {
+    const int32_t k0 = s_lo + ti * kKeys;
+    const int32_t last = s_hi - 1 - k0;
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(kseq + static_cast<int64_t>(k0) * row_pitch, kKeys * row_pitch);
+    const int32_t ln = lane_here();
+#pragma unroll
+    for (int i = 0; i < kWaveOps; ++i) {
+      // op i of this wave covers one row: 64 lanes x 16 bytes = 1 KB
+      const int32_t first = (wave * kWaveOps + i) * 64;
+      const int32_t row = first / kRowChunks;
+      const int32_t lc = ln ^ swz(row);
+      const uint32_t off = static_cast<uint32_t>(min(row, last)) * row_pitch + static_cast<uint32_t>(lc) * 16u;
+      copy_to_lds<16, kStreamAux>(rs, off, dst + first * 8);
+    }
+  };
+
+  // Q^T operand: lane holds d = dlo + ds*16 + h*8 + [0, 8) of its column.
+  bf16x8 qf[kDS];
+  {
+    const uint16_t* qrow = p.q + ((static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head) * kD + dlo + h * 8;
+#pragma unroll
+    for (int ds = 0; ds < kDS; ++ds) qf[ds] = col_ok ? *reinterpret_cast<const bf16x8*>(qrow + ds * 16) : bf16x8{};
+  }
+  f32x16 o[kDB];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  if (n_t > 0) issue(0, ts0);
+  wait_vmcnt<0>();   // Q^T and the first tile
+  __syncthreads();
+
+  // Tile ti from slot cur, while tile ti + 1 is copied into nxt.
+  auto step = [&](int32_t ti, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
+    if (ti + 1 < n_t) issue(ti + 1, nxt);
+    const int32_t kt = s_lo + ti * kKeys;
+    const int32_t ln = lane_here();
+    // S^T over this wave's half of D.  Lane (jj, hh) reads chunk
+    // dlo/8 + 2*ds + hh of key row jj; step ds is one XOR of the base.
+    f32x16 sacc = f32x16{};
+    {
+      const int32_t jj = ln & 31;
+      const int32_t hh = ln >> 5;
+      const uint32_t kaddr = static_cast<uint32_t>(jj * kD * 2 + dlo * 2 + ((hh ^ swz(jj)) << 4));
+      const char* kbc = reinterpret_cast<const char*>(cur);
+      constexpr int kLA = 4;
+      bf16x8 a[kLA];
+#pragma unroll
+      for (int ds = 0; ds < kLA; ++ds) a[ds] = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>(ds * 32)));
+#pragma unroll
+      for (int ds = 0; ds < kDS; ++ds) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds % kLA], qf[ds], sacc, 0, 0, 0);
+        if (ds + kLA < kDS)
+          a[ds % kLA] = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>((ds + kLA) * 32)));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // The pair's two halves of D: consecutive lanes, consecutive 16 bytes.
+    {
+      f32x4* mine = sx + wave * 256 + ln;
+      const f32x4* other = sx + (wave ^ 1) * 256 + ln;
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) mine[(r / 4) * 64] = f32x4{sacc[r], sacc[r + 1], sacc[r + 2], sacc[r + 3]};
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const f32x4 t4 = other[(r / 4) * 64];
+        sacc[r] += t4[0];
+        sacc[r + 1] += t4[1];
+        sacc[r + 2] += t4[2];
+        sacc[r + 3] += t4[3];
+      }
+    }
+    // Lane holds keys kt + (r/4)*8 + h*4 + r%4 of its column.  With a cap,
+    // x = 1/(exp(2*s*scale/cap) + 1) and the capped logit is cap*(1 - 2x)
+    // (log2 units): the row max comes from the smallest x, a masked key gets
+    // +inf.  Without a cap x = s and a masked key gets -inf.
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (CAP) x[r] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(sacc[r] * p.cap_in2) + 1.f);
+      else x[r] = sacc[r];
+    }
+    const bool full = kt + kKeys - 1 < s_hi && kt + kKeys - 1 <= first_hi && (p.window <= 0 || kt >= last_lo);
+    if (__builtin_expect(!full, 0)) {
+      const int32_t kb0 = kt + h * 4;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t key = kb0 + (r >> 2) * 8 + (r & 3);
+        const bool ok = (key < s_hi) & (key <= key_hi) & (key >= key_lo);
+        x[r] = ok ? x[r] : (CAP ? INFINITY : -INFINITY);
+      }
+    }
+    float mx;
+    if (CAP) {
+      float mr = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mr = fminf(mr, x[r]);
+      mr = xhalf_min(mr);
+      mx = fmaf(-2.f * p.cap_log2, mr, p.cap_log2);
+    } else {
+      mx = x[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      mx = xhalf_max(mx) * p.scale_log2;
+    }
+    const bool grow = mx > m_run + kTau;
+    const float m_next = grow ? mx : m_run;
+    const float m_use = m_next == -INFINITY ? 0.f : m_next;
+    if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) o[db] *= alpha;
+    }
+    m_run = m_next;
+
+    // Probabilities rounded to bf16; the row sum adds the same rounded values.
+    uint32_t pk[8];
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+    const float cap_m = p.cap_log2 - m_use;
+    const float neg2cap = -2.f * p.cap_log2;
+    auto prob_pair = [&](int r) {
+      float e0, e1;
+      if (CAP) {
+        e0 = __builtin_amdgcn_exp2f(fmaf(neg2cap, x[2 * r], cap_m));
+        e1 = __builtin_amdgcn_exp2f(fmaf(neg2cap, x[2 * r + 1], cap_m));
+      } else {
+        e0 = __builtin_amdgcn_exp2f(fmaf(x[2 * r], p.scale_log2, -m_use));
+        e1 = __builtin_amdgcn_exp2f(fmaf(x[2 * r + 1], p.scale_log2, -m_use));
+      }
+      pk[r] = pack_bf16x2(e0, e1);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[r]), ones, l_run, false);
+    };
+#pragma unroll
+    for (int r = 0; r < 4; ++r) prob_pair(r);
+
+    // O^T += V^T . P^T: product v is half v / kDB (16 keys), block v % kDB.
+    // Lane (lgrp, li16) reads chunk dlo/8 + 4*db + 2*(lgrp&1) + (li16&3)/2 of
+    // rows r0 and r0 + 8 (transpose reads); block db is one XOR of the base.
+    {
+      const int32_t lgrp = ln >> 4;
+      const int32_t li16 = ln & 15;
+      const int32_t cl = 2 * (lgrp & 1) + ((li16 & 3) >> 1);
+      const char* vbc = reinterpret_cast<const char*>(cur);
+      const uint32_t rest = static_cast<uint32_t>(dlo * 2 + (li16 & 1) * 8);
+      auto vread = [&](int v) -> bf16x8 {
+        const int t = v / kDB;
+        const int db = v % kDB;
+        const int32_t r0 = 16 * t + 4 * (ln >> 5) + (li16 >> 2);
+        const int32_t r1 = r0 + 8;
+        const uint32_t va0 = static_cast<uint32_t>(r0 * kD * 2 + ((cl ^ swz(r0)) << 4)) + rest;
+        const uint32_t va1 = static_cast<uint32_t>(r1 * kD * 2 + ((cl ^ swz(r1)) << 4)) + rest;
+        const i16x4 a0 = lds_read_tr16(vbc + (va0 ^ static_cast<uint32_t>(db * 64)));
+        const i16x4 a1 = lds_read_tr16(vbc + (va1 ^ static_cast<uint32_t>(db * 64)));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int kV = 2 * kDB;
+      constexpr int kLV = 2;
+      bf16x8 va[kLV];
+#pragma unroll
+      for (int v = 0; v < kLV; ++v) va[v] = vread(v);
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const int t = v / kDB;
+        const int db = v % kDB;
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]});
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[v % kLV], bop, o[db], 0, 0, 0);
+        if (v + kLV < kV) va[v % kLV] = vread(v + kLV);
+        if (t == 0) {
+#pragma unroll
+          for (int r = 4; r < 8; ++r)
+            if ((r - 4) * kDB / 4 == db) prob_pair(r);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // The next tile must have landed before it is read, and this slot and the
+    // score buffer are rewritten only after every wave is done with them.
+    wait_vmcnt<0>();
+    __syncthreads();
+  };
+  for (int32_t ti = 0; ti < n_t; ti += 2) {
+    step(ti, ts0, ts1);
+    if (ti + 1 < n_t) step(ti + 1, ts1, ts0);
+  }
+
+  const float l_tot = xhalf_sum(l_run);
+  // Partial of (sequence b, token tok, head) from workgroup w: slot w + b.
+  if (col_ok) {
+    const int64_t part = ((static_cast<int64_t>(blk.w) + b) * p.q_len + tok) * p.hq + head;
+    float* dst = p.ws_o + part * kD + dlo;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        *reinterpret_cast<f32x4*>(dst + db * 32 + a * 8 + h * 4) =
+            f32x4{o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]};
+      }
+    }
+    if ((wave & 1) == 0 && h == 0) {
+      p.ws_m[part] = m_run;
+      p.ws_l[part] = l_tot;
+    }
+  }
+  __syncthreads();   // LDS slots are reused by the next segment
+  });
+}
+
 template <int D, int G, bool KEQV, bool CAP>
 hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t stream) {
   if (!a.per_seq) {   // the balanced ranges need the prefix sums of the spans
@@ -1034,13 +1328,21 @@ hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t st
   // head times several tokens): four blocks per workgroup share one stream
   // of cache tiles (bf16 caches, head width 256 or 512).
   constexpr int kCBW = 4;
-  const bool wide = !prm.ks && D >= 256 && prm.n_cb >= 3;
+  const bool tile = a.tile != 0;
+  const bool wide = !tile && !prm.ks && D >= 256 && prm.n_cb >= 3;
   DecodeParams pp = prm;
   if (wide) pp.n_cb = (prm.n_cb + kCBW - 1) / kCBW;
+  if (tile) pp.n_cb = (a.group * a.q_len + 63) / 64;   // 64-column groups
   const int64_t nblocks = decode_grid(a.hkv, a.n_wg, pp.n_cb);
   if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(nblocks), 1u, 1u);
-  if (prm.ks) {
+  if (tile) {
+    if constexpr (D == 512 && KEQV) {
+      hipLaunchKernelGGL((decode_tile_kernel<G, CAP>), grid, dim3(256), 0, stream, pp);
+    } else {
+      return hipErrorInvalidValue;   // the plan selects the tile kernel only for keys as values at width 512
+    }
+  } else if (prm.ks) {
     hipLaunchKernelGGL((decode_split_i8_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D, 1>::kWaves * 64), 0, stream,
                        pp);
   } else if (wide) {

@@ -53,6 +53,7 @@ struct DecodeArgs {
   int32_t batch, max_ctx, hq, hkv, dim, group, window, k_eq_v;
   int32_t n_wg, q_len;        // workgroups per (KV head, column block); query tokens per sequence
   int32_t per_seq;            // 1: workgroup w takes sequence w whole (n_wg = batch)
+  int32_t tile;               // 1: the 32-key tile kernel (bf16, keys as values, head width 512)
   const void* q;
   const void* k_cache;
   const void* v_cache;

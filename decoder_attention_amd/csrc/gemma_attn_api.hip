@@ -86,6 +86,7 @@ int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch
   a.k_eq_v = L.k_eq_v;
   a.n_wg = plan.n_wg;
   a.per_seq = plan.per_seq ? 1 : 0;
+  a.tile = (plan.tile && k_scales == nullptr) ? 1 : 0;
   a.q_len = q_len;
   a.q = q;
   a.k_cache = k_cache;

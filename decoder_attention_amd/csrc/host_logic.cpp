@@ -83,14 +83,24 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
   p.span_max = L.window > 0 ? static_cast<int32_t>(wspan < max_ctx ? wspan : max_ctx) : max_ctx;
   if (p.span_max < 1) p.span_max = 1;
   const long long col_blocks = (static_cast<long long>(L.group) * ql + 15) / 16;
-  const long long rows = static_cast<long long>(L.num_kv_heads) * col_blocks;
-  // One round of workgroups on 256 CUs: the split kernel's workgroups per CU
-  // follow from its LDS ring (two waves per workgroup, two waves per SIMD).
-  const long long team = L.head_dim > 256 ? 2 : 1;
-  const long long lds = (2 / team) * 2 * 16LL * L.head_dim * 2 * (L.k_eq_v ? 1 : 2);
-  long long per_cu = (160LL * 1024) / lds;
-  if (per_cu > 4) per_cu = 4;
-  if (per_cu < 1) per_cu = 1;
+  // Many query columns per KV head at head width 512 with keys as values (a
+  // multi-token step on an MQA global layer): the tile kernel, which takes 64
+  // columns per workgroup through 32x32 products, two workgroups per CU.
+  p.tile = L.k_eq_v && L.head_dim == 512 && col_blocks >= 3;
+  long long rows = static_cast<long long>(L.num_kv_heads) * col_blocks;
+  long long per_cu;
+  if (p.tile) {
+    rows = static_cast<long long>(L.num_kv_heads) * ((static_cast<long long>(L.group) * ql + 63) / 64);
+    per_cu = 2;
+  } else {
+    // One round of workgroups on 256 CUs: the split kernel's workgroups per CU
+    // follow from its LDS ring (two waves per workgroup, two waves per SIMD).
+    const long long team = L.head_dim > 256 ? 2 : 1;
+    const long long lds = (2 / team) * 2 * 16LL * L.head_dim * 2 * (L.k_eq_v ? 1 : 2);
+    per_cu = (160LL * 1024) / lds;
+    if (per_cu > 4) per_cu = 4;
+    if (per_cu < 1) per_cu = 1;
+  }
   long long n = (256 * per_cu) / rows;
   const long long line_max = static_cast<long long>(batch > 0 ? batch : 1) * p.span_max;
   const long long at_least = (line_max + 16383) / 16384;   // at most 16K keys per workgroup

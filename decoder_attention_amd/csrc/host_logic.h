@@ -37,6 +37,8 @@ struct DecodePlan {
   int32_t n_wg;
   int32_t span_max;
   bool per_seq;   // workgroup w takes sequence w whole (n_wg = B); see decode_plan
+  bool tile;      // bf16 keys-as-values caches at head width 512 with >= 48 query columns per KV head:
+                  // the 32-key tile kernel, 64 columns per workgroup, two workgroups per CU
 };
 DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t max_ctx, int32_t q_len);
 

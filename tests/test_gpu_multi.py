@@ -20,6 +20,10 @@ pytestmark = pytest.mark.gpu
 MULTI = [
     ("gemma4_local_q4", GEMMA4 | dict(sliding_window=1024), 0, 4),
     ("gemma4_global_keqv_q3", GEMMA4, 5, 3),
+    # many columns per KV head at width 512 (the 32-key tile kernel): a capped
+    # variant with a partly filled second column group, and four column groups
+    ("gemma4_global_keqv_cap_q5", GEMMA4 | dict(attn_logit_softcapping=30.0), 5, 5),
+    ("gemma4_global_keqv_q16", GEMMA4, 5, 16),
     ("gemma2_local_cap_q8", GEMMA2, 0, 8),
     ("gemma2_global_cap_q5", GEMMA2, 1, 5),
     ("gemma3_local_mqa_q16", GEMMA3, 0, 16),
