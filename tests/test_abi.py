@@ -237,3 +237,22 @@ def test_int8_entry_points_reject_bad_arguments(ga):
     assert Q(2, 4, 0, 64, 16, fake, None, fake, fake, None) == ga.GA_ERR_INVALID_ARG
     assert Q(2, 4, 1, 64, 16, fake, None, fake, None, None) == ga.GA_ERR_INVALID_ARG
     assert Q(0, 4, 1, 64, 16, None, None, None, None, None) == ga.GA_OK
+
+
+@pytest.mark.parametrize("q_len", [1, 2, 3, 4, 5, 16])
+def test_decode_workspace_follows_the_kernel_choice(ga, q_len):
+    """Keys as values at head width 512 (an MQA global layer, g = 16): with 48 or more query columns the
+    32-key tile kernel runs, 64 columns per workgroup and two workgroups per CU; otherwise the split
+    kernel, 16-column blocks and four workgroups per CU (a 32 KB ring).  The workspace holds one partial
+    per (workgroup + sequence, token, head) of the chosen plan."""
+    kw = dict(num_heads=16, num_kv_heads=1, head_dim=512, k_eq_v=True, sliding_window=0, sliding_window_pattern=1)
+    B, max_ctx = 64, 65536
+    need = ga.decode_multi_workspace_size(kw, 0, B, q_len, max_ctx)
+    cols = 16 * q_len
+    if cols >= 48:
+        rows, per_cu = -(-cols // 64), 2
+    else:
+        rows, per_cu = -(-cols // 16), 4
+    line = B * max_ctx
+    n_wg = max(1, min(max(256 * per_cu // rows, -(-line // 16384)), -(-line // 256)))
+    assert need == _decode_ws_bytes(B, q_len, 16, 512, n_wg)
