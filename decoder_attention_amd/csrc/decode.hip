@@ -1154,14 +1154,18 @@ void decode_tile_kernel(DecodeParams p) {
       const uint32_t kaddr = static_cast<uint32_t>(jj * kD * 2 + dlo * 2 + ((hh ^ swz(jj)) << 4));
       const char* kbc = reinterpret_cast<const char*>(cur);
       constexpr int kLA = 4;
+      // Address bit 8 of kaddr is clear, so the step's top bit is an addition,
+      // which folds into the instruction's offset.
+      auto kread = [&](int ds) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>((ds & 7) * 32)) + (ds >> 3) * 256);
+      };
       bf16x8 a[kLA];
 #pragma unroll
-      for (int ds = 0; ds < kLA; ++ds) a[ds] = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>(ds * 32)));
+      for (int ds = 0; ds < kLA; ++ds) a[ds] = kread(ds);
 #pragma unroll
       for (int ds = 0; ds < kDS; ++ds) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds % kLA], qf[ds], sacc, 0, 0, 0);
-        if (ds + kLA < kDS)
-          a[ds % kLA] = *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>((ds + kLA) * 32)));
+        if (ds + kLA < kDS) a[ds % kLA] = kread(ds + kLA);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1261,8 +1265,10 @@ void decode_tile_kernel(DecodeParams p) {
         const int32_t r1 = r0 + 8;
         const uint32_t va0 = static_cast<uint32_t>(r0 * kD * 2 + ((cl ^ swz(r0)) << 4)) + rest;
         const uint32_t va1 = static_cast<uint32_t>(r1 * kD * 2 + ((cl ^ swz(r1)) << 4)) + rest;
-        const i16x4 a0 = lds_read_tr16(vbc + (va0 ^ static_cast<uint32_t>(db * 64)));
-        const i16x4 a1 = lds_read_tr16(vbc + (va1 ^ static_cast<uint32_t>(db * 64)));
+        // bit 8 of va0/va1 is clear: db's top bit is an offset addition
+        const uint32_t x = static_cast<uint32_t>((db & 3) * 64);
+        const i16x4 a0 = lds_read_tr16(vbc + (va0 ^ x) + (db >> 2) * 256);
+        const i16x4 a1 = lds_read_tr16(vbc + (va1 ^ x) + (db >> 2) * 256);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       constexpr int kV = 2 * kDB;
