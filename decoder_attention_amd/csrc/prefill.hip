@@ -47,6 +47,12 @@
 //     tile is both K and V.
 //   Tiles outside a wave's causal/window band are skipped by that wave.
 //
+// Output
+//   O^T leaves the accumulators through the idle ring: each wave parks its
+//   32 columns in LDS and writes them back in row order, 16 bytes per lane,
+//   so a store instruction covers whole cache lines instead of 16-byte
+//   pieces of 32 rows.
+//
 // Sources: causal decoder attention (Gemma page), sliding-window local layers
 // and the tanh logit soft cap (Gemma 2 page, introduction and Gemma2Model
 // table), query_pre_attn_scalar (Gemma 2 / Gemma 3 tables), GQA/MQA head
@@ -214,6 +220,27 @@ void prefill_kernel(PrefillParams p) {
     else if constexpr (decltype(B)::value == 0) return v_lds0;
     else if constexpr (decltype(B)::value == 1) return v_lds1;
     else return v_lds2;
+  };
+  // After the last tile the ring arrays hold each wave's output slice
+  // (32 columns x kDW) on its way to memory: array n of the ring (K slots,
+  // then V slots) holds kStagePer slices.
+  constexpr int kStageBytes = kCols * kDW * 2;
+  constexpr int kStagePer = kTileElems * 2 / kStageBytes;
+  constexpr int kRingArrays = KEQV ? kBufs : 2 * kBufs;
+  constexpr bool kStageO = kStagePer >= 1 && kRingArrays * kStagePer >= kWaves;
+  auto stage_region = [&](int n) -> uint16_t* {
+    if (n == 0) return k_lds0;
+    if constexpr (kBufs > 2) {
+      if (n == 2) return k_lds2;
+    }
+    if constexpr (!KEQV) {
+      if (n == kBufs) return v_lds0;
+      if (n == kBufs + 1) return v_lds1;
+      if constexpr (kBufs > 2) {
+        if (n == kBufs + 2) return v_lds2;
+      }
+    }
+    return k_lds1;
   };
 
   int32_t pair, tq;
@@ -525,27 +552,60 @@ void prefill_kernel(PrefillParams p) {
   }
 
   const float l_tot = xhalf_sum(l_run);
-  if (col_valid) {
-    // Padded rows are written as exact zeros (their accumulators are not
-    // meaningful: a padded query row may hold anything).
-    const bool live = kept && l_tot > 0.f;
-    const float inv = live ? 1.f / l_tot : 0.f;
-    uint16_t* orow = p.out + ((static_cast<int64_t>(b) * S + pos) * p.hq + head) * D + dlo;
+  // Padded rows are written as exact zeros (their accumulators are not
+  // meaningful: a padded query row may hold anything).
+  const bool live = kept && l_tot > 0.f;
+  const float inv = live ? 1.f / l_tot : 0.f;
+  auto out_pair = [&](int db, int a) -> u32x2 {
+    u32x2 w2;
+    w2[0] = pack_bf16x2(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
+    w2[1] = pack_bf16x2(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+    return kept ? w2 : u32x2{0u, 0u};
+  };
+  if constexpr (kStageO) {
+    // The accumulators hold O^T: a lane owns one column and 8-byte pieces of
+    // its row, so stores straight from them would write 16 bytes into each
+    // of 32 rows per instruction.  Instead each wave parks its slice in its
+    // own region of the (now idle) ring, then reads it back in row order and
+    // writes whole 16-byte chunks: one instruction covers 1 KB of rows.
+    wait_vmcnt<0>();
+    __syncthreads();                 // every wave is done with the ring
+    char* st = reinterpret_cast<char*>(stage_region(wave / kStagePer)) + (wave % kStagePer) * kStageBytes;
+    constexpr int kRowCh = kDW / 8;  // 16-byte chunks per staged row
+    constexpr int kSwz = (kRowCh < 16 ? kRowCh : 16) - 1;
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int32_t d = db * 32 + a * 8 + h * 4;
-        u32x2 w2;
-        w2[0] = pack_bf16x2(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
-        w2[1] = pack_bf16x2(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
-        if (!kept) w2 = u32x2{0u, 0u};
-        *reinterpret_cast<u32x2*>(orow + d) = w2;
+        const int32_t ch = (db * 4 + a) ^ (j & kSwz);
+        *reinterpret_cast<u32x2*>(st + j * (kDW * 2) + ch * 16 + h * 8) = out_pair(db, a);
       }
     }
-    if (p.lse && h == 0 && dlo == 0) {
-      p.lse[(static_cast<int64_t>(b) * p.hq + head) * S + pos] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    __syncthreads();
+    const int32_t ln = lane_id_here();
+#pragma unroll
+    for (int i = 0; i < kCols * kRowCh / 64; ++i) {
+      const int32_t q = i * 64 + ln;
+      const int32_t col = q / kRowCh;
+      const int32_t dc = q % kRowCh;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + col * (kDW * 2) + ((dc ^ (col & kSwz)) * 16));
+      const int32_t cc = cw * kCols + col;
+      const int32_t cpos = p0 + cc / G;
+      if (cpos < S) {
+        uint16_t* dst = p.out + ((static_cast<int64_t>(b) * S + cpos) * p.hq + kvh * G + cc % G) * D + dlo + dc * 8;
+        *reinterpret_cast<bf16x8*>(dst) = v;
+      }
     }
+  } else if (col_valid) {
+    uint16_t* orow = p.out + ((static_cast<int64_t>(b) * S + pos) * p.hq + head) * D + dlo;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) *reinterpret_cast<u32x2*>(orow + db * 32 + a * 8 + h * 4) = out_pair(db, a);
+    }
+  }
+  if (col_valid && p.lse && h == 0 && dlo == 0) {
+    p.lse[(static_cast<int64_t>(b) * p.hq + head) * S + pos] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
