@@ -155,6 +155,37 @@ def test_prefill_instantiations(gpu, D, g, keqv, cap, W):
     assert_close(from_dev_f64(lse), rl, what=f"D{D} g{g} lse")
 
 
+@pytest.mark.parametrize("D,g,keqv,cap,S", [(64, 1, False, 0.0, 163), (64, 4, True, 50.0, 163), (256, 2, False, 50.0, 163),
+                                             (256, 16, True, 0.0, 97), (512, 16, True, 0.0, 163),
+                                             (512, 2, False, 50.0, 1), (256, 4, False, 0.0, 1)])
+def test_prefill_writes_only_its_output(gpu, D, g, keqv, cap, S):
+    """The output goes into a view of a larger buffer whose guard regions hold a
+    sentinel pattern: every guard byte stays unchanged (the last block runs past
+    S, so its columns beyond the sequence must not be written), and the view
+    matches a plain call bit for bit."""
+    import torch
+
+    ga = gpu
+    Hkv = 2 if g <= 4 else 1
+    kw = dict(num_heads=g * Hkv, num_kv_heads=Hkv, head_dim=D, sliding_window=0, sliding_window_pattern=0,
+              attn_logit_softcapping=cap, k_eq_v=keqv)
+    B = 2
+    print(f"[prefill guard] D={D} g={g} keqv={keqv} S={S}", flush=True)
+    q = to_dev_bf16(normal_bf16(510, (B, S, g * Hkv, D)))
+    k = to_dev_bf16(normal_bf16(511, (B, S, Hkv, D)))
+    v = None if keqv else to_dev_bf16(normal_bf16(512, (B, S, Hkv, D)))
+    n = B * S * g * Hkv * D
+    guard = 8192                                          # elements; keeps the view 16-byte aligned
+    big = torch.full((n + 2 * guard,), 0x5A5A, dtype=torch.int16, device="cuda")
+    out = big[guard:guard + n].view(torch.bfloat16).view(B, S, g * Hkv, D)
+    ga.attn_prefill(kw, 0, q, k, v, out=out)
+    ref = ga.attn_prefill(kw, 0, q, k, v)
+    torch.cuda.synchronize()
+    host = big.cpu().numpy()
+    assert (host[:guard] == 0x5A5A).all() and (host[guard + n:] == 0x5A5A).all(), "a guard element was written"
+    assert np.array_equal(host[guard:guard + n], from_dev_bf16_bits(ref).reshape(-1).view(np.int16))
+
+
 @pytest.mark.parametrize("scale", [8.0, 32.0])
 @pytest.mark.parametrize("kw,layer", [(GEMMA2, 0), (GEMMA2, 1), (GEMMA4, 5)])
 def test_prefill_peaked(gpu, kw, layer, scale):
