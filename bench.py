@@ -460,6 +460,15 @@ def main():
 
     torch.cuda.set_device(0)
     ga.load()
+    if a.calibrate_copy:
+        # three 1 GiB device copies: a known byte count for scaling the HBM counters
+        x = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+        torch.cuda.empty_cache()
     if a.workload in ("gemma3", "gemma4", "decode"):
         out = {}
         if a.workload == "gemma3":
@@ -499,12 +508,6 @@ def main():
         "prologue_ms": pair["prologue_ms"],
         "prefill_tflops": {k: round(v, 2) for k, v in pair["prefill_tflops"].items()},
     }
-    if a.calibrate_copy:
-        x = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
-        y = torch.empty_like(x)
-        for _ in range(3):
-            y.copy_(x)
-        torch.cuda.synchronize()
     if not a.no_extra and a.workload == "all":
         log("[bench] gemma3 stack / gemma4 global prefill")
         cfgs = {}
