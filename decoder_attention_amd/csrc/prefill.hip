@@ -382,8 +382,10 @@ void prefill_kernel(PrefillParams p) {
       // matrix instructions long.
       constexpr int kLA = kDS < 4 ? kDS : 4;
       bf16x8 a[kLA];
-      // Address bit 8 of kaddr is clear (the chunk bits are 4-7), so the step's
-      // top bit is an addition, which folds into the instruction's offset.
+      // From D = 256 up the row pitch is a multiple of 512 bytes and the chunk
+      // bits are 4-7 (plus the slice's bit 9 at D = 512), so bit 8 of kaddr is
+      // clear and the step's top bit is an addition, folded into the
+      // instruction's offset.  At D = 64 the steps never reach bit 8.
       auto kread = [&](int ds) -> bf16x8 {
         return *reinterpret_cast<const bf16x8*>(kbc + (kaddr ^ static_cast<uint32_t>((ds & 7) * 32)) + (ds >> 3) * 256);
       };
@@ -509,7 +511,8 @@ void prefill_kernel(PrefillParams p) {
         const int32_t r1 = r0 + 8;
         const uint32_t va0 = static_cast<uint32_t>(r0 * D * 2 + ((cl ^ swz<D>(r0)) << 4)) + rest;
         const uint32_t va1 = static_cast<uint32_t>(r1 * D * 2 + ((cl ^ swz<D>(r1)) << 4)) + rest;
-        // bit 8 of va0/va1 is clear: db's top bit is an offset addition
+        // as for K: bit 8 of va0/va1 is clear from D = 256 up, so db's top bit
+        // is an offset addition (at D = 64, db < 2 never reaches it)
         const uint32_t x = static_cast<uint32_t>((db & 3) * 64);
         const i16x4 a0 = lds_read_tr16(vbc + (va0 ^ x) + (db >> 2) * 256);
         const i16x4 a1 = lds_read_tr16(vbc + (va1 ^ x) + (db >> 2) * 256);
