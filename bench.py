@@ -212,7 +212,7 @@ def bench_pair(ga, steps, warmup):
         prefill_tflops={"local_w4096": flops[0] / (pre[0] * 1e-3) / 1e12, "global": flops[1] / (pre[1] * 1e-3) / 1e12},
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=_pair_traffic(),
-                      kernel="prefill_kernel<256,2,false,true>",
+                      kernel="prefill_kernel<256,2,false,true,WIDE>: local WIDE=false (4 waves), global WIDE=true (8)",
                       flops_per_launch={"local_w4096": flops[0], "global": flops[1]},
                       avg_launch_ms={"local_w4096": round(pre[0], 4), "global": round(pre[1], 4)}),
         layers=layers,

@@ -165,25 +165,28 @@ constexpr int waves_per_simd() {
 }
 
 // Waves per workgroup: four, one per SIMD; with two waves per SIMD two
-// workgroups share a CU.  One workgroup of eight with a three-tile ring
-// measured 2% faster on global layers but 14% slower on a 4096-key window.
-template <int D, bool KEQV>
+// workgroups share a CU.  WIDE: one workgroup of eight (two per SIMD) with a
+// three-tile ring, every K/V tile serving twice the columns.  On a
+// soft-capped global layer of width 256 it measured 4.6% faster (Gemma-2
+// pair, 935 against 894 TFLOP/s); on a 4096-key window it was 16% slower and
+// without the cap about even, so it is taken only for the first.
+template <int D, bool KEQV, bool WIDE>
 constexpr int pf_waves() {
-  return 4;
+  return WIDE ? 8 : 4;
 }
 
-template <int D, int G, bool KEQV>
+template <int D, int G, bool KEQV, bool WIDE>
 constexpr int positions_per_block() {
-  return (pf_waves<D, KEQV>() / DSplit<D>::value) * kCols / G;
+  return (pf_waves<D, KEQV, WIDE>() / DSplit<D>::value) * kCols / G;
 }
 
-template <int D, int G, bool KEQV, bool CAP>
-__global__ __launch_bounds__((pf_waves<D, KEQV>() * 64)) __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, KEQV>(), 2)))
+template <int D, int G, bool KEQV, bool CAP, bool WIDE>
+__global__ __launch_bounds__((pf_waves<D, KEQV, WIDE>() * 64)) __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, KEQV>(), 2)))
 void prefill_kernel(PrefillParams p) {
-  constexpr int kWaves = pf_waves<D, KEQV>();
+  constexpr int kWaves = pf_waves<D, KEQV, WIDE>();
   constexpr int kSplit = DSplit<D>::value;
   constexpr int kDW = D / kSplit;            // D slice of one wave
-  constexpr int kP = positions_per_block<D, G, KEQV>();
+  constexpr int kP = positions_per_block<D, G, KEQV, WIDE>();
   constexpr int kDS = kDW / 16;              // k-steps of QK^T per wave
   constexpr int kDB = kDW / 32;              // 32-row blocks of O^T per wave
   constexpr int kRowChunks = D / 8;          // 16-byte chunks per key row
@@ -612,9 +615,9 @@ void prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int D, int G, bool KEQV, bool CAP>
+template <int D, int G, bool KEQV, bool CAP, bool WIDE = false>
 hipError_t launch_t(const PrefillArgs& a, const PrefillParams& prm, hipStream_t stream) {
-  constexpr int kP = positions_per_block<D, G, KEQV>();
+  constexpr int kP = positions_per_block<D, G, KEQV, WIDE>();
   PrefillParams pp = prm;
   pp.n_qblocks = (a.seq + kP - 1) / kP;
   const int32_t npairs = a.batch * a.hkv;
@@ -626,8 +629,8 @@ hipError_t launch_t(const PrefillArgs& a, const PrefillParams& prm, hipStream_t 
   pp.n_qblocks_pad = pad;
   const int64_t blocks = static_cast<int64_t>(npairs) * pad;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, G, KEQV, CAP>), dim3(static_cast<uint32_t>(blocks)), dim3(pf_waves<D, KEQV>() * 64), 0,
-                     stream, pp);
+  hipLaunchKernelGGL((prefill_kernel<D, G, KEQV, CAP, WIDE>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(pf_waves<D, KEQV, WIDE>() * 64), 0, stream, pp);
   return hipGetLastError();
 }
 
@@ -635,6 +638,10 @@ template <int D, int G>
 hipError_t dispatch_flags(const PrefillArgs& a, const PrefillParams& prm, hipStream_t s) {
   const bool cap = a.softcap > 0.0;
   if (a.k_eq_v) return cap ? launch_t<D, G, true, true>(a, prm, s) : launch_t<D, G, true, false>(a, prm, s);
+  if constexpr (D == 256) {
+    const bool global = a.window <= 0 || a.window >= a.seq;
+    if (cap && global) return launch_t<D, G, false, true, true>(a, prm, s);
+  }
   return cap ? launch_t<D, G, false, true>(a, prm, s) : launch_t<D, G, false, false>(a, prm, s);
 }
 
