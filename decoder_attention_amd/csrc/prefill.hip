@@ -10,6 +10,9 @@
 //   holds half of Q^T and O^T, computes a partial S^T over its half and the
 //   pair exchanges the partials through LDS (fp32 a+b == b+a, so both waves
 //   see the same scores bit for bit).  A workgroup then covers 64 columns.
+//   Soft-capped global layers of width 256 take the WIDE form: eight waves
+//   (256 columns) in one workgroup per CU, each staged tile serving twice the
+//   query rows.
 //
 // Block order
 //   The dispatcher deals linear block ids round-robin over the 8 XCDs, each
