@@ -228,12 +228,15 @@ void prefill_kernel(PrefillParams p) {
     else return v_lds2;
   };
   // After the last tile the ring arrays hold each wave's output slice
-  // (32 columns x kDW) on its way to memory: array n of the ring (K slots,
-  // then V slots) holds kStagePer slices.
-  constexpr int kStageBytes = kCols * kDW * 2;
-  constexpr int kStagePer = kTileElems * 2 / kStageBytes;
+  // (32 columns x kDW) on its way to memory, whole or, where the ring is too
+  // small for every wave's slice, half of it per pass: array n of the ring
+  // (K slots, then V slots) holds kSlicePer of them.
   constexpr int kRingArrays = KEQV ? kBufs : 2 * kBufs;
-  constexpr bool kStageO = kStagePer >= 1 && kRingArrays * kStagePer >= kWaves;
+  constexpr int kWhole = kCols * kDW * 2;
+  constexpr int kPasses = kRingArrays * (kTileElems * 2 / kWhole) >= kWaves ? 1 : 2;
+  constexpr int kSlice = kWhole / kPasses;
+  constexpr int kSlicePer = kTileElems * 2 / kSlice;
+  constexpr bool kStageO = kSlicePer >= 1 && kRingArrays * kSlicePer >= kWaves && kDB % kPasses == 0;
   auto stage_region = [&](int n) -> uint16_t* {
     if (n == 0) return k_lds0;
     if constexpr (kBufs > 2) {
@@ -574,36 +577,43 @@ void prefill_kernel(PrefillParams p) {
   if constexpr (kStageO) {
     // The accumulators hold O^T: a lane owns one column and 8-byte pieces of
     // its row, so stores straight from them would write 16 bytes into each
-    // of 32 rows per instruction.  Instead each wave parks its slice in its
-    // own region of the (now idle) ring, then reads it back in row order and
-    // writes whole 16-byte chunks: one instruction covers 1 KB of rows.
+    // of 32 rows per instruction.  Instead each wave parks its slice (or half
+    // of it per pass) in its own region of the now idle ring, then reads it
+    // back in row order and writes whole 16-byte chunks: one instruction
+    // covers 1 KB of rows.
     wait_vmcnt<0>();
     __syncthreads();                 // every wave is done with the ring
-    char* st = reinterpret_cast<char*>(stage_region(wave / kStagePer)) + (wave % kStagePer) * kStageBytes;
-    constexpr int kRowCh = kDW / 8;  // 16-byte chunks per staged row
+    char* st = reinterpret_cast<char*>(stage_region(wave / kSlicePer)) + (wave % kSlicePer) * kSlice;
+    constexpr int kRowCh = kDW / 8 / kPasses;   // 16-byte chunks per staged row
     constexpr int kSwz = (kRowCh < 16 ? kRowCh : 16) - 1;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int32_t ch = (db * 4 + a) ^ (j & kSwz);
-        *reinterpret_cast<u32x2*>(st + j * (kDW * 2) + ch * 16 + h * 8) = out_pair(db, a);
-      }
-    }
-    __syncthreads();
+    constexpr int kPassDB = kDB / kPasses;
     const int32_t ln = lane_id_here();
 #pragma unroll
-    for (int i = 0; i < kCols * kRowCh / 64; ++i) {
-      const int32_t q = i * 64 + ln;
-      const int32_t col = q / kRowCh;
-      const int32_t dc = q % kRowCh;
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + col * (kDW * 2) + ((dc ^ (col & kSwz)) * 16));
-      const int32_t cc = cw * kCols + col;
-      const int32_t cpos = p0 + cc / G;
-      if (cpos < S) {
-        uint16_t* dst = p.out + ((static_cast<int64_t>(b) * S + cpos) * p.hq + kvh * G + cc % G) * D + dlo + dc * 8;
-        *reinterpret_cast<bf16x8*>(dst) = v;
+    for (int hp = 0; hp < kPasses; ++hp) {
+#pragma unroll
+      for (int db = 0; db < kPassDB; ++db) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int32_t ch = (db * 4 + a) ^ (j & kSwz);
+          *reinterpret_cast<u32x2*>(st + j * (kRowCh * 16) + ch * 16 + h * 8) = out_pair(hp * kPassDB + db, a);
+        }
       }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kCols * kRowCh / 64; ++i) {
+        const int32_t q = i * 64 + ln;
+        const int32_t col = q / kRowCh;
+        const int32_t dc = q % kRowCh;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + col * (kRowCh * 16) + ((dc ^ (col & kSwz)) * 16));
+        const int32_t cc = cw * kCols + col;
+        const int32_t cpos = p0 + cc / G;
+        if (cpos < S) {
+          uint16_t* dst = p.out + ((static_cast<int64_t>(b) * S + cpos) * p.hq + kvh * G + cc % G) * D + dlo +
+                          hp * (kDW / kPasses) + dc * 8;
+          *reinterpret_cast<bf16x8*>(dst) = v;
+        }
+      }
+      if (kPasses > 1) __syncthreads();   // the next pass rewrites the region
     }
   } else if (col_valid) {
     uint16_t* orow = p.out + ((static_cast<int64_t>(b) * S + pos) * p.hq + head) * D + dlo;
