@@ -186,6 +186,32 @@ def test_prefill_writes_only_its_output(gpu, D, g, keqv, cap, S):
     assert np.array_equal(host[guard:guard + n], from_dev_bf16_bits(ref).reshape(-1).view(np.int16))
 
 
+@pytest.mark.parametrize("g", [1, 2, 4, 16])
+def test_prefill_eight_and_four_wave_forms_agree(gpu, g):
+    """A soft-capped layer of width 256 whose window reaches the whole sequence
+    (W = S) runs the eight-wave form; W = S - 1 runs the four-wave form and
+    masks only key 0 for the last row.  Every column visits the same tiles in
+    the same key order in both, so all other rows agree bit for bit."""
+    ga = gpu
+    Hkv = 2 if g <= 4 else 1
+    B, S, D = 2, 300, 256
+    print(f"[prefill forms] g={g} S={S}", flush=True)
+    q = to_dev_bf16(normal_bf16(520, (B, S, g * Hkv, D), scale=2.0))
+    k = to_dev_bf16(normal_bf16(521, (B, S, Hkv, D)))
+    v = to_dev_bf16(normal_bf16(522, (B, S, Hkv, D)))
+    outs = []
+    for W in (S, S - 1):
+        kw = dict(num_heads=g * Hkv, num_kv_heads=Hkv, head_dim=D, sliding_window=W, sliding_window_pattern=0,
+                  attn_logit_softcapping=50.0)
+        outs.append(ga.attn_prefill(kw, 0, q, k, v, want_lse=True))
+    (o8, l8), (o4, l4) = outs
+    a8, a4 = from_dev_bf16_bits(o8), from_dev_bf16_bits(o4)
+    assert np.array_equal(a8[:, :S - 1], a4[:, :S - 1])
+    assert not np.array_equal(a8[:, S - 1], a4[:, S - 1])     # key 0 is masked only in the windowed form
+    lw8, lw4 = from_dev_f64(l8), from_dev_f64(l4)
+    assert np.array_equal(lw8[:, :, :S - 1], lw4[:, :, :S - 1])
+
+
 @pytest.mark.parametrize("scale", [8.0, 32.0])
 @pytest.mark.parametrize("kw,layer", [(GEMMA2, 0), (GEMMA2, 1), (GEMMA4, 5)])
 def test_prefill_peaked(gpu, kw, layer, scale):
