@@ -225,8 +225,11 @@ def qk_prologue(cfg, layer_idx, q, k=None, q_out=None, k_out=None, q_norm_w=None
         _expect(k, (B, S, L["num_kv_heads"], L["head_dim"]), "k")
     if q_out is None:
         q_out = torch.empty_like(q)
+    _expect(q_out, tuple(q.shape), "q_out")
     if k is not None and k_out is None:
         k_out = torch.empty_like(k)
+    if k is not None:
+        _expect(k_out, tuple(k.shape), "k_out")
     for w, n in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
         if w is not None:
             _expect(w, (L["head_dim"],), n)
@@ -298,8 +301,11 @@ def attn_decode(cfg, layer_idx, q, k_cache, v_cache, ctx_len, out=None, lse=None
     _expect(ctx_len, (B,), "ctx_len")
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, tuple(q.shape), "out")
     if want_lse and lse is None:
         lse = torch.empty((B, cfg.num_heads), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, (B, cfg.num_heads), "lse")
     need = decode_workspace_size(cfg, layer_idx, B, Smax)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -333,10 +339,15 @@ def attn_decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len, out=None, ls
     if v_cache is not None and not L["k_eq_v"]:
         _expect(v_cache, (B, Smax, L["num_kv_heads"], L["head_dim"]), "v_cache")
     _expect(ctx_len, (B,), "ctx_len")
+    if kv_start is not None:
+        _expect(kv_start, (B,), "kv_start")
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, tuple(q.shape), "out")
     if want_lse and lse is None:
         lse = torch.empty((B, cfg.num_heads, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, (B, cfg.num_heads, Lq), "lse")
     need = decode_multi_workspace_size(cfg, layer_idx, B, Lq, Smax)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -370,6 +381,7 @@ def qk_prologue_cache(cfg, layer_idx, q, k, v, k_cache, v_cache, ctx_len, q_out=
     _expect(ctx_len, (B,), "ctx_len")
     if q_out is None:
         q_out = torch.empty_like(q)
+    _expect(q_out, tuple(q.shape), "q_out")
     bf = torch.bfloat16
     rc = load().gemma_qk_prologue_cache(
         ctypes.byref(cfg.to_c()), int(layer_idx), B, Lq, Smax, _ptr(q, bf, "q"), _ptr(k, bf, "k"),
@@ -399,10 +411,15 @@ def attn_decode_int8(cfg, layer_idx, q, k_codes, k_scales, v_codes, v_scales, ct
         _expect(v_codes, (B, Smax, Hkv, D), "v_codes")
         _expect(v_scales, (B, Hkv, Smax), "v_scales")
     _expect(ctx_len, (B,), "ctx_len")
+    if kv_start is not None:
+        _expect(kv_start, (B,), "kv_start")
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, tuple(q.shape), "out")
     if want_lse and lse is None:
         lse = torch.empty((B, cfg.num_heads, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, (B, cfg.num_heads, Lq), "lse")
     need = decode_multi_workspace_size(cfg, layer_idx, B, Lq, Smax)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -440,6 +457,7 @@ def qk_prologue_cache_int8(cfg, layer_idx, q, k, v, k_codes, k_scales, v_codes, 
     _expect(ctx_len, (B,), "ctx_len")
     if q_out is None:
         q_out = torch.empty_like(q)
+    _expect(q_out, tuple(q.shape), "q_out")
     bf = torch.bfloat16
     rc = load().gemma_qk_prologue_cache_int8(
         ctypes.byref(cfg.to_c()), int(layer_idx), B, Lq, Smax, _ptr(q, bf, "q"), _ptr(k, bf, "k"),

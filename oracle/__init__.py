@@ -31,6 +31,8 @@ from .gemma_ref import (  # noqa: F401
     resolve_layer,
     rms_norm,
     rotary,
+    rotary_zero_pad,
+    ROTARY_LAYOUTS,
     rotary_inv_freq,
     round_bf16,
     softcap,

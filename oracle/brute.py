@@ -47,13 +47,29 @@ def _rope(vec, pos, theta, r):
     return out
 
 
+def _rope_zero_pad(vec, pos, theta, r):
+    """Zero-padded frequencies over the whole width: pair (j, j + D/2) turns
+    by pos * theta^(-2j/D) for j < r/2 and stays put for larger j."""
+    out = list(vec)
+    n = len(vec)
+    for j in range(n // 2):
+        if j >= r // 2:
+            continue
+        z = complex(vec[j], vec[j + n // 2]) * cmath.exp(1j * pos * theta ** (-(2.0 * j) / n))
+        out[j], out[j + n // 2] = z.real, z.imag
+    return out
+
+
 def brute_layer(p: dict, layer_idx, q, k, v=None, q_norm_w=None, k_norm_w=None, pos0=None, keep=None):
     """Whole layer (QK-norm, rotary, attention) for tiny shapes.
 
     ``p`` uses the pages' knob names (same meaning as the oracle's config).
     ``keep`` (optional, [B][S] of 0/1) is an attention mask: a position with 0
     is neither a query (its output row is 0, lse -inf) nor a key.
+    ``p["rotary_layout"]`` "zero_pad" takes the zero-padded reading of partial
+    rotary (default "first": the first r dims).
     """
+    rope = _rope_zero_pad if p.get("rotary_layout", "first") == "zero_pad" else _rope
     kind = layer_kind(p.get("sliding_window_pattern", 1), p.get("sliding_window", 0), layer_idx)
     pos_div = 1.0
     if kind == "global":
@@ -90,7 +106,7 @@ def brute_layer(p: dict, layer_idx, q, k, v=None, q_norm_w=None, k_norm_w=None, 
             vec = [float(x) for x in vec]
             if w is not None:
                 vec = _norm(vec, w, eps, off)
-            return _rope(vec, (base + s) / pos_div, theta, r)
+            return rope(vec, (base + s) / pos_div, theta, r)
 
         kk = [[prep(k[b][s][h], k_norm_w, s) for h in range(hkv)] for s in range(S)]
         vv = kk if tied else [[[float(x) for x in v[b][s][h]] for h in range(hkv)] for s in range(S)]

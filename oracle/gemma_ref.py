@@ -155,6 +155,38 @@ def rotary(x: np.ndarray, positions: np.ndarray, theta: float, rotary_dim: int) 
     return out
 
 
+def rotary_zero_pad(x: np.ndarray, positions: np.ndarray, theta: float, rotary_dim: int) -> np.ndarray:
+    """The other reading of partial rotary: a zero-padded frequency vector.
+
+    The Gemma 4 page ("Zero-pad partial rope") can also be read as rotating
+    every head vector over its full width D in rotate-half pairs (j, j + D/2),
+    with the frequencies of a full-width rotary, theta^(-2j/D), kept for the
+    first r/2 pairs and set to zero (no rotation) for the rest; r is the same
+    ``rotary_dim`` as in :func:`rotary`.  The rotated dims are then
+    [0, r/2) and [D/2, D/2 + r/2) instead of [0, r).  At r = D the two readings
+    are the same function.  ``x`` is [B, S, H, D], ``positions`` [B, S].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    D = x.shape[-1]
+    half = D // 2
+    n_rot = rotary_dim // 2
+    if n_rot == 0:
+        return out
+    j = np.arange(half, dtype=np.float64)
+    omega = np.where(j < n_rot, np.power(float(theta), -2.0 * j / float(D)), 0.0)
+    phi = np.asarray(positions, dtype=np.float64)[:, :, None, None] * omega  # [B,S,1,D/2]
+    c, s = np.cos(phi), np.sin(phi)
+    a = x[..., :half]
+    b = x[..., half:2 * half]
+    out[..., :half] = a * c - b * s
+    out[..., half:2 * half] = b * c + a * s
+    return out
+
+
+ROTARY_LAYOUTS = ("first", "zero_pad")
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Nearest bf16 value (8 significant bits, ties to even), returned as fp64.
 
@@ -199,13 +231,18 @@ def allowed(i: np.ndarray, j: np.ndarray, window: int) -> np.ndarray:
     return ok
 
 
-def prologue(cfg, layer_idx, q, k=None, q_norm_w=None, k_norm_w=None, pos0=None):
+def prologue(cfg, layer_idx, q, k=None, q_norm_w=None, k_norm_w=None, pos0=None, rotary_layout="first"):
     """QK-norm then rotary on q [B,S,Hq,D] and k [B,S,Hkv,D]; returns fp64 arrays.
 
     Positions are ``pos0[b] + s`` (``pos0`` defaults to zeros), divided by the
     layer's ``pos_div`` (rope scaling).  The norm is applied only when its
-    weight is given.  Values are never normed or rotated.
+    weight is given.  Values are never normed or rotated.  ``rotary_layout``
+    picks the reading of partial rotary: "first" (the first r dims, the
+    library's reading; :func:`rotary`) or "zero_pad" (:func:`rotary_zero_pad`).
     """
+    if rotary_layout not in ROTARY_LAYOUTS:
+        raise ValueError(f"rotary_layout must be one of {ROTARY_LAYOUTS}")
+    rot = rotary if rotary_layout == "first" else rotary_zero_pad
     L = resolve_layer(cfg, layer_idx)
     q = np.asarray(q, dtype=np.float64)
     B, S = q.shape[0], q.shape[1]
@@ -217,7 +254,7 @@ def prologue(cfg, layer_idx, q, k=None, q_norm_w=None, k_norm_w=None, pos0=None)
     def one(x, w):
         if w is not None:
             x = rms_norm(x, w, cfg.norm_eps, cfg.norm_weight_offset)
-        return rotary(x, positions, L["theta"], L["rotary_dim"])
+        return rot(x, positions, L["theta"], L["rotary_dim"])
 
     qo = one(q, q_norm_w)
     ko = None if k is None else one(np.asarray(k, dtype=np.float64), k_norm_w)

@@ -256,3 +256,54 @@ def test_decode_workspace_follows_the_kernel_choice(ga, q_len):
     line = B * max_ctx
     n_wg = max(1, min(max(256 * per_cu // rows, -(-line // 16384)), -(-line // 256)))
     assert need == _decode_ws_bytes(B, q_len, 16, 512, n_wg)
+
+
+# ----------------------------------------------------------------------------- binding: output shapes
+_G4 = dict(num_heads=16, num_kv_heads=8, num_global_kv_heads=1, head_dim=256, global_head_dim=512,
+           sliding_window=64, sliding_window_pattern=6, partial_rotary_factor=0.25, k_eq_v=True)
+
+
+def _bad_output_calls(ga):
+    """(name, call) pairs whose one wrongly shaped output must be refused.
+
+    The tensors live on the CPU: the binding checks every shape before it
+    takes a device pointer, so a refusal here happens before any launch."""
+    import torch
+
+    bf, B, S, L, Smax = torch.bfloat16, 2, 5, 3, 40
+    e = lambda *s, dt=bf: torch.empty(s, dtype=dt)            # noqa: E731
+    i32 = torch.int32
+    q, k = e(B, S, 16, 256), e(B, S, 8, 256)
+    qd, kc = e(B, 16, 512), e(B, Smax, 1, 512)
+    qm = e(B, L, 16, 512)
+    ctx = e(B, dt=i32)
+    codes, scales = e(B, Smax, 1, 512, dt=torch.int8), e(B, 1, Smax, dt=torch.float32)
+    kcl, vcl = e(B, Smax, 8, 256), e(B, Smax, 8, 256)
+    return [
+        ("prologue q_out", lambda: ga.qk_prologue(_G4, 0, q, k, q_out=e(B, S, 16, 128))),
+        ("prologue k_out", lambda: ga.qk_prologue(_G4, 0, q, k, k_out=e(B, S - 1, 8, 256))),
+        ("prefill out", lambda: ga.attn_prefill(_G4, 0, q, k, k, out=e(B, S, 8, 256))),
+        ("prefill lse", lambda: ga.attn_prefill(_G4, 0, q, k, k, lse=e(B, 16, S - 1, dt=torch.float32))),
+        ("decode out", lambda: ga.attn_decode(_G4, 5, qd, kc, None, ctx, out=e(B, 16, 256))),
+        ("decode lse", lambda: ga.attn_decode(_G4, 5, qd, kc, None, ctx, lse=e(B, 8, dt=torch.float32))),
+        ("decode_multi out", lambda: ga.attn_decode_multi(_G4, 5, qm, kc, None, ctx, out=e(B, L - 1, 16, 512))),
+        ("decode_multi lse", lambda: ga.attn_decode_multi(_G4, 5, qm, kc, None, ctx,
+                                                          lse=e(B, 16, L + 1, dt=torch.float32))),
+        ("decode_multi kv_start", lambda: ga.attn_decode_multi(_G4, 5, qm, kc, None, ctx, kv_start=e(B + 1, dt=i32))),
+        ("decode_int8 out", lambda: ga.attn_decode_int8(_G4, 5, qm, codes, scales, None, None, ctx,
+                                                        out=e(B, L, 16, 256))),
+        ("decode_int8 lse", lambda: ga.attn_decode_int8(_G4, 5, qm, codes, scales, None, None, ctx,
+                                                        lse=e(B, 16, dt=torch.float32))),
+        ("prologue_cache q_out", lambda: ga.qk_prologue_cache(_G4, 0, e(B, L, 16, 256), e(B, L, 8, 256),
+                                                              e(B, L, 8, 256), kcl, vcl, ctx,
+                                                              q_out=e(B, L, 8, 256))),
+        ("prologue_cache_int8 q_out", lambda: ga.qk_prologue_cache_int8(_G4, 5, qm, e(B, L, 1, 512), None, codes,
+                                                                        scales, None, None, ctx,
+                                                                        q_out=e(B, L, 16, 511))),
+    ]
+
+
+def test_binding_refuses_wrongly_shaped_outputs(ga):
+    for name, call in _bad_output_calls(ga):
+        with pytest.raises(ValueError, match="has shape"):
+            call()

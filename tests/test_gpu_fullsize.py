@@ -1,4 +1,4 @@
-"""GPU parity at the benchmark's own sizes and launches, on sampled outputs.
+"""GPU parity at the benchmark's own sizes and launches, on every output.
 
 The inputs are the benchmark's seeded tensors (bench.py builds them, the
 same calls launch the kernels), so every launch shape timed there is also
@@ -9,13 +9,17 @@ checked here:
   * decode: the Gemma-4-12B-shaped step over 64 ragged contexts of up to
     65536 rows (local layer window 1024, global layer D512), one new token,
     four new tokens, and the int8 cache.
-The oracle computes the sampled query rows one by one: each row's processed
-query from its raw bits at its own position, all keys of the layer, then the
-row's attention.  Outputs and lse are held to the attention tolerance
+The oracle recomputes every output: the prologue of the whole q and k
+tensors, then the attention of every query row (prefill) or of every
+sequence (decode).  Outputs and lse are held to the attention tolerance
 (max-abs 2e-2, mean-abs 2e-3), prologue outputs to one bf16 ulp, int8 codes
 and scales bit for bit.  Decode caches are NaN outside the rows a sequence
 may read, so a stray read shows as a non-finite output anywhere in the batch.
+The oracle runs in a pool of host threads with the BLAS library held to one
+thread per worker.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -24,34 +28,79 @@ from oracle import gemma_ref as R
 from synth import bf16_bits_to_f64, normal_bf16_row, seed_for
 from tests.gpu_util import assert_close, assert_within_one_ulp, from_dev_f64, to_dev
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
 PREFILL = [(f"{name}_layer{layer}", name, layer)
            for name, (_, _, layers, _, _, _) in bench.PREFILL_WORKLOADS.items() for layer in layers]
 
 
-def _sample_rows(B, S, Hq, W, seed, n_random=8):
-    """(b, head, i) rows: the first positions, tile edges, both sides of the
-    window edge, the last positions, and seeded random ones; heads and
-    sequences cycle so every GQA group member and sequence appears."""
-    rng = np.random.default_rng(seed)
-    pos = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, S // 2, S - 2, S - 1}
-    if W:
-        pos |= {W - 2, W - 1, W, W + 1}
-    pos |= set(int(x) for x in rng.integers(0, S, n_random))
-    pos = sorted(p for p in pos if 0 <= p < S)
-    return [(j % B, int((j * 5 + rng.integers(0, Hq)) % Hq), p) for j, p in enumerate(pos)]
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+
+    return threadpool_limits(limits=1)
+
+
+def _threads():
+    return min(16, len(os.sched_getaffinity(0)))
+
+
+def _chunks(S):
+    n = _threads()
+    step = max(1, -(-S // n))
+    return [(s0, min(S, s0 + step)) for s0 in range(0, S, step)]
+
+
+def _prologue_rows(cfg, layer, q, k, qw, kw):
+    """The oracle's prologue of [B,S,H,D] tensors, in position chunks on host
+    threads (a chunk starting at s0 takes positions s0, s0 + 1, ...)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    B, S = q.shape[0], q.shape[1]
+    rq = np.empty(q.shape)
+    rk = np.empty(k.shape)
+
+    def run(c):
+        s0, s1 = c
+        a, b = R.prologue(cfg, layer, bf16_bits_to_f64(q[:, s0:s1]), bf16_bits_to_f64(k[:, s0:s1]), qw, kw,
+                          pos0=[s0] * B)
+        rq[:, s0:s1] = a
+        rk[:, s0:s1] = b
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(run, _chunks(S)))
+    return rq, rk
+
+
+def _rowwise(fn, x, *more):
+    """fn applied to position chunks of [B,S,...] arrays on host threads (fn is row-wise)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    chunks = _chunks(x.shape[1])
+    with ThreadPoolExecutor(_threads()) as ex:
+        return list(ex.map(lambda c: fn(x[:, c[0]:c[1]], *(m[:, c[0]:c[1]] for m in more)), chunks)), chunks
+
+
+def _round_bf16(x):
+    parts, chunks = _rowwise(R.round_bf16, x)
+    out = np.empty(x.shape)
+    for (s0, s1), p in zip(chunks, parts):
+        out[:, s0:s1] = p
+    return out
+
+
+def _within_one_ulp(got, ref, what):
+    _rowwise(lambda a, b: assert_within_one_ulp(a, b, what=what), got, ref)
 
 
 @pytest.mark.parametrize("case,workload,layer", PREFILL, ids=[p[0] for p in PREFILL])
-def test_prefill_full_size_sampled(gpu, case, workload, layer):
+def test_prefill_full_size_every_row(gpu, case, workload, layer):
     ga = gpu
     import torch
 
     cfg_id, kw, _, B, S, norm = bench.PREFILL_WORKLOADS[workload]
     cfg = R.GemmaAttnConfig(**kw)
     L = R.resolve_layer(cfg, layer)
-    Hq, W = cfg.num_heads, L["window"]
+    W = L["window"]
     print(f"[fullsize] {case}: B={B} S={S} D={L['head_dim']} window={W}", flush=True)
     h = bench.layer_inputs(cfg_id, kw, layer, B, S, norm)
     t = bench.layer_tensors(cfg_id, kw, layer, B, S, norm, host=h)
@@ -59,32 +108,32 @@ def test_prefill_full_size_sampled(gpu, case, workload, layer):
     out2, lse = ga.attn_prefill(kw, layer, t["qt"], t["kt"], t["v"], want_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), t["out"].view(torch.int16)), "lse request changed the output"
-
-    rows = _sample_rows(B, S, Hq, W, seed=cfg_id * 100 + layer)
-    bi = torch.tensor([r[0] for r in rows], device="cuda")
-    hi = torch.tensor([r[1] for r in rows], device="cuda")
-    ii = torch.tensor([r[2] for r in rows], device="cuda")
-    got_q = from_dev_f64(t["qt"][bi, ii, hi])
-    got_o = from_dev_f64(t["out"][bi, ii, hi])
-    got_l = from_dev_f64(lse[bi, hi, ii])
+    del out2
+    got_q = from_dev_f64(t["qt"])
     got_k = from_dev_f64(t["kt"])
-    del t, out2, lse
+    got_o = from_dev_f64(t["out"])
+    got_l = from_dev_f64(lse)
+    del t, lse
     torch.cuda.empty_cache()
 
-    # oracle: each sampled query row processed alone at its own position
-    ref_q = np.stack([R.prologue(cfg, layer, bf16_bits_to_f64(h["q"][b, i][None, None]), None, h["qw"], None,
-                                 pos0=[i])[0][0, 0, hq] for b, hq, i in rows])
-    # keys: the prologue of the whole key tensor (its norm weight, positions 0..S-1)
-    ref_k = R.prologue(cfg, layer, bf16_bits_to_f64(h["k"]), None, h["kw"], None)[0]
-    assert_within_one_ulp(got_q, ref_q, what=case + " q rows")
-    assert_within_one_ulp(got_k, ref_k, what=case + " k")
-    del got_k
+    # oracle: the prologue of the whole tensors (positions 0..S-1), then every row's attention
+    ref_q, ref_k = _prologue_rows(cfg, layer, h["q"], h["k"], h["qw"], h["kw"])
+    _within_one_ulp(got_q, ref_q, what=case + " q")
+    _within_one_ulp(got_k, ref_k, what=case + " k")
+    del got_q, got_k
     v = None if L["k_eq_v"] else bf16_bits_to_f64(h["v"])
+    del h
     # the processed q and k cross the library boundary as bf16
-    ro, rl = R.prefill_rows(cfg, layer, R.round_bf16(ref_q), R.round_bf16(ref_k), v, rows)
+    rq, rk = _round_bf16(ref_q), _round_bf16(ref_k)
+    del ref_q, ref_k
+    block = 64 if L["head_dim"] > 256 or S > 16384 else 256     # bounds the oracle's score blocks
+    with _one_blas_thread():
+        ro, rl = R.prefill(cfg, layer, rq, rk, v, block_rows=block, threads=_threads())
+    del rq, rk, v
     mx, mn = assert_close(got_o, ro, what=case)
     assert_close(got_l, rl, what=case + " lse")
-    print(f"[fullsize] {case}: {len(rows)} rows, max-abs {mx:.2e} mean-abs {mn:.2e}", flush=True)
+    print(f"[fullsize] {case}: {got_o.shape[0] * got_o.shape[1] * got_o.shape[2]} rows, max-abs {mx:.2e} "
+          f"mean-abs {mn:.2e}", flush=True)
 
 
 class _Spans:
@@ -103,20 +152,24 @@ class _Spans:
 
 
 def _decode_oracle_caches(layer, ctx, sel):
-    """The sampled sequences' cache rows, drawn on the host from the same
+    """The selected sequences' cache rows, drawn on the host from the same
     seeded streams that fill the device caches: (spans, bf16 bits per tensor)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     L = R.resolve_layer(R.GemmaAttnConfig(**bench.GEMMA4_12B), layer)
     Hkv, D, W = L["num_kv_heads"], L["head_dim"], L["window"]
     spans = [bench.decode_span(ctx[b], W) for b in sel]
     bits = {}
     for tensor in (("k",) if L["k_eq_v"] else ("k", "v")):
         seed = seed_for(5, layer, tensor)
-        bits[tensor] = [normal_bf16_row(seed, int(b), (hi - lo, Hkv, D)) for b, (lo, hi) in zip(sel, spans)]
+        with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+            bits[tensor] = list(ex.map(lambda a: normal_bf16_row(seed, int(a[0]), (a[1][1] - a[1][0], Hkv, D)),
+                                       zip(sel, spans)))
     return spans, bits
 
 
 @pytest.mark.parametrize("layer", [0, 5], ids=["local_w1024", "global_keqv_d512"])
-def test_decode_full_size_sampled(gpu, layer):
+def test_decode_full_size_every_sequence(gpu, layer):
     ga = gpu
     import torch
 
@@ -125,10 +178,8 @@ def test_decode_full_size_sampled(gpu, layer):
     L = R.resolve_layer(cfg, layer)
     B, Smax, D, Lq = bench.DECODE_B, bench.DECODE_SMAX, L["head_dim"], bench.DECODE_MULTI
     ctx = bench.decode_contexts()
-    rng = np.random.default_rng(50 + layer)
-    sel = sorted({int(np.argmin(ctx)), int(np.argmax(ctx))} | set(int(x) for x in rng.choice(B, 4, replace=False)))
-    print(f"[fullsize] decode layer {layer}: B={B} Smax={Smax} D={D} sampled {sel} ctx {ctx[sel].tolist()}",
-          flush=True)
+    sel = list(range(B))
+    print(f"[fullsize] decode layer {layer}: B={B} Smax={Smax} D={D} ctx {ctx.min()}..{ctx.max()}", flush=True)
 
     # the timed launches, in the timed configuration
     kc, vc = bench.decode_caches(ga, layer, ctx)
@@ -161,8 +212,8 @@ def test_decode_full_size_sampled(gpu, layer):
     del kc, vc, kq, ksq, vq, vsq, out, out_l, outm, out8, ws, wsm
     torch.cuda.empty_cache()
 
-    assert _decode_oracle_caches(layer, ctx, sel)[0] == spans
-    bits = _decode_oracle_caches(layer, ctx, sel)[1]
+    o_spans, bits = _decode_oracle_caches(layer, ctx, sel)
+    assert o_spans == spans
     f64 = {t: [bf16_bits_to_f64(x) for x in xs] for t, xs in bits.items()}
     kc_o = _Spans(spans, f64["k"])
     vc_o = None if L["k_eq_v"] else _Spans(spans, f64["v"])

@@ -447,3 +447,90 @@ def test_ragged_mutant_is_caught(monkeypatch):
     with pytest.raises(AssertionError):
         test_prefill_ragged_matches_brute_force_mask(0, 0.0, False)
     monkeypatch.setattr(R, "prefill_ragged", orig)
+
+
+# --------------------------------------------------------------------------- the zero-pad rotary reading
+# The Gemma 4 page's "Zero-pad partial rope" has two plain readings (the
+# library takes the first): rotate the first r dims in pairs (i, i + r/2) at
+# theta^(-2i/r), or rotate the full width in pairs (j, j + D/2) at the
+# full-width frequencies theta^(-2j/D) with all but the first r/2 set to 0.
+@pytest.mark.parametrize("layer,f", [(0, 0.25), (0, 0.5), (2, 0.25), (2, 0.75), (0, 1.0), (2, 0.0)])
+def test_zero_pad_rotary_matches_brute_force(layer, f):
+    cfg = R.GemmaAttnConfig(num_heads=4, num_kv_heads=2, head_dim=8, num_global_kv_heads=1,
+                            global_head_dim=16, sliding_window=4, sliding_window_pattern=3,
+                            rope_theta=1e6, rope_local_theta=1e4, partial_rotary_factor=f,
+                            k_eq_v=True, norm_weight_offset=0, attn_logit_softcapping=3.0)
+    Lr = R.resolve_layer(cfg, layer)
+    D, Hkv = Lr["head_dim"], Lr["num_kv_heads"]
+    B, S = 2, 9
+    q, k, v = _inputs(19, B, S, 4, Hkv, D, qscale=2.0)
+    qw, kw = norm_weight(7, D), norm_weight(8, D)
+    pos0 = np.array([3, 1000])
+    qt, kt = R.prologue(cfg, layer, q, k, qw, kw, pos0, rotary_layout="zero_pad")
+    o, l = R.prefill(cfg, layer, qt, kt, v, block_rows=4)
+    p = _cfg_dict(cfg) | dict(rotary_layout="zero_pad")
+    ob, lb = brute_layer(p, layer, q.tolist(), k.tolist(), v.tolist(), qw.tolist(), kw.tolist(), pos0.tolist())
+    assert np.abs(o - np.array(ob)).max() < TOL
+    assert np.abs(l - np.array(lb)).max() < TOL
+
+
+def test_zero_pad_rotary_closed_forms():
+    D, r, theta = 16, 4, 1e4
+    x = bf16_bits_to_f64(normal_bf16(41, (1, 3, 2, D)))
+    pos = np.array([[0, 7, 300]])
+    y = R.rotary_zero_pad(x, pos, theta, r)
+    # position 0 is the identity; only dims [0, r/2) and [D/2, D/2 + r/2) move
+    assert np.array_equal(y[:, 0], x[:, 0])
+    moved = np.any(y != x, axis=(0, 1, 2))
+    assert moved.tolist() == [d < r // 2 or D // 2 <= d < D // 2 + r // 2 for d in range(D)]
+    # each pair (j, j + D/2) keeps its norm; pair 0 turns by p (frequency 1),
+    # pair 1 by p * theta^(-2/D)
+    a, b = x[..., :D // 2], x[..., D // 2:]
+    ya, yb = y[..., :D // 2], y[..., D // 2:]
+    assert np.abs(np.hypot(ya, yb) - np.hypot(a, b)).max() < 1e-12
+    e = np.zeros((1, 1, 1, D))
+    e[..., 1] = 1.0
+    z = R.rotary_zero_pad(e, np.array([[5]]), theta, r)
+    w = 5.0 * theta ** (-2.0 / D)
+    assert abs(z[0, 0, 0, 1] - math.cos(w)) < 1e-15 and abs(z[0, 0, 0, 1 + D // 2] - math.sin(w)) < 1e-15
+
+
+def test_rotary_readings_agree_at_full_width_and_differ_when_partial():
+    x = bf16_bits_to_f64(normal_bf16(42, (2, 5, 3, 32)))
+    pos = np.array([[0, 1, 2, 3, 4], [9, 10, 11, 12, 13]])
+    assert np.array_equal(R.rotary(x, pos, 1e6, 32), R.rotary_zero_pad(x, pos, 1e6, 32))
+    for r in (2, 8, 16, 30):
+        a, b = R.rotary(x, pos, 1e6, r), R.rotary_zero_pad(x, pos, 1e6, r)
+        assert np.abs(a - b).max() > 1e-3, r
+    # the difference reaches the attention output of a partial layer (the
+    # Gemma-4-shaped global layer: r = 128 of 512)
+    cfg = R.GemmaAttnConfig(num_heads=2, num_kv_heads=1, head_dim=512, partial_rotary_factor=0.25, k_eq_v=True)
+    q, k, _ = _inputs(43, 1, 24, 2, 1, 512)
+    o1, _ = R.prefill(cfg, 0, *R.prologue(cfg, 0, q, k, pos0=[100]))
+    o2, _ = R.prefill(cfg, 0, *R.prologue(cfg, 0, q, k, pos0=[100], rotary_layout="zero_pad"))
+    assert np.abs(o1 - o2).max() > 1e-3
+
+
+def test_zero_pad_mutant_is_caught(monkeypatch):
+    """Frequencies over r instead of D (the first reading's) fail the brute force."""
+    def wrong(x, positions, theta, rotary_dim):
+        x = np.asarray(x, dtype=np.float64)
+        out = x.copy()
+        D = x.shape[-1]
+        j = np.arange(D // 2, dtype=np.float64)
+        omega = np.where(j < rotary_dim // 2, np.power(theta, -2.0 * j / rotary_dim), 0.0)
+        phi = np.asarray(positions, dtype=np.float64)[:, :, None, None] * omega
+        a, b = x[..., :D // 2], x[..., D // 2:]
+        out[..., :D // 2] = a * np.cos(phi) - b * np.sin(phi)
+        out[..., D // 2:] = b * np.cos(phi) + a * np.sin(phi)
+        return out
+
+    cfg = R.GemmaAttnConfig(num_heads=2, num_kv_heads=1, head_dim=16, partial_rotary_factor=0.5)
+    q, k, v = _inputs(44, 1, 7, 2, 1, 16)
+    p = _cfg_dict(cfg) | dict(rotary_layout="zero_pad")
+    ob, _ = brute_layer(p, 0, q.tolist(), k.tolist(), v.tolist(), pos0=[50])
+    o, _ = R.prefill(cfg, 0, *R.prologue(cfg, 0, q, k, pos0=[50], rotary_layout="zero_pad"), v)
+    assert np.abs(o - np.array(ob)).max() < TOL
+    monkeypatch.setattr(R, "rotary_zero_pad", wrong)
+    om, _ = R.prefill(cfg, 0, *R.prologue(cfg, 0, q, k, pos0=[50], rotary_layout="zero_pad"), v)
+    assert np.abs(om - np.array(ob)).max() > 1e-3
