@@ -67,6 +67,7 @@ struct DecodeParams {
   int32_t batch, max_ctx, hq, hkv, window, n_wg;   // n_wg: workgroups per (KV head, column block)
   int32_t per_seq;            // workgroup w takes sequence w whole (n_wg = batch)
   int32_t q_len, n_cb;        // query tokens per sequence; 16-column blocks per KV head
+  int32_t xcd_log2;           // the dispatcher deals linear block ids round-robin over 2^xcd_log2 XCDs
   float scale_log2, cap_in2, cap_log2;
 };
 
@@ -133,30 +134,33 @@ __device__ __forceinline__ int64_t wg_of(int64_t x, int64_t total, int64_t n_wg)
 }
 
 // Block placement.  Work item (KV head, key range w) is kvh + Hkv * w; its
-// n_cb column blocks take linear ids 8 apart, so they run on one XCD (linear
-// ids are dealt round-robin to the 8 XCDs) at about the same time, and that
-// XCD's L2 serves the cache rows they all read.  With one column block the
-// order is the item order: the KV heads of one range side by side.
+// n_cb column blocks take linear ids nx apart (nx = the XCD count), so they run
+// on one XCD (linear ids are dealt round-robin to the XCDs) at about the same
+// time, and that XCD's L2 serves the cache rows they all read.  With one
+// column block the order is the item order: the KV heads of one range side by
+// side.
 struct DecodeBlock {
   int32_t kvh, cb, w;
   bool valid;
 };
 __device__ __forceinline__ DecodeBlock decode_block(const DecodeParams& p) {
   const int32_t L = static_cast<int32_t>(blockIdx.x);
-  const int32_t per = 8 * p.n_cb;
+  const int32_t nx = 1 << p.xcd_log2;
+  const int32_t per = nx * p.n_cb;
   const int32_t g = L / per;
   const int32_t r = L - g * per;
-  const int32_t item = g * 8 + (r & 7);
+  const int32_t item = g * nx + (r & (nx - 1));
   DecodeBlock d;
   d.valid = item < p.hkv * p.n_wg;
   d.kvh = item % p.hkv;
   d.w = item / p.hkv;
-  d.cb = r >> 3;
+  d.cb = r >> p.xcd_log2;
   return d;
 }
-inline int64_t decode_grid(int32_t hkv, int32_t n_wg, int32_t n_cb) {
+inline int64_t decode_grid(int32_t hkv, int32_t n_wg, int32_t n_cb, int32_t xcd_log2) {
   const int64_t items = static_cast<int64_t>(hkv) * n_wg;
-  return n_cb == 1 ? items : (items + 7) / 8 * 8 * n_cb;
+  const int64_t nx = int64_t{1} << xcd_log2;
+  return n_cb == 1 ? items : (items + nx - 1) / nx * nx * n_cb;
 }
 
 // Calls f(b, s_lo, s_hi, ctx) for every sequence b that this workgroup's range
@@ -1326,8 +1330,7 @@ void decode_tile_kernel(DecodeParams p) {
 template <int D, int G, bool KEQV, bool CAP>
 hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t stream) {
   if (!a.per_seq) {   // the balanced ranges need the prefix sums of the spans
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, prm);
-    hipError_t e0 = hipGetLastError();
+    const hipError_t e0 = launch_kernel(decode_plan_kernel, dim3(1), dim3(kPlanThreads), stream, prm);
     if (e0 != hipSuccess) return e0;
   }
   // Three or more 16-column blocks per KV head (many query heads per KV
@@ -1339,32 +1342,30 @@ hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t st
   DecodeParams pp = prm;
   if (wide) pp.n_cb = (prm.n_cb + kCBW - 1) / kCBW;
   if (tile) pp.n_cb = (a.group * a.q_len + 63) / 64;   // 64-column groups
-  const int64_t nblocks = decode_grid(a.hkv, a.n_wg, pp.n_cb);
-  if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t nblocks = decode_grid(a.hkv, a.n_wg, pp.n_cb, pp.xcd_log2);
+  if (nblocks > 0x7fffffff) return hipErrorNotSupported;
   const dim3 grid(static_cast<uint32_t>(nblocks), 1u, 1u);
+  hipError_t e = hipSuccess;
   if (tile) {
     if constexpr (D == 512 && KEQV) {
-      hipLaunchKernelGGL((decode_tile_kernel<G, CAP>), grid, dim3(256), 0, stream, pp);
+      e = launch_kernel(decode_tile_kernel<G, CAP>, grid, dim3(256), stream, pp);
     } else {
-      return hipErrorInvalidValue;   // the plan selects the tile kernel only for keys as values at width 512
+      return hipErrorNotSupported;   // the plan selects the tile kernel only for keys as values at width 512
     }
   } else if (prm.ks) {
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, G, KEQV, CAP>), grid, dim3(DecodeShape<D, 1>::kWaves * 64), 0, stream,
-                       pp);
+    e = launch_kernel(decode_split_i8_kernel<D, G, KEQV, CAP>, grid, dim3(DecodeShape<D, 1>::kWaves * 64), stream, pp);
   } else if (wide) {
     if constexpr (D >= 256) {
-      hipLaunchKernelGGL((decode_split_kernel<D, G, KEQV, CAP, kCBW>), grid, dim3(DecodeShape<D, kCBW>::kWaves * 64), 0,
-                         stream, pp);
+      e = launch_kernel(decode_split_kernel<D, G, KEQV, CAP, kCBW>, grid, dim3(DecodeShape<D, kCBW>::kWaves * 64),
+                        stream, pp);
     }
   } else {
-    hipLaunchKernelGGL((decode_split_kernel<D, G, KEQV, CAP, 1>), grid, dim3(DecodeShape<D, 1>::kWaves * 64), 0, stream,
-                       pp);
+    e = launch_kernel(decode_split_kernel<D, G, KEQV, CAP, 1>, grid, dim3(DecodeShape<D, 1>::kWaves * 64), stream, pp);
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(static_cast<uint32_t>(a.hq * a.q_len), static_cast<uint32_t>(a.batch)),
-                     dim3(64), 0, stream, prm);
-  return hipGetLastError();
+  return launch_kernel(decode_combine_kernel<D>,
+                       dim3(static_cast<uint32_t>(a.hq * a.q_len), static_cast<uint32_t>(a.batch)), dim3(64), stream,
+                       prm);
 }
 
 template <int D, int G>
@@ -1382,7 +1383,7 @@ hipError_t dispatch_group(const DecodeArgs& a, const DecodeParams& prm, hipStrea
     case 4: return dispatch_flags<D, 4>(a, prm, s);
     case 8: return dispatch_flags<D, 8>(a, prm, s);
     case 16: return dispatch_flags<D, 16>(a, prm, s);
-    default: return hipErrorInvalidValue;
+    default: return hipErrorNotSupported;
   }
 }
 
@@ -1414,6 +1415,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   prm.per_seq = a.per_seq;
   prm.q_len = a.q_len;
   prm.n_cb = (a.group * a.q_len + 15) / 16;
+  // XCD-aware block placement needs a power-of-two XCD count; otherwise plain order.
+  prm.xcd_log2 = 0;
+  if (a.xcds > 1 && (a.xcds & (a.xcds - 1)) == 0)
+    while ((1 << prm.xcd_log2) < a.xcds) ++prm.xcd_log2;
   const double log2e = 1.4426950408889634;
   prm.scale_log2 = static_cast<float>(a.scale * log2e);
   prm.cap_in2 = a.softcap > 0.0 ? static_cast<float>(2.0 * a.scale * log2e / a.softcap) : 0.f;
@@ -1422,7 +1427,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     case 64: return dispatch_group<64>(a, prm, stream);
     case 256: return dispatch_group<256>(a, prm, stream);
     case 512: return dispatch_group<512>(a, prm, stream);
-    default: return hipErrorInvalidValue;
+    default: return hipErrorNotSupported;
   }
 }
 

@@ -6,6 +6,19 @@
 
 namespace ga {
 
+// Launch a kernel that takes one parameter struct and return the launch's own
+// status (hipLaunchKernel reports it directly, so no stale error from an
+// earlier, unrelated call is picked up).
+template <class P>
+inline hipError_t launch_kernel(void (*fn)(P), dim3 grid, dim3 block, hipStream_t stream, P p) {
+  void* args[] = {&p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, 0, stream);
+}
+
+// Launchers return hipErrorNotSupported for a shape with no kernel
+// instantiation or a grid beyond the launch limits; the C ABI reports that as
+// GA_ERR_UNSUPPORTED and every other failure as GA_ERR_HIP.
+
 struct PrologueArgs {
   int32_t batch, seq, hq, hkv, dim, rotary_dim;
   const void* q_in;
@@ -45,8 +58,8 @@ struct PrefillArgs {
   const int32_t* seq_start;   // padded batch (device [B], may be null): kept rows [start, end)
   const int32_t* seq_end;
   double scale, softcap;
+  int32_t xcds;               // L2 domains (XCDs) the dispatcher deals workgroups over, round-robin
 };
-// Returns hipErrorInvalidValue for an unsupported (dim, group) pair.
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
@@ -71,6 +84,7 @@ struct DecodeArgs {
   const float* k_scales;
   const float* v_scales;
   double scale, softcap;
+  int32_t xcds;               // L2 domains (XCDs) the dispatcher deals workgroups over, round-robin
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

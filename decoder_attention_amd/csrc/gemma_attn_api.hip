@@ -1,8 +1,9 @@
 // C ABI entry points (include/gemma_attn.h): host-side checks, then launches.
-// Every check runs before the first HIP call, so an error return means nothing
-// was enqueued.
+// Every argument check runs before anything is enqueued, so an argument error
+// means nothing was enqueued.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 
 #include "gemma_attn.h"
@@ -13,10 +14,36 @@ namespace {
 
 bool dev_ok(const void* p) { return p != nullptr && ga::aligned16(p); }
 
+// hipErrorNotSupported is what the launchers return for a shape with no
+// instantiation or a grid beyond the launch limits; any other failure is the
+// runtime's.
 int hip_rc(hipError_t e) {
   if (e == hipSuccess) return GA_OK;
-  if (e == hipErrorInvalidValue) return GA_ERR_UNSUPPORTED;
+  if (e == hipErrorNotSupported) return GA_ERR_UNSUPPORTED;
   return GA_ERR_HIP;
+}
+
+// CU count, LDS per CU and XCD count of the current device, queried once per
+// device and cached (the values never change while the process runs).  Without
+// a usable device the whole-MI355X shape stands in, so sizes computed on a
+// host with no GPU match the single-partition part.
+ga::DeviceShape current_device_shape() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int32_t> cus[kMaxDev], lds[kMaxDev], xcds[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return ga::kMI355X;
+  ga::DeviceShape d{cus[dev].load(std::memory_order_acquire), lds[dev].load(std::memory_order_relaxed),
+                    xcds[dev].load(std::memory_order_relaxed)};
+  if (d.cus > 0) return d;
+  int c = 0, l = 0, x = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) return ga::kMI355X;
+  if (hipDeviceGetAttribute(&l, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || l < 1)
+    l = ga::kMI355X.lds_per_cu;
+  if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x < 1) x = 1;
+  lds[dev].store(l, std::memory_order_relaxed);
+  xcds[dev].store(x, std::memory_order_relaxed);
+  cus[dev].store(c, std::memory_order_release);
+  return ga::DeviceShape{c, l, x};
 }
 
 int prefill_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq, const void* q,
@@ -50,6 +77,7 @@ int prefill_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batc
   a.seq_end = seq_end;
   a.scale = L.scale;
   a.softcap = L.softcap;
+  a.xcds = current_device_shape().xcds;
   return hip_rc(ga::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -63,15 +91,14 @@ int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch
   if (rc != GA_OK) return rc;
   if (batch < 0 || max_ctx < 1 || q_len < 1 || q_len > max_ctx) return GA_ERR_INVALID_ARG;
   if (!ga::attn_dim_supported(L.head_dim) || !ga::attn_group_supported(L.group)) return GA_ERR_UNSUPPORTED;
-  const long long col_blocks = (static_cast<long long>(L.group) * q_len + 15) / 16;
-  if (batch > 65535 || L.num_kv_heads * col_blocks > 65535 || static_cast<long long>(cfg->num_heads) * q_len > 0x7fffffff)
-    return GA_ERR_UNSUPPORTED;
+  if (!ga::decode_shape_supported(L, cfg->num_heads, batch, q_len)) return GA_ERR_UNSUPPORTED;
   if (batch == 0) return GA_OK;
   if (!dev_ok(q) || !dev_ok(k_cache) || !dev_ok(out) || ctx_len == nullptr) return GA_ERR_INVALID_ARG;
   if (!L.k_eq_v && !dev_ok(v_cache)) return GA_ERR_INVALID_ARG;
   if (k_scales && (!dev_ok(k_scales) || (!L.k_eq_v && !dev_ok(v_scales)))) return GA_ERR_INVALID_ARG;
   if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
-  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len);
+  const ga::DeviceShape dev = current_device_shape();
+  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len, dev);
   const ga::DecodeWorkspace ws = ga::decode_workspace(L, cfg->num_heads, batch, q_len, plan);
   if (workspace == nullptr || !ga::aligned16(workspace) || workspace_bytes < ws.total) return GA_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(workspace);
@@ -104,6 +131,7 @@ int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch
   a.ws_lo = reinterpret_cast<int32_t*>(wsb + ws.lo_off);
   a.scale = L.scale;
   a.softcap = L.softcap;
+  a.xcds = dev.xcds;
   return hip_rc(ga::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -181,7 +209,8 @@ size_t gemma_attn_decode_multi_workspace_size(const gemma_attn_config* cfg, int3
   gemma_attn_layer L;
   if (ga::resolve_layer(cfg, layer_idx, &L) != GA_OK) return 0;
   if (batch < 0 || max_ctx < 1 || q_len < 1 || q_len > max_ctx) return 0;
-  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len);
+  if (!ga::decode_shape_supported(L, cfg->num_heads, batch, q_len)) return 0;
+  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len, current_device_shape());
   return ga::decode_workspace(L, cfg->num_heads, batch, q_len, plan).total;
 }
 

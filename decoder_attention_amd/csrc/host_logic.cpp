@@ -40,7 +40,8 @@ int resolve_layer(const gemma_attn_config* c, int32_t layer_idx, gemma_attn_laye
   std::memset(&L, 0, sizeof(L));
   const int32_t n = c->sliding_window_pattern;
   // One global layer every n layers, local layers first in each period.
-  const bool is_global = c->sliding_window <= 0 || (n >= 1 && (layer_idx + 1) % n == 0);
+  // (64-bit: layer_idx + 1 overflows int32 at the largest index)
+  const bool is_global = c->sliding_window <= 0 || (n >= 1 && (static_cast<int64_t>(layer_idx) + 1) % n == 0);
   L.is_global = is_global ? 1 : 0;
   if (is_global) {
     L.window = 0;
@@ -75,9 +76,12 @@ bool attn_dim_supported(int32_t d) { return d == 64 || d == 256 || d == 512; }
 
 bool attn_group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
-DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t max_ctx, int32_t q_len) {
+DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t max_ctx, int32_t q_len,
+                       const DeviceShape& dev) {
   (void)num_heads;
   DecodePlan p;
+  const long long cus = dev.cus > 0 ? dev.cus : kMI355X.cus;
+  const long long lds_cu = dev.lds_per_cu > 0 ? dev.lds_per_cu : kMI355X.lds_per_cu;
   const long long ql = q_len > 0 ? q_len : 1;
   const long long wspan = static_cast<long long>(L.window) + ql - 1;
   p.span_max = L.window > 0 ? static_cast<int32_t>(wspan < max_ctx ? wspan : max_ctx) : max_ctx;
@@ -93,15 +97,15 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
     rows = static_cast<long long>(L.num_kv_heads) * ((static_cast<long long>(L.group) * ql + 63) / 64);
     per_cu = 2;
   } else {
-    // One round of workgroups on 256 CUs: the split kernel's workgroups per CU
-    // follow from its LDS ring (two waves per workgroup, two waves per SIMD).
+    // One round of workgroups on the device: the split kernel's workgroups
+    // per CU follow from its LDS ring (two waves per workgroup, two waves per SIMD).
     const long long team = L.head_dim > 256 ? 2 : 1;
     const long long lds = (2 / team) * 2 * 16LL * L.head_dim * 2 * (L.k_eq_v ? 1 : 2);
-    per_cu = (160LL * 1024) / lds;
+    per_cu = lds_cu / lds;
     if (per_cu > 4) per_cu = 4;
     if (per_cu < 1) per_cu = 1;
   }
-  long long n = (256 * per_cu) / rows;
+  long long n = (cus * per_cu) / rows;
   const long long line_max = static_cast<long long>(batch > 0 ? batch : 1) * p.span_max;
   const long long at_least = (line_max + 16383) / 16384;   // at most 16K keys per workgroup
   const long long at_most = (line_max + 255) / 256;        // at least 256 keys per workgroup
@@ -113,9 +117,17 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
   // Short spans (local windows) with enough sequences to fill the round: one
   // workgroup per sequence.  Every span is then at most 8K keys, so no
   // workgroup runs long, and none straddles two sequences.
-  p.per_seq = static_cast<long long>(batch) * rows >= 256 * per_cu && p.span_max <= 8192;
+  const long long round = cus * per_cu;
+  p.per_seq = batch > 0 && batch >= (round + rows - 1) / rows && p.span_max <= 8192;
   if (p.per_seq) p.n_wg = batch;
   return p;
+}
+
+bool decode_shape_supported(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t q_len) {
+  if (batch > 65535 || q_len < 1 || L.num_kv_heads < 1) return false;
+  const long long col_blocks = (static_cast<long long>(L.group) * q_len + 15) / 16;
+  if (col_blocks * L.num_kv_heads > 65535) return false;
+  return static_cast<long long>(num_heads) * q_len <= 0x7fffffff;
 }
 
 DecodeWorkspace decode_workspace(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t q_len,

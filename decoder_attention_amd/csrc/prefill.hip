@@ -15,8 +15,9 @@
 //   query rows.
 //
 // Block order
-//   The dispatcher deals linear block ids round-robin over the 8 XCDs, each
-//   with its own L2.  Blocks are renumbered so that the blocks an XCD runs
+//   The dispatcher deals linear block ids round-robin over the XCDs (8 on a
+//   whole MI355X, fewer on a partition; the host passes the count), each with
+//   its own L2.  Blocks are renumbered so that the blocks an XCD runs
 //   together belong to as few (sequence, KV head) pairs as possible -- they
 //   then stream the same K/V tiles through that XCD's L2 -- while every XCD
 //   gets the same amount of work; inside a pair, the longest causal rows go
@@ -84,6 +85,7 @@ struct PrefillParams {
   const int32_t* seq_start;   // padded batch: sequence b keeps rows [start, end) (null: 0, seq)
   const int32_t* seq_end;
   int32_t seq, hq, hkv, window, n_qblocks, n_qblocks_pad, batch;
+  int32_t xcd_log2;   // the dispatcher deals linear block ids round-robin over 2^xcd_log2 XCDs
   float scale_log2;   // scale * log2(e)            (no cap)
   float cap_in2;      // 2 * scale * log2(e) / cap  (cap: exp2 argument of tanh)
   float cap_log2;     // cap * log2(e)
@@ -144,13 +146,14 @@ __device__ __forceinline__ void block_work(const PrefillParams& p, int32_t& pair
   const int32_t lin = static_cast<int32_t>(blockIdx.x);
   const int32_t npairs = p.batch * p.hkv;
   const int32_t nq = p.n_qblocks_pad;
-  const int32_t xcd = lin & 7;
-  const int32_t slot = lin >> 3;
-  if ((npairs & 7) == 0) {          // every XCD owns npairs/8 pairs, one after another
-    pair = xcd + 8 * (slot / nq);
+  const int32_t nx = 1 << p.xcd_log2;
+  const int32_t xcd = lin & (nx - 1);
+  const int32_t slot = lin >> p.xcd_log2;
+  if ((npairs & (nx - 1)) == 0) {          // every XCD owns npairs/nx pairs, one after another
+    pair = xcd + nx * (slot / nq);
     t = slot % nq;
-  } else if ((8 % npairs) == 0) {   // 8/npairs XCDs share a pair and interleave its q-blocks
-    const int32_t k = 8 / npairs;
+  } else if ((nx % npairs) == 0) {         // nx/npairs XCDs share a pair and interleave its q-blocks
+    const int32_t k = nx / npairs;
     pair = xcd % npairs;
     t = slot * k + xcd / npairs;
   } else {
@@ -634,17 +637,17 @@ hipError_t launch_t(const PrefillArgs& a, const PrefillParams& prm, hipStream_t 
   PrefillParams pp = prm;
   pp.n_qblocks = (a.seq + kP - 1) / kP;
   const int32_t npairs = a.batch * a.hkv;
+  const int32_t nx = 1 << pp.xcd_log2;
   int32_t pad = pp.n_qblocks;
-  if ((npairs & 7) != 0 && (8 % npairs) == 0) {
-    const int32_t k = 8 / npairs;
+  if ((npairs & (nx - 1)) != 0 && (nx % npairs) == 0) {
+    const int32_t k = nx / npairs;
     pad = (pp.n_qblocks + k - 1) / k * k;
   }
   pp.n_qblocks_pad = pad;
   const int64_t blocks = static_cast<int64_t>(npairs) * pad;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, G, KEQV, CAP, WIDE>), dim3(static_cast<uint32_t>(blocks)),
-                     dim3(pf_waves<D, KEQV, WIDE>() * 64), 0, stream, pp);
-  return hipGetLastError();
+  if (blocks > 0x7fffffff) return hipErrorNotSupported;
+  return launch_kernel(prefill_kernel<D, G, KEQV, CAP, WIDE>, dim3(static_cast<uint32_t>(blocks)),
+                       dim3(pf_waves<D, KEQV, WIDE>() * 64), stream, pp);
 }
 
 template <int D, int G>
@@ -666,7 +669,7 @@ hipError_t dispatch_group(const PrefillArgs& a, const PrefillParams& prm, hipStr
     case 4: return dispatch_flags<D, 4>(a, prm, s);
     case 8: return dispatch_flags<D, 8>(a, prm, s);
     case 16: return dispatch_flags<D, 16>(a, prm, s);
-    default: return hipErrorInvalidValue;
+    default: return hipErrorNotSupported;
   }
 }
 
@@ -689,6 +692,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   prm.batch = a.batch;
   prm.n_qblocks = 0;
   prm.n_qblocks_pad = 0;
+  // XCD-aware block order needs a power-of-two XCD count; otherwise plain order.
+  prm.xcd_log2 = 0;
+  if (a.xcds > 1 && (a.xcds & (a.xcds - 1)) == 0)
+    while ((1 << prm.xcd_log2) < a.xcds) ++prm.xcd_log2;
   const double log2e = 1.4426950408889634;
   prm.scale_log2 = static_cast<float>(a.scale * log2e);
   prm.cap_in2 = a.softcap > 0.0 ? static_cast<float>(2.0 * a.scale * log2e / a.softcap) : 0.f;
@@ -697,7 +704,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     case 64: return dispatch_group<64>(a, prm, stream);
     case 256: return dispatch_group<256>(a, prm, stream);
     case 512: return dispatch_group<512>(a, prm, stream);
-    default: return hipErrorInvalidValue;
+    default: return hipErrorNotSupported;
   }
 }
 

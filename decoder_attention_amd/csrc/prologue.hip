@@ -451,7 +451,7 @@ hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream) {
   // Rows per item: kLoads passes of the block, fewer when the tokens an item
   // can touch would not fit the LDS tables.
   const int32_t heads = a.hq + (a.k_in ? a.hkv : 0) + (a.v_in ? a.hkv : 0);
-  if (heads < 1) return hipErrorInvalidValue;
+  if (heads < 1) return hipErrorNotSupported;
   const int32_t rpp = kThreads / (a.dim >> 3);
   const int32_t tab_tok = tab_tokens(a.dim);     // >= 7
   // An item of n rows touches at most (n - 1) / heads + 2 tokens.
@@ -471,9 +471,9 @@ hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream) {
     }
     const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>(items, resident));
     if (use_shfl) {
-      hipLaunchKernelGGL((qk_prologue_kernel<T, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+      err = launch_kernel(qk_prologue_kernel<T, true>, dim3(grid), dim3(kThreads), stream, p);
     } else {
-      hipLaunchKernelGGL((qk_prologue_kernel<T, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+      err = launch_kernel(qk_prologue_kernel<T, false>, dim3(grid), dim3(kThreads), stream, p);
     }
   };
   switch (a.dim >> 3) {
@@ -484,10 +484,9 @@ hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream) {
     case 16: go(std::integral_constant<int, 16>{}); break;
     case 32: go(std::integral_constant<int, 32>{}); break;
     case 64: go(std::integral_constant<int, 64>{}); break;
-    default: return hipErrorInvalidValue;
+    default: return hipErrorNotSupported;
   }
-  if (err != hipSuccess) return err;
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace ga

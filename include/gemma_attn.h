@@ -22,9 +22,15 @@
  *  - Device pointers must be 16-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *    asynchronously; nothing in the library synchronizes the host.
- *  - Every argument check runs on the host before the first HIP call; a call
- *    that returns an error has enqueued nothing.  GA_ERR_HIP reports a failed
- *    launch (hipGetLastError after the launch).
+ *  - Every argument check runs on the host before anything is enqueued; a
+ *    call that returns an error has enqueued nothing (except GA_ERR_HIP from a
+ *    decode, whose second launch can fail after its first was enqueued).
+ *    GA_ERR_HIP carries the status the runtime returned for the library's own
+ *    launch; an error left pending by an earlier, unrelated call is neither
+ *    reported nor cleared.
+ *  - Launch plans follow the current device's CU count, LDS size and XCD
+ *    count (queried once per device), so a partitioned MI355X is planned for
+ *    what it has.  Workspace sizes are those of the current device.
  */
 #ifndef GEMMA_ATTN_H
 #define GEMMA_ATTN_H
@@ -39,7 +45,8 @@ extern "C" {
 enum {
   GA_OK = 0,
   GA_ERR_INVALID_ARG = 1, /* a null pointer, a size out of range, an inconsistent config */
-  GA_ERR_UNSUPPORTED = 2, /* valid, but no kernel instantiation (head width, group size) */
+  GA_ERR_UNSUPPORTED = 2, /* valid, but no kernel instantiation (head width, group size) or a shape
+                             beyond the launch limits (batch or grid too large) */
   GA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
   GA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
 };
@@ -158,8 +165,9 @@ int gemma_attn_prefill_ragged(const gemma_attn_config* cfg, int32_t layer_idx, i
                               const int32_t* seq_start, const int32_t* seq_end, void* stream);
 
 /*
- * Bytes of device workspace gemma_attn_decode needs for (layer, batch, max_ctx);
- * 0 when the arguments are invalid.
+ * Bytes of device workspace gemma_attn_decode needs for (layer, batch, max_ctx)
+ * on the current device; 0 when the arguments are invalid or the shape is
+ * unsupported (batch > 65535).
  */
 size_t gemma_attn_decode_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
                                         int32_t max_ctx);
@@ -205,7 +213,9 @@ int gemma_attn_decode_multi(const gemma_attn_config* cfg, int32_t layer_idx, int
                             const int32_t* ctx_len, const int32_t* kv_start, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of gemma_attn_decode_multi; 0 when the arguments are invalid. */
+/* Workspace bytes of gemma_attn_decode_multi on the current device; 0 when the
+ * arguments are invalid or the shape is unsupported (batch > 65535, KV heads x
+ * ceil(g * q_len / 16) > 65535, Hq x q_len >= 2^31). */
 size_t gemma_attn_decode_multi_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
                                               int32_t q_len, int32_t max_ctx);
 
