@@ -21,7 +21,15 @@ The same JSON line also carries
   * ``prefill_configs``: the Gemma-3-1B-shaped 6-layer stack and the
     Gemma-4-12B-shaped global layer (TFLOP/s per layer);
   * ``cpu_baseline``: the fp64 oracle timed on the host's cores over a
-    bounded sample of the same workload.
+    bounded sample of the same workload (``value``), and beside it over
+    samples of the Gemma-3 stack, the Gemma-4 global layer and the decode
+    step (``configs``), with the CPU model and the threads used.
+Every ``roofline`` block (the pair's, one per layer in ``prefill_configs``,
+and the decode one) divides the kernel's algorithmic work per launch by its
+mean launch time from HIP events recorded on the launch stream around the
+timed launches (``timing`` says so); ``traffic`` is the HBM bytes per launch
+from the committed rocprofv3 counter summary under ``profiles/`` while the
+kernel source still hashes to the value recorded there, else null.
 All inputs are seeded synthetic tensors (N(0,1) drawn in fp32, rounded to
 bf16); no trained weights or datasets are involved.
 """
@@ -63,9 +71,12 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+TIMING = "HIP events on the launch stream around each timed launch; mean over the timed launches"
+
+
 def measured_traffic(kernel_source: str, summary: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    when the kernel source has changed since the counters were taken."""
+    """The JSON block of a committed rocprofv3 counter summary, or None when the
+    kernel source has changed since the counters were taken."""
     import hashlib
     import re
 
@@ -78,6 +89,22 @@ def measured_traffic(kernel_source: str, summary: str):
     if block.get("source_sha256") != src:
         return None
     return block
+
+
+def traffic_of(kernel_source: str, summary: str, key: str):
+    """HBM bytes per launch of one workload from a counter summary (None if absent or stale)."""
+    block = measured_traffic(kernel_source, summary)
+    if block is None:
+        return None
+    v = block.get("hbm_bytes_per_launch", {}).get(key)
+    return None if v is None else int(v)
+
+
+def mfma_roofline(flops: int, ms: float, kernel: str, traffic=None) -> dict:
+    achieved = flops / (ms * 1e-3) / 1e12
+    return dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic, kernel=kernel,
+                flops_per_launch=int(flops), avg_launch_ms=round(ms, 4), timing=TIMING)
 
 
 def _flops(kw, layer, B, S) -> int:
@@ -214,12 +241,21 @@ def bench_pair(ga, steps, warmup):
                       frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=_pair_traffic(),
                       kernel="prefill_kernel<256,2,false,true,WIDE>: local WIDE=false (4 waves), global WIDE=true (8)",
                       flops_per_launch={"local_w4096": flops[0], "global": flops[1]},
-                      avg_launch_ms={"local_w4096": round(pre[0], 4), "global": round(pre[1], 4)}),
+                      avg_launch_ms={"local_w4096": round(pre[0], 4), "global": round(pre[1], 4)},
+                      timing=TIMING + "; achieved = both layers' FLOPs over their summed mean launch times"),
         layers=layers,
     )
 
 
-def bench_prefill_layer(ga, workload, layer, reps=10):
+# Kernel forms the host picks for the prefill workloads (for the roofline blocks).
+PREFILL_KERNEL = {
+    ("gemma3_stack", 0): "prefill_kernel<256,4,false,false,false> (4 waves)",
+    ("gemma3_stack", 5): "prefill_kernel<256,4,false,false,false> (4 waves)",
+    ("gemma4_global", 5): "prefill_kernel<512,16,true,false,false> (4 waves, D split in pairs)",
+}
+
+
+def bench_prefill_layer(ga, workload, layer, reps=10, traffic_key=None):
     import torch
 
     cfg_id, kw, _, B, S, with_norm = PREFILL_WORKLOADS[workload]
@@ -231,12 +267,17 @@ def bench_prefill_layer(ga, workload, layer, reps=10):
     for _ in range(reps):
         run_layer_step(ga, kw, layer, t, timer)
     torch.cuda.synchronize()
-    ms = float(np.median(timer.ms("prefill")))
+    ms = float(np.mean(timer.ms("prefill")))
     f = _flops(kw, layer, B, S)
     del t
     torch.cuda.empty_cache()
+    traffic = None
+    if traffic_key:
+        traffic = traffic_of("decoder_attention_amd/csrc/prefill.hip", "prefill_gemma3_gemma4_hbm_traffic.md",
+                             traffic_key)
     return dict(prefill_ms=round(ms, 4), tflops=round(f / (ms * 1e-3) / 1e12, 2),
-                prologue_ms=round(float(np.median(timer.ms("prologue"))), 4), flops=f)
+                prologue_ms=round(float(np.mean(timer.ms("prologue"))), 4), flops=f,
+                roofline=mfma_roofline(f, ms, PREFILL_KERNEL[(workload, layer)], traffic))
 
 
 DECODE_B, DECODE_SMAX, DECODE_MULTI = 64, 65536, 4
@@ -315,6 +356,25 @@ def decode_query(layer, multi=False):
     return normal_bf16(seed_for(5, layer, "q"), (DECODE_B, 1, 16, D))
 
 
+DECODE_KERNEL = {
+    "local_w1024": "decode_split_kernel<256,2,false,false,1> + decode_combine_kernel<256> (one workgroup per sequence)",
+    "local_w1024_q4": "decode_split_kernel<256,2,false,false,1> + decode_combine_kernel<256> (one workgroup per sequence)",
+    "local_w1024_int8": "decode_split_i8_kernel<256,2,false,false> + decode_combine_kernel<256>",
+    "global_keqv": "decode_plan_kernel + decode_split_kernel<512,16,true,false,1> + decode_combine_kernel<512>",
+    "global_keqv_q4": "decode_plan_kernel + decode_tile_kernel<16,false> + decode_combine_kernel<512>",
+    "global_keqv_int8": "decode_plan_kernel + decode_split_i8_kernel<512,16,true,false> + decode_combine_kernel<512>",
+}
+
+
+def hbm_roofline(nbytes: int, ms: float, case: str) -> dict:
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    traffic = traffic_of("decoder_attention_amd/csrc/decode.hip", "decode_hbm_traffic.md", case)
+    return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic, kernel=DECODE_KERNEL[case],
+                bytes_per_launch=int(nbytes), avg_launch_ms=round(ms, 4),
+                timing=TIMING + " (the whole decode call: every kernel it launches)")
+
+
 def bench_decode(ga, reps=20):
     """Gemma-4-12B decode step: one local and one global layer over 64 ragged contexts."""
     import torch
@@ -347,10 +407,11 @@ def bench_decode(ga, reps=20):
         torch.cuda.synchronize()
         span = np.minimum(ctx, W) if W else ctx
         nbytes = int(span.sum()) * Hkv * D * 2 * (1 if L["k_eq_v"] else 2)
-        ms = float(np.median(timer.ms("decode")))
+        ms = float(np.mean(timer.ms("decode")))
         res[name] = dict(decode_ms=round(ms, 4), kv_bytes=nbytes, gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
                          frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         prologue_ms=round(float(np.median(timer.ms("prologue"))), 4))
+                         prologue_ms=round(float(np.mean(timer.ms("prologue"))), 4),
+                         roofline=hbm_roofline(nbytes, ms, name))
 
         # Several new tokens per sequence (draft verification): the same cache
         # rows plus the DECODE_MULTI - 1 extra rows the first token's window adds.
@@ -370,9 +431,10 @@ def bench_decode(ga, reps=20):
         torch.cuda.synchronize()
         span_m = np.minimum(ctx, W + Lq - 1) if W else ctx
         nb_m = int(span_m.sum()) * Hkv * D * 2 * (1 if L["k_eq_v"] else 2)
-        ms_m = float(np.median(tm.ms("m")))
+        ms_m = float(np.mean(tm.ms("m")))
         res[name + "_q4"] = dict(decode_ms=round(ms_m, 4), kv_bytes=nb_m, gbs=round(nb_m / (ms_m * 1e-3) / 1e9, 1),
-                                 frac=round(nb_m / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+                                 frac=round(nb_m / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 roofline=hbm_roofline(nb_m, ms_m, name + "_q4"))
         del qm, outm, wsm
 
         # int8 cache: the same rows quantized on the device (codes + one fp32
@@ -390,53 +452,124 @@ def bench_decode(ga, reps=20):
             t8.stop("d8")
         torch.cuda.synchronize()
         nb8 = int(span.sum()) * Hkv * (D + 4) * (1 if L["k_eq_v"] else 2)
-        ms8 = float(np.median(t8.ms("d8")))
+        ms8 = float(np.mean(t8.ms("d8")))
         res[name + "_int8"] = dict(decode_ms=round(ms8, 4), kv_bytes=nb8, gbs=round(nb8 / (ms8 * 1e-3) / 1e9, 1),
                                    frac=round(nb8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                   speedup_vs_bf16=round(ms / ms8, 3))
+                                   speedup_vs_bf16=round(ms / ms8, 3),
+                                   roofline=hbm_roofline(nb8, ms8, name + "_int8"))
         del kq, ksq, vq, vsq, kc, vc
         torch.cuda.empty_cache()
     tot_bytes = 5 * res["local_w1024"]["kv_bytes"] + res["global_keqv"]["kv_bytes"]
     tot_ms = 5 * res["local_w1024"]["decode_ms"] + res["global_keqv"]["decode_ms"]
     res["stack_5local_1global"] = dict(ms=round(tot_ms, 4), gbs=round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1))
-    res["roofline"] = dict(bound="hbm", achieved=res["global_keqv"]["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                           frac=res["global_keqv"]["frac"], traffic=None, kernel="decode_split_kernel<512,16,true,false,1>")
+    res["roofline"] = res["global_keqv"]["roofline"]
     return res
 
 
-def cpu_baseline(seconds_hint=20.0):
-    """The fp64 oracle on a bounded sample of the timed workload: both layers of
-    the Gemma-2-2B pair over the first S' positions of both sequences."""
-    from oracle import gemma_ref as R
-    from synth import bf16_bits_to_f64, normal_bf16, seed_for
-
-    cfg = R.GemmaAttnConfig(**GEMMA2_PAIR)
-    threads = len(os.sched_getaffinity(0))
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
-    B, S = 2, 8192
-    s_sample = S
-    total_flops, total_s = 0, 0.0
-    for layer in (0, 1):
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+class _SpanCache:
+    """[B', Smax, Hkv, D] view of per-sequence cache rows [lo_b, hi_b) (the rows a decode step reads)."""
+
+    def __init__(self, spans, rows):
+        self.spans, self.rows = spans, rows
+
+    def __getitem__(self, idx):
+        b, s, h, d = idx
+        lo, hi = self.spans[b]
+        assert s.step is None and lo <= s.start <= s.stop <= hi
+        return self.rows[b][s.start - lo:s.stop - lo, h, d]
+
+
+def cpu_baseline():
+    """The fp64 oracle as it stands, on the host's cores, with BLAS held to one
+    thread per worker (threadpoolctl is required: without it the workers'
+    BLAS calls would oversubscribe the cores and the figure would mean
+    nothing).  ``value``: both layers of the Gemma-2-2B pair, whole.  Beside
+    it (``configs``): the Gemma-3-1B local and global layers, whole; the
+    Gemma-4-12B global layer on its first 8192 positions (a causal prefix is
+    a complete problem of its own); the Gemma-4-12B decode step on every
+    eighth of its 64 sequences (GB/s over those sequences' KV bytes).  Only
+    the oracle's attention (and, for prefill, its prologue) is timed; drawing
+    the inputs is not."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gemma_ref as R
+    from synth import bf16_bits_to_f64, normal_bf16, norm_weight, normal_bf16_row, seed_for
+
+    threads = len(os.sched_getaffinity(0))
+
+    def prefill_sample(workload, layer, s_sample):
+        cfg_id, kw, _, B, S, with_norm = PREFILL_WORKLOADS[workload]
+        cfg = R.GemmaAttnConfig(**kw)
         L = R.resolve_layer(cfg, layer)
-        q = bf16_bits_to_f64(normal_bf16(seed_for(2, layer, "q"), (B, S, 8, 256))[:, :s_sample])
-        k = bf16_bits_to_f64(normal_bf16(seed_for(2, layer, "k"), (B, S, 4, 256))[:, :s_sample])
-        v = bf16_bits_to_f64(normal_bf16(seed_for(2, layer, "v"), (B, S, 4, 256))[:, :s_sample])
+        D, Hkv, Hq = L["head_dim"], L["num_kv_heads"], cfg.num_heads
+        q = bf16_bits_to_f64(normal_bf16(seed_for(cfg_id, layer, "q"), (B, S, Hq, D))[:, :s_sample])
+        k = bf16_bits_to_f64(normal_bf16(seed_for(cfg_id, layer, "k"), (B, S, Hkv, D))[:, :s_sample])
+        v = None if L["k_eq_v"] else bf16_bits_to_f64(
+            normal_bf16(seed_for(cfg_id, layer, "v"), (B, S, Hkv, D))[:, :s_sample])
+        qw = norm_weight(seed_for(cfg_id, layer, "q_norm_w"), D) if with_norm else None
+        kw_ = norm_weight(seed_for(cfg_id, layer, "k_norm_w"), D) if with_norm else None
         t0 = time.perf_counter()
-        if threadpool_limits:
-            with threadpool_limits(limits=1):
-                qt, kt = R.prologue(cfg, layer, q, k)
-                R.prefill(cfg, layer, qt, kt, v, threads=threads)
-        else:
-            qt, kt = R.prologue(cfg, layer, q, k)
-            R.prefill(cfg, layer, qt, kt, v, threads=threads)
-        total_s += time.perf_counter() - t0
-        total_flops += R.prefill_flops(cfg, layer, B, s_sample)
-    return dict(value=round(total_flops / total_s / 1e12, 5), unit="TFLOP/s", cores=threads, kind="oracle",
-                sample=f"both layers of the Gemma-2-2B pair, first {s_sample} of {S} positions of both sequences "
-                       f"({total_flops:.3e} unmasked FLOPs in {total_s:.1f} s, fp64 numpy)")
+        with threadpool_limits(limits=1):
+            qt, kt = R.prologue(cfg, layer, q, k, qw, kw_)
+            R.prefill(cfg, layer, qt, kt, v, block_rows=64 if D > 256 else 256, threads=threads)
+        dt = time.perf_counter() - t0
+        f = R.prefill_flops(cfg, layer, B, s_sample)
+        return f, dt
+
+    pf, pt = 0, 0.0
+    for layer in (0, 1):
+        f, dt = prefill_sample("gemma2_pair", layer, 8192)
+        pf += f
+        pt += dt
+    configs = {}
+    for name, (wl, layer, s_sample) in {"gemma3_1b_local_w512": ("gemma3_stack", 0, 16384),
+                                          "gemma3_1b_global": ("gemma3_stack", 5, 16384),
+                                          "gemma4_12b_global_keqv_d512": ("gemma4_global", 5, 8192)}.items():
+        f, dt = prefill_sample(wl, layer, s_sample)
+        S = PREFILL_WORKLOADS[wl][4]
+        configs[name] = dict(value=round(f / dt / 1e12, 5), unit="TFLOP/s", seconds=round(dt, 2), flops=f,
+                             sample=f"first {s_sample} of {S} positions, every sequence and head")
+
+    # decode: every eighth sequence of the Gemma-4-12B step, both layers
+    cfg = R.GemmaAttnConfig(**GEMMA4_12B)
+    ctx = decode_contexts()
+    sel = list(range(0, DECODE_B, 8))
+    for layer, name in ((0, "decode_local_w1024"), (5, "decode_global_keqv")):
+        L = R.resolve_layer(cfg, layer)
+        D, Hkv, W = L["head_dim"], L["num_kv_heads"], L["window"]
+        spans = [decode_span(ctx[b], W) for b in sel]
+        caches = []
+        for tensor in (("k",) if L["k_eq_v"] else ("k", "v")):
+            seed = seed_for(5, layer, tensor)
+            caches.append(_SpanCache(spans, [bf16_bits_to_f64(normal_bf16_row(seed, b, (hi - lo, Hkv, D)))
+                                             for b, (lo, hi) in zip(sel, spans)]))
+        kc = caches[0]
+        vc = None if L["k_eq_v"] else caches[1]
+        cs = ctx[sel]
+        q = R.prologue(cfg, layer, bf16_bits_to_f64(decode_query(layer)[sel]), pos0=cs - 1)[0][:, 0]
+        t0 = time.perf_counter()
+        R.decode(cfg, layer, q, kc, vc, cs)
+        dt = time.perf_counter() - t0
+        nbytes = R.decode_kv_bytes(cfg, layer, cs)
+        configs[name] = dict(value=round(nbytes / dt / 1e9, 3), unit="GB/s", seconds=round(dt, 2), kv_bytes=nbytes,
+                             sample=f"sequences {sel} of {DECODE_B} (one new token each)")
+    return dict(value=round(pf / pt / 1e12, 5), unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"both layers of the Gemma-2-2B pair, all 8192 positions of both sequences "
+                       f"({pf:.3e} unmasked FLOPs in {pt:.1f} s, fp64 numpy)",
+                cpu_model=_cpu_model(), configs=configs)
 
 
 def main():
@@ -473,9 +606,10 @@ def main():
         out = {}
         if a.workload == "gemma3":
             for layer, name in ((0, "gemma3_1b_local_w512"), (5, "gemma3_1b_global")):
-                out[name] = bench_prefill_layer(ga, "gemma3_stack", layer, reps=a.steps)
+                out[name] = bench_prefill_layer(ga, "gemma3_stack", layer, reps=a.steps, traffic_key=name)
         elif a.workload == "gemma4":
-            out["gemma4_12b_global_keqv_d512"] = bench_prefill_layer(ga, "gemma4_global", 5, reps=a.steps)
+            out["gemma4_12b_global_keqv_d512"] = bench_prefill_layer(ga, "gemma4_global", 5, reps=a.steps,
+                                                                     traffic_key="gemma4_12b_global_keqv_d512")
         else:
             out["decode"] = bench_decode(ga, reps=a.steps)
         print(json.dumps({"workload": a.workload, **out}), flush=True)
@@ -512,14 +646,15 @@ def main():
         log("[bench] gemma3 stack / gemma4 global prefill")
         cfgs = {}
         for layer, name in ((0, "gemma3_1b_local_w512"), (5, "gemma3_1b_global")):
-            cfgs[name] = bench_prefill_layer(ga, "gemma3_stack", layer)
+            cfgs[name] = bench_prefill_layer(ga, "gemma3_stack", layer, traffic_key=name)
         s3 = cfgs["gemma3_1b_local_w512"]
         g3 = cfgs["gemma3_1b_global"]
         stack_f = 5 * s3["flops"] + g3["flops"]
         stack_ms = 5 * s3["prefill_ms"] + g3["prefill_ms"]
         cfgs["gemma3_1b_stack_5local_1global"] = dict(prefill_ms=round(stack_ms, 4),
                                                        tflops=round(stack_f / (stack_ms * 1e-3) / 1e12, 2))
-        cfgs["gemma4_12b_global_keqv_d512"] = bench_prefill_layer(ga, "gemma4_global", 5, reps=5)
+        cfgs["gemma4_12b_global_keqv_d512"] = bench_prefill_layer(ga, "gemma4_global", 5, reps=5,
+                                                                  traffic_key="gemma4_12b_global_keqv_d512")
         line["prefill_configs"] = cfgs
         log(f"[bench] prefill configs: {json.dumps(cfgs)}")
         log("[bench] gemma4 decode: building caches")
