@@ -19,7 +19,7 @@ from dataclasses import dataclass
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemma_attn.so")
 
-GA_OK, GA_ERR_INVALID_ARG, GA_ERR_UNSUPPORTED, GA_ERR_WORKSPACE, GA_ERR_HIP = 0, 1, 2, 3, 4
+GA_OK, GA_ERR_INVALID_ARG, GA_ERR_UNSUPPORTED, GA_ERR_WORKSPACE, GA_ERR_HIP, GA_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4, 5
 
 
 class GemmaAttnError(RuntimeError):
@@ -143,6 +143,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gemma_attn_decode_multi.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             ctypes.c_size_t, _VP]
     lib.gemma_attn_decode_multi.restype = ctypes.c_int
+    lib.gemma_attn_decode_multi_noalloc.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                    _VP]
+    lib.gemma_attn_decode_multi_noalloc.restype = ctypes.c_int
     lib.gemma_attn_decode_multi_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
     lib.gemma_attn_decode_multi_workspace_size.restype = ctypes.c_size_t
     lib.gemma_qk_prologue_cache.argtypes = [cfgp, i32, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
@@ -358,6 +361,37 @@ def attn_decode_multi(cfg, layer_idx, q, k_cache, v_cache, ctx_len, out=None, ls
         _ptr(kv_start, torch.int32, "kv_start"), _ptr(out, bf, "out"), _ptr(lse, torch.float32, "lse"),
         _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "gemma_attn_decode_multi")
+    return (out, lse) if lse is not None else out
+
+
+def attn_decode_multi_noalloc(cfg, layer_idx, q, k_cache, v_cache, ctx_len, out, lse=None, stream=None,
+                              kv_start=None):
+    """gemma_attn_decode_multi_noalloc: decode_multi with the library's own fixed scratch array as workspace;
+    the caller passes every output (nothing is allocated here either).  Calls overlapping on one GPU race.
+    Returns out, or (out, lse) when lse is given."""
+    import torch
+
+    cfg = Config.from_any(cfg)
+    L = resolve_layer(cfg, layer_idx)
+    B, Lq = q.shape[0], q.shape[1]
+    Smax = k_cache.shape[1]
+    _expect(q, (B, Lq, cfg.num_heads, L["head_dim"]), "q")
+    _expect(k_cache, (B, Smax, L["num_kv_heads"], L["head_dim"]), "k_cache")
+    if v_cache is not None and not L["k_eq_v"]:
+        _expect(v_cache, (B, Smax, L["num_kv_heads"], L["head_dim"]), "v_cache")
+    _expect(ctx_len, (B,), "ctx_len")
+    if kv_start is not None:
+        _expect(kv_start, (B,), "kv_start")
+    _expect(out, tuple(q.shape), "out")
+    if lse is not None:
+        _expect(lse, (B, cfg.num_heads, Lq), "lse")
+    bf = torch.bfloat16
+    rc = load().gemma_attn_decode_multi_noalloc(
+        ctypes.byref(cfg.to_c()), int(layer_idx), B, Lq, Smax, _ptr(q, bf, "q"), _ptr(k_cache, bf, "k_cache"),
+        None if L["k_eq_v"] else _ptr(v_cache, bf, "v_cache"), _ptr(ctx_len, torch.int32, "ctx_len"),
+        _ptr(kv_start, torch.int32, "kv_start"), _ptr(out, bf, "out"), _ptr(lse, torch.float32, "lse"),
+        _stream(stream))
+    _check(rc, "gemma_attn_decode_multi_noalloc")
     return (out, lse) if lse is not None else out
 
 

@@ -46,6 +46,26 @@ ga::DeviceShape current_device_shape() {
   return ga::DeviceShape{c, l, x};
 }
 
+// Scratch of the allocation-free decode entry point: one array per device,
+// held from the library's first use of a device until the process ends.  In
+// host code `scratch` only names the symbol; its device address (a different
+// one on every GPU) comes from hipGetSymbolAddress, once per device, with
+// that device current, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t{80} << 20;   // 80 MiB
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* device_scratch() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<void*> addr[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  addr[dev].store(p, std::memory_order_release);   // racing first calls store the same address
+  return p;
+}
+
 int prefill_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq, const void* q,
                    const void* k, const void* v, void* out, float* lse, const int32_t* seq_start,
                    const int32_t* seq_end, void* stream) {
@@ -85,7 +105,7 @@ int prefill_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batc
 int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len, int32_t max_ctx,
                   const void* q, const void* k_cache, const float* k_scales, const void* v_cache,
                   const float* v_scales, const int32_t* ctx_len, const int32_t* kv_start, void* out, float* lse,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream, bool use_scratch = false) {
   gemma_attn_layer L;
   const int rc = ga::resolve_layer(cfg, layer_idx, &L);
   if (rc != GA_OK) return rc;
@@ -100,6 +120,12 @@ int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch
   const ga::DeviceShape dev = current_device_shape();
   const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len, dev);
   const ga::DecodeWorkspace ws = ga::decode_workspace(L, cfg->num_heads, batch, q_len, plan);
+  if (use_scratch) {   // the allocation-free entry point: the library's own scratch array
+    if (ws.total > kScratchBytes) return GA_ERR_SCRATCH_LIMIT;
+    workspace = device_scratch();
+    if (workspace == nullptr) return GA_ERR_HIP;
+    workspace_bytes = kScratchBytes;
+  }
   if (workspace == nullptr || !ga::aligned16(workspace) || workspace_bytes < ws.total) return GA_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(workspace);
   ga::DecodeArgs a{};
@@ -150,6 +176,7 @@ const char* gemma_attn_strerror(int code) {
     case GA_ERR_UNSUPPORTED: return "unsupported head width or group size";
     case GA_ERR_WORKSPACE: return "decode workspace missing or too small";
     case GA_ERR_HIP: return "HIP launch failed";
+    case GA_ERR_SCRATCH_LIMIT: return "shape needs more decode workspace than the library's 80 MiB scratch holds";
     default: return "unknown error";
   }
 }
@@ -225,6 +252,14 @@ int gemma_attn_decode_multi(const gemma_attn_config* cfg, int32_t layer_idx, int
                             size_t workspace_bytes, void* stream) {
   return decode_common(cfg, layer_idx, batch, q_len, max_ctx, q, k_cache, nullptr, v_cache, nullptr, ctx_len, kv_start,
                        out, lse, workspace, workspace_bytes, stream);
+}
+
+int gemma_attn_decode_multi_noalloc(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                                    int32_t max_ctx, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* ctx_len, const int32_t* kv_start, void* out, float* lse,
+                                    void* stream) {
+  return decode_common(cfg, layer_idx, batch, q_len, max_ctx, q, k_cache, nullptr, v_cache, nullptr, ctx_len, kv_start,
+                       out, lse, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 int gemma_attn_decode_int8(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,

@@ -48,7 +48,9 @@ enum {
   GA_ERR_UNSUPPORTED = 2, /* valid, but no kernel instantiation (head width, group size) or a shape
                              beyond the launch limits (batch or grid too large) */
   GA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
-  GA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+  GA_ERR_HIP = 4,         /* the HIP runtime rejected a launch */
+  GA_ERR_SCRATCH_LIMIT = 5 /* gemma_attn_decode_multi_noalloc: the shape needs more workspace than
+                              the library's fixed scratch array holds */
 };
 
 /*
@@ -218,6 +220,27 @@ int gemma_attn_decode_multi(const gemma_attn_config* cfg, int32_t layer_idx, int
  * ceil(g * q_len / 16) > 65535, Hq x q_len >= 2^31). */
 size_t gemma_attn_decode_multi_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
                                               int32_t q_len, int32_t max_ctx);
+
+/*
+ * gemma_attn_decode_multi without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  It allocates nothing: the split
+ * partials live in a fixed 80 MiB device array of the library, one per GPU,
+ * held from the library's first use of that GPU until the process ends.  Every
+ * call on a GPU uses that GPU's one array, so calls that overlap on one GPU
+ * (on different streams, or from different threads) race and must be
+ * serialised by the caller; calls on different GPUs are independent.  Each
+ * call writes every part of the array it reads before reading it, so nothing
+ * needs clearing between calls.  Arguments, results and errors as for
+ * gemma_attn_decode_multi, plus GA_ERR_SCRATCH_LIMIT when
+ * gemma_attn_decode_multi_workspace_size() of the shape exceeds 80 MiB
+ * (e.g. 64 sequences of up to 65536 keys at head width 512 with 16 new tokens);
+ * nothing is enqueued then.
+ */
+int gemma_attn_decode_multi_noalloc(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t q_len,
+                                    int32_t max_ctx, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* ctx_len, const int32_t* kv_start, void* out, float* lse,
+                                    void* stream);
 
 /*
  * Prologue of q_len new tokens per sequence that appends them to the cache:

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(ga):
                           "gemma_attn_decode_workspace_size", "gemma_attn_decode", "gemma_attn_strerror",
                           "gemma_attn_decode_multi", "gemma_attn_decode_multi_workspace_size",
                           "gemma_qk_prologue_cache", "gemma_attn_decode_int8", "gemma_qk_prologue_cache_int8",
-                          "gemma_kv_quantize_int8", "gemma_attn_prefill_ragged"}
+                          "gemma_kv_quantize_int8", "gemma_attn_prefill_ragged", "gemma_attn_decode_multi_noalloc"}
     lib = ctypes.CDLL(ga.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -307,3 +307,22 @@ def test_binding_refuses_wrongly_shaped_outputs(ga):
     for name, call in _bad_output_calls(ga):
         with pytest.raises(ValueError, match="has shape"):
             call()
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(ga):
+    """64 sequences of up to 65536 keys at head width 512 with 16 new tokens need
+    about 160 MiB of split partials, more than the 80 MiB scratch array: refused
+    on the host with its own error, before anything is enqueued (the pointers
+    here are never dereferenced)."""
+    cfg = ga.Config(**_G4).to_c()
+    fake = ctypes.c_void_p(0x10000)
+    lib = ga.load()
+    need = lib.gemma_attn_decode_multi_workspace_size(ctypes.byref(cfg), 5, 64, 16, 65536)
+    assert need > 80 << 20
+    rc = lib.gemma_attn_decode_multi_noalloc(ctypes.byref(cfg), 5, 64, 16, 65536, fake, fake, None, fake, None, fake,
+                                             None, None)
+    assert rc == ga.GA_ERR_SCRATCH_LIMIT
+    assert b"scratch" in lib.gemma_attn_strerror(rc)
+    # argument errors still come first
+    assert lib.gemma_attn_decode_multi_noalloc(ctypes.byref(cfg), 5, 64, 16, 65536, None, fake, None, fake, None, fake,
+                                               None, None) == ga.GA_ERR_INVALID_ARG
