@@ -291,9 +291,10 @@ def _rows_block(qb, keys, vals, i_pos, j_pos, L):
 def prefill(cfg, layer_idx, q, k, v=None, block_rows: int = 256, threads: int | None = None):
     """Causal (optionally windowed) attention over prologue outputs.
 
-    q [B,S,Hq,D], k [B,S,Hkv,D], v [B,S,Hkv,D] (ignored with keys-as-values:
-    the Gemma 4 page ties the key and value projections on global layers;
-    reading: the value tensor is the processed key tensor).  Query and key
+    q [B,S,Hq,D], k [B,S,Hkv,D], v [B,S,Hkv,D] (ignored with keys-as-values,
+    the k_eq_v flag of the Gemma 4 page's Gemma4Model table, under which one
+    projection serves for keys and values on global layers; reading: the
+    value tensor is the processed key tensor).  Query and key
     positions are 0..S-1.  Returns out [B,S,Hq,D] and lse [B,Hq,S], fp64.
     """
     L = resolve_layer(cfg, layer_idx)
