@@ -30,6 +30,10 @@ mean launch time from HIP events recorded on the launch stream around the
 timed launches (``timing`` says so); ``traffic`` is the HBM bytes per launch
 from the committed rocprofv3 counter summary under ``profiles/`` while the
 kernel source still hashes to the value recorded there, else null.
+``measured_ceiling`` holds what library code reaches on the same GPU in the
+same run (a bf16 GEMM through torch.matmul, a device-to-device copy); each
+roofline block adds ``frac_of_measured``, its achieved rate over that
+ceiling, beside ``frac`` against the published peak.
 All inputs are seeded synthetic tensors (N(0,1) drawn in fp32, rounded to
 bf16); no trained weights or datasets are involved.
 """
@@ -572,6 +576,51 @@ def cpu_baseline():
                 cpu_model=_cpu_model(), configs=configs)
 
 
+def measured_ceilings() -> dict:
+    """What library code reaches on this GPU: a bf16 GEMM through torch.matmul
+    (hipBLASLt) and a device-to-device copy.  Context for the roofline
+    fractions, which stay against the published peaks."""
+    import torch
+
+    n = 8192
+    a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for e0, e1 in ev:
+        e0.record()
+        c = torch.matmul(a, b)
+        e1.record()
+    torch.cuda.synchronize()
+    gemm_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del a, b, c
+    x = torch.empty(1 << 30, dtype=torch.int16, device="cuda")   # 2 GiB
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record()
+        y.copy_(x)
+        e1.record()
+    torch.cuda.synchronize()
+    copy_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del x, y
+    torch.cuda.empty_cache()
+    return dict(
+        mfma_bf16_gemm=dict(value=round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1), unit="TFLOP/s",
+                            how=f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), median of 10 launches"),
+        hbm_copy=dict(value=round(2 * (2 << 30) / (copy_ms * 1e-3) / 1e9, 1), unit="GB/s",
+                      how="2 GiB device-to-device copy, bytes read + written, median of 10"))
+
+
+def _with_measured(roof: dict, ceil: dict) -> dict:
+    key = "mfma_bf16_gemm" if roof.get("bound") == "mfma" else "hbm_copy"
+    return dict(roof, frac_of_measured=round(roof["achieved"] / ceil[key]["value"], 4))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -660,6 +709,17 @@ def main():
         log("[bench] gemma4 decode: building caches")
         line["decode"] = bench_decode(ga)
         log(f"[bench] decode: {json.dumps(line['decode'])}")
+    if a.workload == "all":
+        log("[bench] measured ceilings (library GEMM, device copy)")
+        ceil = measured_ceilings()
+        line["measured_ceiling"] = ceil
+        line["roofline"] = _with_measured(line["roofline"], ceil)
+        for blk in list(line.get("prefill_configs", {}).values()) + list(line.get("decode", {}).values()):
+            if isinstance(blk, dict) and "roofline" in blk:
+                blk["roofline"] = _with_measured(blk["roofline"], ceil)
+        if "decode" in line:
+            line["decode"]["roofline"] = line["decode"]["global_keqv"]["roofline"]
+        log(f"[bench] measured ceilings: {json.dumps(ceil)}")
     if not a.no_cpu_baseline and a.workload == "all":
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline()

@@ -86,6 +86,7 @@ struct PrefillParams {
   const int32_t* seq_end;
   int32_t seq, hq, hkv, window, n_qblocks, n_qblocks_pad, batch;
   int32_t xcd_log2;   // the dispatcher deals linear block ids round-robin over 2^xcd_log2 XCDs
+  int32_t xcd_runs;   // XCDs sharing a pair take contiguous runs of its q-blocks (else interleaved)
   float scale_log2;   // scale * log2(e)            (no cap)
   float cap_in2;      // 2 * scale * log2(e) / cap  (cap: exp2 argument of tanh)
   float cap_log2;     // cap * log2(e)
@@ -152,10 +153,14 @@ __device__ __forceinline__ void block_work(const PrefillParams& p, int32_t& pair
   if ((npairs & (nx - 1)) == 0) {          // every XCD owns npairs/nx pairs, one after another
     pair = xcd + nx * (slot / nq);
     t = slot % nq;
-  } else if ((nx % npairs) == 0) {         // nx/npairs XCDs share a pair and interleave its q-blocks
+  } else if ((nx % npairs) == 0) {         // nx/npairs XCDs share a pair
     const int32_t k = nx / npairs;
     pair = xcd % npairs;
-    t = slot * k + xcd / npairs;
+    // Uniform work (a window much shorter than the sequence): each XCD takes
+    // one contiguous run, so the blocks it runs together share their keys in
+    // its L2.  Causal rows grow with the position: interleaving keeps the
+    // XCDs' shares equal.
+    t = p.xcd_runs ? (xcd / npairs) * (nq / k) + slot : slot * k + xcd / npairs;
   } else {
     pair = lin / nq;
     t = lin % nq;
@@ -291,6 +296,20 @@ void prefill_kernel(PrefillParams p) {
   int32_t kv_begin = max(W > 0 ? max(0, p0 - W + 1) : 0, r_lo);
   kv_begin &= ~(kKeys - 1);
   const int32_t n_tiles = max(0, (kv_end - kv_begin + kKeys - 1) / kKeys);
+  // Tile order on a sliding window: step s visits the block's tile whose
+  // absolute index is congruent to s modulo n_tiles.  Blocks with the same
+  // tile count (every block past the first window) then read the same tile,
+  // or tiles n_tiles apart, at the same step, so the blocks an XCD runs
+  // together share each K/V tile in its L2 instead of each streaming its own
+  // part of the window.  The softmax does not depend on the order; without a
+  // window (first key 0) the order is the plain one.
+  int32_t rot = 0;
+  if (W > 0 && n_tiles > 0) rot = (n_tiles - (kv_begin / kKeys) % n_tiles) % n_tiles;
+  auto tile_key = [&](int32_t s) -> int32_t {
+    int32_t r = s + rot;
+    r -= r >= n_tiles ? n_tiles : 0;
+    return kv_begin + r * kKeys;
+  };
 
   // Issue the direct-to-LDS copies of the tile starting at key kt into ring
   // slot B.  Addresses are a wave-uniform tile base (a buffer resource over
@@ -343,8 +362,8 @@ void prefill_kernel(PrefillParams p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  if (0 < n_tiles) issue(kv_begin, I0{});
-  if (kAhead > 1 && 1 < n_tiles) issue(kv_begin + kKeys, I1{});
+  if (0 < n_tiles) issue(tile_key(0), I0{});
+  if (kAhead > 1 && 1 < n_tiles) issue(tile_key(1), I1{});
 
   // Q^T operand: lane holds d = ds*16 + h*8 + [0, 8) of its column.
   bf16x8 qf[kDS];
@@ -368,8 +387,8 @@ void prefill_kernel(PrefillParams p) {
   // (B + kAhead) % kBufs are issued.
   auto step = [&](auto B) {
     constexpr int kB = decltype(B)::value;
-    const int32_t kt = kv_begin + it * kKeys;
-    if (it + kAhead < n_tiles) issue(kt + kAhead * kKeys, std::integral_constant<int, (kB + kAhead) % kBufs>{});
+    const int32_t kt = tile_key(it);
+    if (it + kAhead < n_tiles) issue(tile_key(it + kAhead), std::integral_constant<int, (kB + kAhead) % kBufs>{});
     const uint16_t* kb = kslot(B);
     const uint16_t* vb = vslot(B);
 
@@ -644,6 +663,9 @@ hipError_t launch_t(const PrefillArgs& a, const PrefillParams& prm, hipStream_t 
     pad = (pp.n_qblocks + k - 1) / k * k;
   }
   pp.n_qblocks_pad = pad;
+  // Contiguous runs only where every block does about the same work: the
+  // lighter blocks before the first full window are at most 1/8 of the rows.
+  pp.xcd_runs = a.window > 0 && static_cast<int64_t>(a.window) * 8 <= a.seq;
   const int64_t blocks = static_cast<int64_t>(npairs) * pad;
   if (blocks > 0x7fffffff) return hipErrorNotSupported;
   return launch_kernel(prefill_kernel<D, G, KEQV, CAP, WIDE>, dim3(static_cast<uint32_t>(blocks)),
@@ -692,6 +714,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   prm.batch = a.batch;
   prm.n_qblocks = 0;
   prm.n_qblocks_pad = 0;
+  prm.xcd_runs = 0;
   // XCD-aware block order needs a power-of-two XCD count; otherwise plain order.
   prm.xcd_log2 = 0;
   if (a.xcds > 1 && (a.xcds & (a.xcds - 1)) == 0)
