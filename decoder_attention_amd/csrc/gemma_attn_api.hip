@@ -118,7 +118,7 @@ int decode_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch
   if (k_scales && (!dev_ok(k_scales) || (!L.k_eq_v && !dev_ok(v_scales)))) return GA_ERR_INVALID_ARG;
   if (lse && !ga::aligned16(lse)) return GA_ERR_INVALID_ARG;
   const ga::DeviceShape dev = current_device_shape();
-  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len, dev);
+  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len, dev, k_scales != nullptr);
   const ga::DecodeWorkspace ws = ga::decode_workspace(L, cfg->num_heads, batch, q_len, plan);
   if (use_scratch) {   // the allocation-free entry point: the library's own scratch array
     if (ws.total > kScratchBytes) return GA_ERR_SCRATCH_LIMIT;
@@ -237,8 +237,13 @@ size_t gemma_attn_decode_multi_workspace_size(const gemma_attn_config* cfg, int3
   if (ga::resolve_layer(cfg, layer_idx, &L) != GA_OK) return 0;
   if (batch < 0 || max_ctx < 1 || q_len < 1 || q_len > max_ctx) return 0;
   if (!ga::decode_shape_supported(L, cfg->num_heads, batch, q_len)) return 0;
-  const ga::DecodePlan plan = ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len, current_device_shape());
-  return ga::decode_workspace(L, cfg->num_heads, batch, q_len, plan).total;
+  // Either cache type: the larger of the bf16 and int8 plans' workspaces.
+  const ga::DeviceShape dev = current_device_shape();
+  const size_t a = ga::decode_workspace(L, cfg->num_heads, batch, q_len,
+                                        ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len, dev, false)).total;
+  const size_t b = ga::decode_workspace(L, cfg->num_heads, batch, q_len,
+                                        ga::decode_plan(L, cfg->num_heads, batch, max_ctx, q_len, dev, true)).total;
+  return a > b ? a : b;
 }
 
 size_t gemma_attn_decode_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,

@@ -77,7 +77,7 @@ bool attn_dim_supported(int32_t d) { return d == 64 || d == 256 || d == 512; }
 bool attn_group_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
 DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t max_ctx, int32_t q_len,
-                       const DeviceShape& dev) {
+                       const DeviceShape& dev, bool int8) {
   (void)num_heads;
   DecodePlan p;
   const long long cus = dev.cus > 0 ? dev.cus : kMI355X.cus;
@@ -90,7 +90,8 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
   // Many query columns per KV head at head width 512 with keys as values (a
   // multi-token step on an MQA global layer): the tile kernel, which takes 64
   // columns per workgroup through 32x32 products, two workgroups per CU.
-  p.tile = L.k_eq_v && L.head_dim == 512 && col_blocks >= 3;
+  // (Not for int8 caches: they always take the split kernel.)
+  p.tile = !int8 && L.k_eq_v && L.head_dim == 512 && col_blocks >= 3;
   long long rows = static_cast<long long>(L.num_kv_heads) * col_blocks;
   long long per_cu;
   if (p.tile) {
@@ -98,7 +99,8 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
     per_cu = 2;
   } else {
     // One round of workgroups on the device: the split kernel's workgroups
-    // per CU follow from its LDS ring (two waves per workgroup, two waves per SIMD).
+    // per CU follow from its LDS ring (two waves per workgroup, two waves per
+    // SIMD): two slots of 16 bf16 rows (or 32 int8 rows, the same bytes) per team.
     const long long team = L.head_dim > 256 ? 2 : 1;
     const long long lds = (2 / team) * 2 * 16LL * L.head_dim * 2 * (L.k_eq_v ? 1 : 2);
     per_cu = lds_cu / lds;

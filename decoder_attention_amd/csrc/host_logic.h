@@ -42,7 +42,8 @@ constexpr DeviceShape kMI355X{256, 160 * 1024, 8};
 // the sequences alone fill the round, workgroup w takes sequence w instead.  `span_max` is
 // the longest key range one sequence can read: min(W + q_len - 1, max_ctx) on
 // local layers (q_len query tokens at the end of the context), max_ctx on
-// global layers.
+// global layers.  `int8`: the plan of an int8-cache call, which always takes
+// the split kernel (never the bf16 tile kernel).
 struct DecodePlan {
   int32_t n_wg;
   int32_t span_max;
@@ -51,7 +52,7 @@ struct DecodePlan {
                   // the 32-key tile kernel, 64 columns per workgroup, two workgroups per CU
 };
 DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t batch, int32_t max_ctx, int32_t q_len,
-                       const DeviceShape& dev = kMI355X);
+                       const DeviceShape& dev = kMI355X, bool int8 = false);
 
 // Decode shapes the kernels' grids and the workspace layout can hold:
 // batch <= 65535, KV heads x 16-column blocks <= 65535, Hq x q_len < 2^31.

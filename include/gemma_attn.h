@@ -215,9 +215,11 @@ int gemma_attn_decode_multi(const gemma_attn_config* cfg, int32_t layer_idx, int
                             const int32_t* ctx_len, const int32_t* kv_start, void* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of gemma_attn_decode_multi on the current device; 0 when the
- * arguments are invalid or the shape is unsupported (batch > 65535, KV heads x
- * ceil(g * q_len / 16) > 65535, Hq x q_len >= 2^31). */
+/* Workspace bytes of gemma_attn_decode_multi on the current device, which
+ * also cover gemma_attn_decode_int8 of the same shape (the larger of the two
+ * launch plans' needs); 0 when the arguments are invalid or the shape is
+ * unsupported (batch > 65535, KV heads x ceil(g * q_len / 16) > 65535,
+ * Hq x q_len >= 2^31). */
 size_t gemma_attn_decode_multi_workspace_size(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch,
                                               int32_t q_len, int32_t max_ctx);
 

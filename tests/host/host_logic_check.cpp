@@ -46,7 +46,7 @@ int main() {
     }
     if (batch < 0 || max_ctx < 1 || q_len < 1 || q_len > max_ctx || batch > 0x7fffffff ||
         !ga::decode_shape_supported(L, c.num_heads, static_cast<int32_t>(batch), static_cast<int32_t>(q_len))) {
-      std::printf("%d %d %d %d %d %d %d %d %.17g %.17g %.17g %.17g -1 -1 -1 -1 0\n", rc, L.is_global, L.window,
+      std::printf("%d %d %d %d %d %d %d %d %.17g %.17g %.17g %.17g -1 -1 -1 -1 0 -1 -1 -1 0\n", rc, L.is_global, L.window,
                   L.num_kv_heads, L.head_dim, L.group, L.rotary_dim, L.k_eq_v, L.theta, L.scale, L.softcap,
                   L.pos_div);
       continue;
@@ -56,9 +56,15 @@ int main() {
                                              static_cast<int32_t>(max_ctx), static_cast<int32_t>(q_len), dev);
     const ga::DecodeWorkspace w = ga::decode_workspace(L, c.num_heads, static_cast<int32_t>(batch),
                                                        static_cast<int32_t>(q_len), p);
-    std::printf("%d %d %d %d %d %d %d %d %.17g %.17g %.17g %.17g %d %d %d %d %zu\n", rc, L.is_global, L.window,
-                L.num_kv_heads, L.head_dim, L.group, L.rotary_dim, L.k_eq_v, L.theta, L.scale, L.softcap, L.pos_div,
-                p.n_wg, p.span_max, p.per_seq ? 1 : 0, p.tile ? 1 : 0, w.total);
+    // the int8 cache's plan (its own ring depth; never the bf16 tile kernel)
+    const ga::DecodePlan p8 = ga::decode_plan(L, c.num_heads, static_cast<int32_t>(batch),
+                                              static_cast<int32_t>(max_ctx), static_cast<int32_t>(q_len), dev, true);
+    const ga::DecodeWorkspace w8 = ga::decode_workspace(L, c.num_heads, static_cast<int32_t>(batch),
+                                                        static_cast<int32_t>(q_len), p8);
+    std::printf("%d %d %d %d %d %d %d %d %.17g %.17g %.17g %.17g %d %d %d %d %zu %d %d %d %zu\n", rc, L.is_global,
+                L.window, L.num_kv_heads, L.head_dim, L.group, L.rotary_dim, L.k_eq_v, L.theta, L.scale, L.softcap,
+                L.pos_div, p.n_wg, p.span_max, p.per_seq ? 1 : 0, p.tile ? 1 : 0, w.total, p8.n_wg, p8.per_seq ? 1 : 0,
+                p8.tile ? 1 : 0, w8.total);
   }
   return 0;
 }

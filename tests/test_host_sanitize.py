@@ -147,11 +147,15 @@ def test_host_logic_under_sanitizers(driver):
         exp = [int(ref["is_global"]), ref["window"], ref["num_kv_heads"], ref["head_dim"], ref["group"],
                ref["rotary_dim"], int(ref["k_eq_v"]), ref["theta"], ref["scale"], ref["softcap"], ref["pos_div"]]
         assert vals == exp, (layer, kw, vals, exp)
-        n_wg, span_max, per_seq, tile, total = (int(x) for x in got[12:])
+        n_wg, span_max, per_seq, tile, total, n_wg8, per_seq8, tile8, total8 = (int(x) for x in got[12:])
         b, m, ql = size[:3]
         if n_wg != -1:
             assert n_wg >= 1 and 1 <= span_max <= m and total > 0
             if per_seq:
                 assert n_wg == b
+            # int8 plan: never the bf16 tile kernel; one sequence per workgroup when per_seq
+            assert n_wg8 >= 1 and total8 > 0 and tile8 == 0
+            if per_seq8:
+                assert n_wg8 == b
     assert resolved > 300
     assert sum(1 for line in lines if len(line.split()) > 1 and line.split()[12] != "-1") > 300
