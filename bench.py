@@ -368,9 +368,9 @@ def decode_query(layer, multi=False):
 
 
 DECODE_KERNEL = {
-    "local_w1024": "decode_split_kernel<256,2,false,false,1> + decode_combine_kernel<256> (one workgroup per sequence)",
-    "local_w1024_q4": "decode_split_kernel<256,2,false,false,1> + decode_combine_kernel<256> (one workgroup per sequence)",
-    "local_w1024_int8": "decode_split_i8_kernel<256,2,false,false> + decode_combine_kernel<256>",
+    "local_w1024": "decode_split_kernel<256,2,false,false,1> (one workgroup per sequence, which writes the output)",
+    "local_w1024_q4": "decode_split_kernel<256,2,false,false,1> (one workgroup per sequence, which writes the output)",
+    "local_w1024_int8": "decode_split_i8_kernel<256,2,false,false> (one workgroup per sequence, which writes the output)",
     "global_keqv": "decode_plan_kernel + decode_split_kernel<512,16,true,false,1> + decode_combine_kernel<512>",
     "global_keqv_q4": "decode_plan_kernel + decode_tile_kernel<16,false> + decode_combine_kernel<512>",
     "global_keqv_int8": "decode_plan_kernel + decode_split_i8_kernel<512,16,true,false> + decode_combine_kernel<512>",
@@ -393,8 +393,19 @@ DECODE_WARMUP = 60
 
 
 def bench_decode(ga, reps=20, warm=DECODE_WARMUP):
-    """Gemma-4-12B decode step: one local and one global layer over 64 ragged contexts."""
+    """Gemma-4-12B decode step: one local and one global layer over 64 ragged contexts.
+
+    Every timed call follows a 1 GiB read that evicts the previous call's lines
+    from the last-level cache: in a model each layer's cache was last read a
+    whole step earlier, while here the same cache is read call after call (the
+    local layer's 0.54 GB would otherwise partly stay cached)."""
     import torch
+
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def cold():
+        torch.sum(flush_buf, dim=0, out=flush_out)
 
     B, Smax = DECODE_B, DECODE_SMAX
     ctx = decode_contexts()
@@ -414,6 +425,7 @@ def bench_decode(ga, reps=20, warm=DECODE_WARMUP):
             ga.attn_decode(GEMMA4_12B, layer, qt.view(B, 16, D), kc, vc, ctx_d, out=out, workspace=ws)
         timer = Timer()
         for _ in range(reps):
+            cold()
             timer.start("prologue")
             ga.qk_prologue(GEMMA4_12B, layer, q, None, q_out=qt, pos0=p32)
             timer.stop("prologue")
@@ -440,6 +452,7 @@ def bench_decode(ga, reps=20, warm=DECODE_WARMUP):
             ga.attn_decode_multi(GEMMA4_12B, layer, qm, kc, vc, ctx_d, out=outm, workspace=wsm)
         tm = Timer()
         for _ in range(reps):
+            cold()
             tm.start("m")
             ga.attn_decode_multi(GEMMA4_12B, layer, qm, kc, vc, ctx_d, out=outm, workspace=wsm)
             tm.stop("m")
@@ -461,6 +474,7 @@ def bench_decode(ga, reps=20, warm=DECODE_WARMUP):
             ga.attn_decode_int8(GEMMA4_12B, layer, q1, kq, ksq, vq, vsq, ctx_d, out=out1, workspace=ws)
         t8 = Timer()
         for _ in range(reps):
+            cold()
             t8.start("d8")
             ga.attn_decode_int8(GEMMA4_12B, layer, q1, kq, ksq, vq, vsq, ctx_d, out=out1, workspace=ws)
             t8.stop("d8")

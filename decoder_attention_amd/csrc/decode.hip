@@ -165,14 +165,16 @@ inline int64_t decode_grid(int32_t hkv, int32_t n_wg, int32_t n_cb, int32_t xcd_
 
 // Calls f(b, s_lo, s_hi, ctx) for every sequence b that this workgroup's range
 // touches, with [s_lo, s_hi) the sequence's keys in the range; uniform across
-// the workgroup.  The caller separates consecutive calls with a barrier.
+// the workgroup.  The caller separates consecutive calls with a barrier.  One
+// workgroup per sequence: f runs for the sequence even when it has no keys
+// to read (s_lo == s_hi), since that workgroup writes the sequence's output.
 template <class F>
 __device__ __forceinline__ void for_each_segment(const DecodeParams& p, int32_t wg, F&& f) {
   if (p.per_seq) {
     const int32_t b = wg;
     int32_t lo, ctx;
     seq_range(p, b, lo, ctx);
-    if (ctx > lo) f(b, lo, ctx, ctx);
+    f(b, lo, ctx, ctx);
     return;
   }
   const int64_t total = p.prefix[p.batch];
@@ -269,13 +271,40 @@ __device__ __forceinline__ void wait_tiles(int32_t n) {
 // each, over different keys): merged through LDS first; merge_buf is
 // [16 columns][D] fp32 and reuses a slot (both waves are past their last
 // tile when the first barrier returns).
+// One workgroup per sequence (p.per_seq) at head width <= 256: that
+// workgroup's (m, l, o) is the whole attention of its columns, so it writes
+// the output o / l (bf16) and the lse itself and no combine kernel runs; a
+// sequence with no keys gets zeros and -inf.  (Width 512 keeps the partial and
+// the combine: the extra code spilled registers in its kernels.)  `row` is the
+// output row (b*q_len + tok)*Hq + head, `lrow` the lse index
+// (b*Hq + head)*q_len + tok.
+template <int D>
+constexpr bool kFinalInKernel = D <= 256;
+template <int D>
+__device__ __forceinline__ void store_final4(const DecodeParams& p, int64_t row, int32_t d, f32x4 v, float inv) {
+  uint16_t* dst = p.out + row * D + d;
+  const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(v[0] * inv)) | (static_cast<uint32_t>(f32_to_bf16(v[1] * inv)) << 16);
+  const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(v[2] * inv)) | (static_cast<uint32_t>(f32_to_bf16(v[3] * inv)) << 16);
+  *reinterpret_cast<u32x2*>(dst) = u32x2{w0, w1};
+}
+__device__ __forceinline__ void store_final_lse(const DecodeParams& p, int64_t lrow, float m, float l) {
+  if (p.lse) p.lse[lrow] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+}
+
 template <int D, int kTeams, int kDB>
 __device__ __forceinline__ void write_partial(const DecodeParams& p, int64_t part, bool col_ok, const f32x4 (&o)[kDB],
                                               float m_run, float l_run, int32_t wave, int32_t member, int32_t dlo,
                                               int32_t grp, int32_t col, float* merge_buf, float (*m_w)[16],
-                                              float (*l_w)[16]) {
+                                              float (*l_w)[16], int64_t row, int64_t lrow) {
   if constexpr (kTeams == 1) {
-    if (col_ok) {
+    if (kFinalInKernel<D> && p.per_seq) {
+      if (col_ok) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) store_final4<D>(p, row, dlo + db * 16 + grp * 4, o[db], inv);
+        if (member == 0 && grp == 0) store_final_lse(p, lrow, m_run, l_run);
+      }
+    } else if (col_ok) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         float* dst = p.ws_o + part * D + dlo + db * 16 + grp * 4;
@@ -305,16 +334,26 @@ __device__ __forceinline__ void write_partial(const DecodeParams& p, int64_t par
     }
     __syncthreads();
     if (wave == 1 && col_ok) {
+      const float l_all =
+          l_w[0][col] * __builtin_amdgcn_exp2f(m_w[0][col] - m_ref) + l_w[1][col] * __builtin_amdgcn_exp2f(m_w[1][col] - m_ref);
+      const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         const f32x4 prev = *reinterpret_cast<const f32x4*>(merge_buf + col * D + (((db * 4 + grp) ^ col) << 2));
-        float* dst = p.ws_o + part * D + db * 16 + grp * 4;
-        *reinterpret_cast<f32x4*>(dst) = prev + o[db] * f;
+        if (kFinalInKernel<D> && p.per_seq) {
+          store_final4<D>(p, row, db * 16 + grp * 4, prev + o[db] * f, inv);
+        } else {
+          float* dst = p.ws_o + part * D + db * 16 + grp * 4;
+          *reinterpret_cast<f32x4*>(dst) = prev + o[db] * f;
+        }
       }
       if (grp == 0) {
-        p.ws_m[part] = m_all;
-        p.ws_l[part] =
-            l_w[0][col] * __builtin_amdgcn_exp2f(m_w[0][col] - m_ref) + l_w[1][col] * __builtin_amdgcn_exp2f(m_w[1][col] - m_ref);
+        if (kFinalInKernel<D> && p.per_seq) {
+          store_final_lse(p, lrow, m_all, l_all);
+        } else {
+          p.ws_m[part] = m_all;
+          p.ws_l[part] = l_all;
+        }
       }
     }
   }
@@ -563,11 +602,12 @@ void decode_split_kernel(DecodeParams p) {
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  // Partial of (sequence b, token tok, head): row ((b*q_len + tok)*Hq + head).
   // Partial of (sequence b, token tok, head) from workgroup w: slot w + b.
   const int64_t part = ((static_cast<int64_t>(blk.w) + b) * p.q_len + tok) * p.hq + head;
   write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, dmem, dlo, grp, col,
-                                reinterpret_cast<float*>(ks0), m_w, l_w);
+                                reinterpret_cast<float*>(ks0), m_w, l_w,
+                                (static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head,
+                                (static_cast<int64_t>(b) * p.hq + head) * p.q_len + tok);
   __syncthreads();   // LDS slots (and the merge buffer) are reused by the next segment
   });
 }
@@ -935,7 +975,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Partial of (sequence b, token tok, head) from workgroup w: slot w + b.
   const int64_t part = ((static_cast<int64_t>(blk.w) + b) * p.q_len + tok) * p.hq + head;
   write_partial<D, kTeams, kDB>(p, part, col_ok, o, m_run, l_run, wave, member, dlo, grp, col,
-                                reinterpret_cast<float*>(ks0), m_w, l_w);
+                                reinterpret_cast<float*>(ks0), m_w, l_w,
+                                (static_cast<int64_t>(b) * p.q_len + tok) * p.hq + head,
+                                (static_cast<int64_t>(b) * p.hq + head) * p.q_len + tok);
   __syncthreads();   // LDS slots (and the merge buffer) are reused by the next segment
   });
 }
@@ -1363,6 +1405,7 @@ hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t st
     e = launch_kernel(decode_split_kernel<D, G, KEQV, CAP, 1>, grid, dim3(DecodeShape<D, 1>::kWaves * 64), stream, pp);
   }
   if (e != hipSuccess) return e;
+  if (a.per_seq && kFinalInKernel<D>) return hipSuccess;   // each sequence's only workgroup wrote its output
   return launch_kernel(decode_combine_kernel<D>,
                        dim3(static_cast<uint32_t>(a.hq * a.q_len), static_cast<uint32_t>(a.batch)), dim3(64), stream,
                        prm);
