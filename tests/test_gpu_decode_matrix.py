@@ -79,13 +79,14 @@ def _check(name, out, lse, ro, rl, ctx, q_len):
                 assert np.all(o[b, t] == 0.0) and np.all(np.isneginf(l[b, :, t])), (name, b, t)
 
 
-def _run_bf16(ga, D, g, keqv, W, cap, q_len, B, Smax, hkv, seed, kv_start=None):
+def _run_bf16(ga, D, g, keqv, W, cap, q_len, B, Smax, hkv, seed, kv_start=None, empty=()):
     import torch
 
     kw = _config(D, g, keqv, W, cap, hkv)
     cfg = R.GemmaAttnConfig(**kw)
     name = _ids((D, g, keqv, W, cap, q_len)) + f"-B{B}"
     ctx = _contexts(seed, B, Smax, q_len)
+    ctx[list(empty)] = 0                    # sequences with nothing to read
     print(f"[decode matrix] {name} ctx={ctx[:6].tolist()}", flush=True)
     kc = normal_bf16(seed + 1, (B, Smax, hkv, D))
     vc = normal_bf16(seed + 2, (B, Smax, hkv, D))
@@ -100,13 +101,14 @@ def _run_bf16(ga, D, g, keqv, W, cap, q_len, B, Smax, hkv, seed, kv_start=None):
     _check(name, out, lse, ro, rl, ctx, q_len)
 
 
-def _run_int8(ga, D, g, keqv, W, cap, q_len, B, Smax, hkv, seed):
+def _run_int8(ga, D, g, keqv, W, cap, q_len, B, Smax, hkv, seed, empty=()):
     import torch
 
     kw = _config(D, g, keqv, W, cap, hkv)
     cfg = R.GemmaAttnConfig(**kw)
     name = "int8-" + _ids((D, g, keqv, W, cap, q_len)) + f"-B{B}"
     ctx = _contexts(seed, B, Smax, q_len)
+    ctx[list(empty)] = 0                    # sequences with nothing to read
     print(f"[decode matrix] {name} ctx={ctx[:6].tolist()}", flush=True)
     kc, ks = R.quantize_int8(bf16_bits_to_f64(normal_bf16(seed + 1, (B, Smax, hkv, D))).astype(np.float32))
     vc, vs = R.quantize_int8(bf16_bits_to_f64(normal_bf16(seed + 2, (B, Smax, hkv, D))).astype(np.float32))
@@ -151,6 +153,23 @@ def test_decode_one_workgroup_per_sequence(gpu, D, g, keqv, W, cap, q_len, hkv):
     B, Smax = 72, 120
     _run_bf16(gpu, D, g, keqv, W, cap, q_len, B=B, Smax=Smax, hkv=hkv, seed=6000 + D + q_len)
     _run_int8(gpu, D, g, keqv, W, cap, q_len, B=B, Smax=Smax, hkv=hkv, seed=6100 + D + q_len)
+
+
+@pytest.mark.parametrize("D,g,keqv,W,q_len", [(256, 2, False, 45, 1), (256, 2, False, 45, 4), (64, 4, False, 30, 4),
+                                               (512, 2, False, 40, 1)])
+def test_decode_one_workgroup_per_sequence_empty(gpu, D, g, keqv, W, q_len):
+    """One workgroup per sequence writes its sequence's output itself (width <= 256) or its
+    partial (width 512): sequences with no readable row (ctx 0, or kv_start at ctx) get zeros
+    and lse -inf, and their neighbours are unaffected."""
+    hkv = 8 if D != 64 else 16
+    B, Smax = 72, 120
+    kv_start = np.zeros(B, dtype=np.int32)
+    ctx = _contexts(6200 + D + q_len, B, Smax, q_len)
+    for b in (5, 40, 71):                   # kv_start at ctx: nothing readable
+        kv_start[b] = ctx[b]
+    _run_bf16(gpu, D, g, keqv, W, 0.0, q_len, B=B, Smax=Smax, hkv=hkv, seed=6200 + D + q_len, kv_start=kv_start,
+              empty=(3, 4, 70))
+    _run_int8(gpu, D, g, keqv, W, 50.0, q_len, B=B, Smax=Smax, hkv=hkv, seed=6300 + D + q_len, empty=(0, 3, 71))
 
 
 @pytest.mark.parametrize("D,g,keqv,W", [(256, 2, False, 45), (512, 16, True, 0), (64, 4, False, 0)])
