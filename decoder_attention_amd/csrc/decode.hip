@@ -378,15 +378,16 @@ void decode_split_kernel(DecodeParams p) {
 
   // Ring of slots per team, one LDS array per slot (so reads of one slot are
   // not ordered behind the copies landing in the others).  One column block:
-  // two slots, one tile in flight while one is computed (a third slot at
-  // head width 512, 48 KB, leaves room for three workgroups per CU instead of
-  // four, which measured slower: 3.9 against 4.6 TB/s on the global layer).
+  // two slots, one tile in flight while one is computed; at head width 512
+  // with keys as values three (48 KB, three workgroups per CU: 96 KB of tiles
+  // in flight per CU instead of 64 KB with four workgroups of two slots;
+  // 403.6 -> 394.1 us on the Gemma-4 global layer).
   // Several column blocks: one or two workgroups fill a CU (two waves per
   // SIMD), so the ring deepens to keep as many tiles in flight per CU.
   constexpr int kSlotBytes = kSlotElems * 2 * (KEQV ? 1 : 2);
   constexpr int kWgPerCu = 8 / Sh::kWaves;
   constexpr int kSlotsFit = (160 * 1024) / (kWgPerCu * kTeams * kSlotBytes);
-  constexpr int kSlots = CBW == 1 ? 2 : (kSlotsFit < 6 ? kSlotsFit : 6);
+  constexpr int kSlots = CBW == 1 ? ((KEQV && D == 512) ? 3 : 2) : (kSlotsFit < 6 ? kSlotsFit : 6);
   static_assert(kSlots >= 2 && kSlots <= 6, "ring depth");
   constexpr int kKE = kTeams * kSlotElems;
   __shared__ __attribute__((aligned(16))) uint16_t ks0[kKE];
@@ -656,9 +657,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(G <= 16, "at most 16 query heads per KV head");
   static_assert(kOps % kTeam == 0, "tile must split into whole 1 KB ops");
   static_assert(kTeams == 1 || kSlotBytes * kTeams >= 16 * D * 4, "merge buffer reuses slot 0");
-  // Ring depth.  Two slots (one tile in flight while one is computed): the
-  // conversion work makes this kernel issue-bound, and a third 16 KB slot at
-  // head width 512 halves the workgroups per CU, which measured slower.
+  // Ring depth.  Two slots (one tile in flight while one is computed).  At
+  // head width 512 with keys as values a third 16 KB slot did not leave room
+  // for three workgroups per CU, and four slots with two workgroups per CU
+  // measured 40% slower: with one wave per SIMD the conversion work is no
+  // longer hidden behind the other workgroups' waits.
   constexpr int kSlots = 2;
   // Copy ops each wave issues per tile (codes, then scales): the wait for the
   // oldest tile leaves the newer tile's ops outstanding.
@@ -669,15 +672,19 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) uint8_t ks0[kTeams * kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ks1[kTeams * kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ks2[kSlots > 2 ? kTeams * kSlotBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ks3[kSlots > 3 ? kTeams * kSlotBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t vs0[KEQV ? 16 : kTeams * kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vs1[KEQV ? 16 : kTeams * kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vs2[(KEQV || kSlots < 3) ? 16 : kTeams * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vs3[(KEQV || kSlots < 4) ? 16 : kTeams * kSlotBytes];
   __shared__ __attribute__((aligned(16))) float ksc0[kTeams * 64];
   __shared__ __attribute__((aligned(16))) float ksc1[kTeams * 64];
   __shared__ __attribute__((aligned(16))) float ksc2[kSlots > 2 ? kTeams * 64 : 4];
+  __shared__ __attribute__((aligned(16))) float ksc3[kSlots > 3 ? kTeams * 64 : 4];
   __shared__ __attribute__((aligned(16))) float vsc0[KEQV ? 4 : kTeams * 64];
   __shared__ __attribute__((aligned(16))) float vsc1[KEQV ? 4 : kTeams * 64];
   __shared__ __attribute__((aligned(16))) float vsc2[(KEQV || kSlots < 3) ? 4 : kTeams * 64];
+  __shared__ __attribute__((aligned(16))) float vsc3[(KEQV || kSlots < 4) ? 4 : kTeams * 64];
   __shared__ float m_w[2][16];
   __shared__ float l_w[2][16];
   // Partial scores of a two-wave team: [member][half][lane].
@@ -902,54 +909,51 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int i = decltype(I)::value;
     if constexpr (i == 0) return ks0 + team * kSlotBytes;
     else if constexpr (i == 1) return ks1 + team * kSlotBytes;
-    else return ks2 + team * kSlotBytes;
+    else if constexpr (i == 2) return ks2 + team * kSlotBytes;
+    else return ks3 + team * kSlotBytes;
   };
   auto vslot = [&](auto I) -> uint8_t* {
     constexpr int i = decltype(I)::value;
     if constexpr (KEQV) return kslot(I);
     else if constexpr (i == 0) return vs0 + team * kSlotBytes;
     else if constexpr (i == 1) return vs1 + team * kSlotBytes;
-    else return vs2 + team * kSlotBytes;
+    else if constexpr (i == 2) return vs2 + team * kSlotBytes;
+    else return vs3 + team * kSlotBytes;
   };
   auto kscl = [&](auto I) -> float* {
     constexpr int i = decltype(I)::value;
     if constexpr (i == 0) return ksc0 + team * 64;
     else if constexpr (i == 1) return ksc1 + team * 64;
-    else return ksc2 + team * 64;
+    else if constexpr (i == 2) return ksc2 + team * 64;
+    else return ksc3 + team * 64;
   };
   auto vscl = [&](auto I) -> float* {
     constexpr int i = decltype(I)::value;
     if constexpr (KEQV) return kscl(I);
     else if constexpr (i == 0) return vsc0 + team * 64;
     else if constexpr (i == 1) return vsc1 + team * 64;
-    else return vsc2 + team * 64;
+    else if constexpr (i == 2) return vsc2 + team * 64;
+    else return vsc3 + team * 64;
   };
   auto team_sync = [&]() {
     if constexpr (kTeam > 1) __syncthreads();
   };
-  // Wait for the oldest tile in flight: with a newer tile also in flight its
-  // ops stay outstanding.
-  auto wait_oldest = [&](bool newer_in_flight) __attribute__((always_inline)) {
-    if (kSlots > 2 && newer_in_flight) {
-      if (member == 0) wait_vmcnt<kOpsMember0>();
-      else wait_vmcnt<kOpsMember1>();
-    } else {
-      wait_vmcnt<0>();
-    }
-  };
   // The team's tiles are ti = team, team + kTeams, ...; tile k of the team
-  // sits in slot k % kSlots.
+  // sits in slot k % kSlots, and up to kSlots - 1 tiles are copied ahead.
+  // Before computing a tile its copies must have landed; the newer tiles'
+  // copies (kOpsMember0 or kOpsMember1 per wave each) may stay in flight.
   int32_t ti = team;
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  if (ti < n_t) copy_tile(ti, kslot(S0{}), vslot(S0{}), kscl(S0{}), vscl(S0{}));
-  if constexpr (kSlots > 2) {
-    if (ti + kTeams < n_t) copy_tile(ti + kTeams, kslot(S1{}), vslot(S1{}), kscl(S1{}), vscl(S1{}));
-  }
+  static_for([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    if (ti + i * kTeams < n_t) copy_tile(ti + i * kTeams, kslot(I), vslot(I), kscl(I), vscl(I));
+  }, std::make_integer_sequence<int, kSlots - 1>{});
   auto step = [&](auto I) __attribute__((always_inline)) -> bool {
     constexpr int kCur = decltype(I)::value;
     using Next = std::integral_constant<int, (kCur + kSlots - 1) % kSlots>;
-    wait_oldest(ti + kTeams < n_t);
+    const int32_t after = (n_t - 1 - ti) / kTeams;          // team tiles issued after this one, capped below
+    const int32_t newer = after < kSlots - 2 ? after : kSlots - 2;
+    if (member == 0) wait_tiles<kSlots - 2, kOpsMember0>(newer);
+    else wait_tiles<kSlots - 2, kOpsMember1>(newer);
     team_sync();
     const int32_t ta = ti + (kSlots - 1) * kTeams;
     if (ta < n_t) copy_tile(ta, kslot(Next{}), vslot(Next{}), kscl(Next{}), vscl(Next{}));
@@ -958,11 +962,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return ti < n_t;
   };
   while (ti < n_t) {
-    if (!step(std::integral_constant<int, 0>{})) break;
-    if (!step(std::integral_constant<int, 1>{})) break;
-    if constexpr (kSlots > 2) {
-      if (!step(std::integral_constant<int, 2>{})) break;
-    }
+    if (!static_all(step, std::make_integer_sequence<int, kSlots>{})) break;
   }
 
   l_run += __shfl_xor(l_run, 16, 64);

@@ -100,9 +100,12 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
   } else {
     // One round of workgroups on the device: the split kernel's workgroups
     // per CU follow from its LDS ring (two waves per workgroup, two waves per
-    // SIMD): two slots of 16 bf16 rows (or 32 int8 rows, the same bytes) per team.
+    // SIMD): slots of 16 bf16 rows (or 32 int8 rows, the same bytes) per team,
+    // two of them, or three for bf16 caches with keys as values at width 512
+    // (three workgroups per CU, more tiles in flight).
     const long long team = L.head_dim > 256 ? 2 : 1;
-    const long long lds = (2 / team) * 2 * 16LL * L.head_dim * 2 * (L.k_eq_v ? 1 : 2);
+    const long long slots = (!int8 && L.k_eq_v && L.head_dim == 512) ? 3 : 2;
+    const long long lds = (2 / team) * slots * 16LL * L.head_dim * 2 * (L.k_eq_v ? 1 : 2);
     per_cu = lds_cu / lds;
     if (per_cu > 4) per_cu = 4;
     if (per_cu < 1) per_cu = 1;
