@@ -212,6 +212,13 @@ void prefill_kernel(PrefillParams p) {
   constexpr int kWgPerCu = waves_per_simd<D, KEQV>() * 4 / kWaves;
   constexpr int kBufs = kWgPerCu * (3 * kTileBytes + kSxBytes) <= kLdsBudget ? 3 : 2;
   constexpr int kAhead = kBufs - 1;          // tiles in flight beyond the one computed
+  // Wave priority while a wave issues its matrix products (QK^T, PV): when
+  // both waves of a SIMD are ready, the one feeding the matrix core goes
+  // first and the other's softmax fills the gaps.  Same-box runs: Gemma-4
+  // global -4 to -5%, Gemma-3 window 512 -2 to -3%, Gemma-2 global -1 to -2.5%,
+  // Gemma-3 global -0.5 to -0.7%; the capped four-wave form (Gemma-2 window
+  // 4096) lost about 1%, so it keeps the default priority.
+  constexpr int kMatPrio = (CAP && !WIDE) ? 0 : 3;
 
   // One LDS array per ring slot: every access names its slot at compile time
   // (the loop is unrolled by the ring depth), so the compiler can tell a read
@@ -422,12 +429,14 @@ void prefill_kernel(PrefillParams p) {
       };
 #pragma unroll
       for (int ds = 0; ds < kLA; ++ds) a[ds] = kread(ds);
+      if constexpr (kMatPrio > 0) __builtin_amdgcn_s_setprio(kMatPrio);
 #pragma unroll
       for (int ds = 0; ds < kDS; ++ds) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ds % kLA], qf[ds], sacc, 0, 0, 0);
         if (ds + kLA < kDS) a[ds % kLA] = kread(ds + kLA);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (kMatPrio > 0) __builtin_amdgcn_s_setprio(0);
     }
     if (kSplit > 1) {
       // [wave][r/4][lane] float4 layout: consecutive lanes, consecutive 16 bytes.
@@ -554,6 +563,7 @@ void prefill_kernel(PrefillParams p) {
       bf16x8 va[kLV];
 #pragma unroll
       for (int v = 0; v < kLV; ++v) va[v] = vread(v);
+      if constexpr (kMatPrio > 0) __builtin_amdgcn_s_setprio(kMatPrio);
 #pragma unroll
       for (int v = 0; v < kV; ++v) {
         const int t = v / kDB;
@@ -568,6 +578,7 @@ void prefill_kernel(PrefillParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (kMatPrio > 0) __builtin_amdgcn_s_setprio(0);
     }
     // The next tile's copies must have landed before anyone reads them; the
     // copies of the tile after it may stay in flight.
