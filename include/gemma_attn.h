@@ -16,7 +16,9 @@
  *    contiguous: q [B,S,Hq,D], k and v [B,S,Hkv,D], caches [B,Smax,Hkv,D].
  *    Norm weights are fp32 [D].  Log-sum-exp outputs are fp32, natural log.
  *  - Every data pointer is a DEVICE pointer owned by the caller; the library
- *    allocates nothing, keeps no state between calls and is re-entrant.
+ *    allocates nothing, keeps no state between calls and is re-entrant (the
+ *    one exception: the fixed device array that gemma_attn_decode_multi_noalloc
+ *    uses in place of a workspace, see there).
  *    Configuration structs and layer structs are HOST pointers, read during the
  *    call only.
  *  - Device pointers must be 16-byte aligned.
