@@ -260,6 +260,34 @@ def test_prefill_integer_facts(gpu, D, g, W):
             assert np.array_equal(ob[0, :, hq], v[0, :, hq // g])
 
 
+# Short windows (at most 1/8 of the sequence): the XCDs sharing a (sequence, KV
+# head) pair take contiguous runs of its query blocks, the last run ending in
+# padding blocks, and every block past the first window visits its key tiles in
+# the shared rotated order.  (B, Hkv) give 1 or 2 pairs (8 or 4 XCDs per pair).
+RUNS = [(1, 1, 2, 256, 2100, 200, 0.0), (2, 1, 4, 256, 1700, 160, 50.0), (1, 2, 8, 256, 2500, 300, 0.0),
+        (1, 1, 4, 64, 3000, 96, 50.0), (2, 1, 2, 512, 1300, 150, 0.0)]
+
+
+@pytest.mark.parametrize("B,Hkv,g,D,S,W,cap", RUNS, ids=[f"B{r[0]}-Hkv{r[1]}-g{r[2]}-D{r[3]}-S{r[4]}-W{r[5]}"
+                                                         for r in RUNS])
+def test_prefill_short_window_block_runs(gpu, B, Hkv, g, D, S, W, cap):
+    ga = gpu
+    kw = dict(num_heads=g * Hkv, num_kv_heads=Hkv, head_dim=D, sliding_window=W, sliding_window_pattern=0,
+              attn_logit_softcapping=cap)
+    cfg = R.GemmaAttnConfig(**kw)
+    print(f"[prefill runs] B={B} Hkv={Hkv} g={g} D={D} S={S} W={W}", flush=True)
+    q = normal_bf16(830, (B, S, g * Hkv, D), scale=2.0)
+    k = normal_bf16(831, (B, S, Hkv, D))
+    v = normal_bf16(832, (B, S, Hkv, D))
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    out, lse = ga.attn_prefill(kw, 0, qd, kd, vd, want_lse=True)
+    again = ga.attn_prefill(kw, 0, qd, kd, vd)
+    ro, rl = R.prefill(cfg, 0, bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v))
+    assert_close(from_dev_f64(out), ro, what="short-window runs")
+    assert_close(from_dev_f64(lse), rl, what="short-window runs lse")
+    assert np.array_equal(from_dev_bf16_bits(out), from_dev_bf16_bits(again))
+
+
 def test_prefill_deterministic(gpu):
     ga = gpu
     cfg, L, q, k, v, _, _ = _layer_inputs(GEMMA2, 0, 2, 700, seed=800)
