@@ -21,7 +21,10 @@
 //   together belong to as few (sequence, KV head) pairs as possible -- they
 //   then stream the same K/V tiles through that XCD's L2 -- while every XCD
 //   gets the same amount of work; inside a pair, the longest causal rows go
-//   first.
+//   first.  On short windows the XCDs sharing a pair take contiguous runs of
+//   its blocks, and every block visits its window's tiles in an order shared
+//   by all blocks (the tile whose index is congruent to the step), so blocks
+//   running together read the same tile at the same time.
 //
 // K/V staging
 //   Tiles of 32 keys are copied HBM -> LDS by the gfx950 direct-to-LDS loads
@@ -50,6 +53,9 @@
 //     B = P^T from the score registers.  With keys-as-values the same LDS
 //     tile is both K and V.
 //   Tiles outside a wave's causal/window band are skipped by that wave.
+//   A wave raises its priority while it issues the matrix products, so the
+//   SIMD's other wave runs its softmax in the gaps (not on the capped
+//   four-wave form, where it measured slower).
 //
 // Output
 //   O^T leaves the accumulators through the idle ring: each wave parks its
