@@ -20,6 +20,9 @@ The same JSON line also carries
     stored as int8 codes with per-(token, head) scales (``*_int8``);
   * ``prefill_configs``: the Gemma-3-1B-shaped 6-layer stack and the
     Gemma-4-12B-shaped global layer (TFLOP/s per layer);
+  * ``prologue_ms`` / ``prologue_gbs`` (and the same per prefill config): the
+    QK prologue's time and its rate over the bytes it must move (q and k read
+    and written once), as it is HBM-bound;
   * ``cpu_baseline``: the fp64 oracle timed on the host's cores over a
     bounded sample of the same workload (``value``), and beside it over
     samples of the Gemma-3 stack, the Gemma-4 global layer and the decode
@@ -203,6 +206,14 @@ def run_layer_step(ga, kw, layer, t, timer=None, tag=""):
         timer.stop(f"prefill{tag}")
 
 
+def _prologue_bytes(kw, layer, B, S) -> int:
+    """Bytes the QK prologue must move: q and k read once and written once (bf16)."""
+    import decoder_attention_amd as ga
+
+    L = ga.resolve_layer(kw, layer)
+    return 2 * 2 * B * S * (kw["num_heads"] + L["num_kv_heads"]) * L["head_dim"]
+
+
 def _pair_traffic():
     """Mean HBM bytes per launch of the pair's prefill kernel (counter summary), or None."""
     t = measured_traffic("decoder_attention_amd/csrc/prefill.hip", "prefill_gemma2_pair_hbm_traffic.md")
@@ -240,6 +251,8 @@ def bench_pair(ga, steps, warmup):
         value=total_flops / (step_ms * 1e-3) / 1e12,
         prefill_ms={"local_w4096": pre[0], "global": pre[1]},
         prologue_ms={"local_w4096": pro[0], "global": pro[1]},
+        prologue_gbs={name: round(_prologue_bytes(kw, layer, B, S) / (pro[layer] * 1e-3) / 1e9, 1)
+                      for layer, name in ((0, "local_w4096"), (1, "global"))},
         prefill_tflops={"local_w4096": flops[0] / (pre[0] * 1e-3) / 1e12, "global": flops[1] / (pre[1] * 1e-3) / 1e12},
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=_pair_traffic(),
@@ -279,6 +292,7 @@ def bench_prefill_layer(ga, workload, layer, reps=10, traffic_key=None):
         run_layer_step(ga, kw, layer, t, timer)
     torch.cuda.synchronize()
     ms = float(np.mean(timer.ms("prefill")))
+    pro_ms = float(np.mean(timer.ms("prologue")))
     f = _flops(kw, layer, B, S)
     del t
     torch.cuda.empty_cache()
@@ -287,7 +301,8 @@ def bench_prefill_layer(ga, workload, layer, reps=10, traffic_key=None):
         traffic = traffic_of("decoder_attention_amd/csrc/prefill.hip", "prefill_gemma3_gemma4_hbm_traffic.md",
                              traffic_key)
     return dict(prefill_ms=round(ms, 4), tflops=round(f / (ms * 1e-3) / 1e12, 2),
-                prologue_ms=round(float(np.mean(timer.ms("prologue"))), 4), flops=f,
+                prologue_ms=round(pro_ms, 4),
+                prologue_gbs=round(_prologue_bytes(kw, layer, B, S) / (pro_ms * 1e-3) / 1e9, 1), flops=f,
                 roofline=mfma_roofline(f, ms, PREFILL_KERNEL[(workload, layer)], traffic))
 
 
@@ -715,6 +730,7 @@ def main():
         "roofline": pair["roofline"],
         "prefill_ms": pair["prefill_ms"],
         "prologue_ms": pair["prologue_ms"],
+        "prologue_gbs": pair["prologue_gbs"],
         "prefill_tflops": {k: round(v, 2) for k, v in pair["prefill_tflops"].items()},
     }
     if not a.no_extra and a.workload == "all":
