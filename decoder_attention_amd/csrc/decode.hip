@@ -378,16 +378,16 @@ void decode_split_kernel(DecodeParams p) {
 
   // Ring of slots per team, one LDS array per slot (so reads of one slot are
   // not ordered behind the copies landing in the others).  One column block:
-  // two slots, one tile in flight while one is computed; at head width 512
-  // with keys as values three (48 KB, three workgroups per CU: 96 KB of tiles
-  // in flight per CU instead of 64 KB with four workgroups of two slots;
-  // 403.6 -> 394.1 us on the Gemma-4 global layer).
+  // two slots, one tile in flight while one is computed.  (At head width 512
+  // with keys as values the launch reserves LDS for three workgroups per CU;
+  // a three-slot ring that kept two tiles in flight per workgroup was 4%
+  // slower on the Gemma-4 global layer, 408 against 392 us.)
   // Several column blocks: one or two workgroups fill a CU (two waves per
   // SIMD), so the ring deepens to keep as many tiles in flight per CU.
   constexpr int kSlotBytes = kSlotElems * 2 * (KEQV ? 1 : 2);
   constexpr int kWgPerCu = 8 / Sh::kWaves;
   constexpr int kSlotsFit = (160 * 1024) / (kWgPerCu * kTeams * kSlotBytes);
-  constexpr int kSlots = CBW == 1 ? ((KEQV && D == 512) ? 3 : 2) : (kSlotsFit < 6 ? kSlotsFit : 6);
+  constexpr int kSlots = CBW == 1 ? 2 : (kSlotsFit < 6 ? kSlotsFit : 6);
   static_assert(kSlots >= 2 && kSlots <= 6, "ring depth");
   constexpr int kKE = kTeams * kSlotElems;
   __shared__ __attribute__((aligned(16))) uint16_t ks0[kKE];
@@ -454,12 +454,14 @@ void decode_split_kernel(DecodeParams p) {
 
   // Copy this wave's share of tile ti (keys s_lo + 16*ti ...) into a slot.
   // Rows past s_hi repeat row s_hi - 1, so no row outside the sequence's
-  // range is read.
-  auto copy_tile = [&](int32_t ti, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
-    const int32_t k0 = s_lo + ti * kTK;
+  // range is read.  A tile that is not live (past the range) gets a zero-byte
+  // resource: its copies read no memory and write zeros into the slot.
+  auto copy_tile = [&](int32_t ti, uint16_t* kdst, uint16_t* vdst, bool live) __attribute__((always_inline)) {
+    const int32_t k0 = live ? s_lo + ti * kTK : 0;
     const int32_t last = s_hi - 1 - k0;
-    const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kseq + static_cast<int64_t>(k0) * row_pitch, kTK * row_pitch);
-    const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vseq + static_cast<int64_t>(k0) * row_pitch, kTK * row_pitch);
+    const uint32_t nbytes = live ? kTK * row_pitch : 0u;
+    const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kseq + static_cast<int64_t>(k0) * row_pitch, nbytes);
+    const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vseq + static_cast<int64_t>(k0) * row_pitch, nbytes);
     const int32_t ln = lane_here();
 #pragma unroll
     for (int i = 0; i < kWaveOps; ++i) {
@@ -573,25 +575,44 @@ void decode_split_kernel(DecodeParams p) {
   // wave's part of a tile and fences the slot being refilled (every wave
   // runs the same trips).
   auto team_sync = [&]() {
-    if constexpr (kTeam > 1) __syncthreads();
+    if constexpr (kTeam > 1) lds_barrier();
   };
   // The team's tiles are ti = team, team + kTeams, ...; tile k of the team
   // sits in slot k % kSlots, and up to kSlots - 1 tiles are copied ahead.
   // Before computing a tile, its copies must have landed; the newer tiles'
   // copies (kOpsPerTile per wave each) may stay in flight.
+  //
+  // With two slots a copy is issued only for a live tile and each step waits
+  // for all copies.  With three or more (several column blocks), every step
+  // issues one tile's copies (dead tiles past the range copy nothing), so the
+  // wait is one constant count, and no copy sits under a branch: behind such
+  // a branch the compiler lost track of which slot the copy writes and made
+  // the next read of that slot wait for every copy in flight.
+  constexpr bool kAlwaysIssue = kSlots > 2;
+  static_assert((kSlots - 2) * kOpsPerTile <= 63, "vmcnt range");
   int32_t ti = team;
   static_for([&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value;
-    if (ti + i * kTeams < n_t) copy_tile(ti + i * kTeams, kslot(I), vslot(I));
+    const bool live = ti + i * kTeams < n_t;
+    if (kAlwaysIssue || live) copy_tile(ti + i * kTeams, kslot(I), vslot(I), live);
   }, std::make_integer_sequence<int, kSlots - 1>{});
+  // With tiles left in flight across steps, Q^T (loaded before these copies)
+  // must be complete before the loop: a load still pending on its registers
+  // at the loop head made the compiler wait for every copy in flight before
+  // the first product of each pass over the ring.
+  if constexpr (kAlwaysIssue) wait_vmcnt<0>();
   auto step = [&](auto I) __attribute__((always_inline)) -> bool {
     constexpr int kCur = decltype(I)::value;
     using Next = std::integral_constant<int, (kCur + kSlots - 1) % kSlots>;
-    const int32_t after = (n_t - 1 - ti) / kTeams;          // team tiles issued after this one, capped below
-    wait_tiles<kSlots - 2, kOpsPerTile>(after < kSlots - 2 ? after : kSlots - 2);
+    if constexpr (kAlwaysIssue) {
+      wait_vmcnt<(kSlots - 2) * kOpsPerTile>();
+    } else {
+      const int32_t after = (n_t - 1 - ti) / kTeams;          // team tiles issued after this one, capped below
+      wait_tiles<kSlots - 2, kOpsPerTile>(after < kSlots - 2 ? after : kSlots - 2);
+    }
     team_sync();
     const int32_t ta = ti + (kSlots - 1) * kTeams;
-    if (ta < n_t) copy_tile(ta, kslot(Next{}), vslot(Next{}));
+    if (kAlwaysIssue || ta < n_t) copy_tile(ta, kslot(Next{}), vslot(Next{}), ta < n_t);
     compute(ti, kslot(I), vslot(I));
     ti += kTeams;
     return ti < n_t;
@@ -599,7 +620,9 @@ void decode_split_kernel(DecodeParams p) {
   while (ti < n_t) {
     if (!static_all(step, std::make_integer_sequence<int, kSlots>{})) break;
   }
-  (void)kOpsPerTile;
+  // The dead tiles' copies write their slots: they land before the merge
+  // buffer (slot 0) is written.
+  if constexpr (kAlwaysIssue) wait_vmcnt<0>();
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
@@ -657,17 +680,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(G <= 16, "at most 16 query heads per KV head");
   static_assert(kOps % kTeam == 0, "tile must split into whole 1 KB ops");
   static_assert(kTeams == 1 || kSlotBytes * kTeams >= 16 * D * 4, "merge buffer reuses slot 0");
-  // Ring depth.  Two slots (one tile in flight while one is computed).  At
-  // head width 512 with keys as values a third 16 KB slot did not leave room
-  // for three workgroups per CU, and four slots with two workgroups per CU
-  // measured 40% slower: with one wave per SIMD the conversion work is no
-  // longer hidden behind the other workgroups' waits.
+  // Ring depth.  Two slots (one tile in flight while one is computed), four
+  // workgroups per CU at head width 512 with keys as values.  Fewer
+  // workgroups per CU were slower on the Gemma-4 global layer, with the same
+  // ring and LDS reserved at launch (three per CU 284-296 us, two 602 us,
+  // against 245-272 us), and so was a three-slot ring (two tiles in flight,
+  // three per CU: 468 us): the code conversion makes each tile's work long,
+  // and the other workgroups' waves are what hide it.
   constexpr int kSlots = 2;
   // Copy ops each wave issues per tile (codes, then scales): the wait for the
   // oldest tile leaves the newer tile's ops outstanding.
   constexpr int kCodeOps = kWaveOps * (KEQV ? 1 : 2);
-  constexpr int kOpsMember0 = kCodeOps + (kTeam == 1 ? (KEQV ? 1 : 2) : 1);
-  constexpr int kOpsMember1 = kCodeOps + (KEQV ? 0 : 1);
+  constexpr int kOpsPerTile = kCodeOps + (KEQV ? 1 : 2);
 
   __shared__ __attribute__((aligned(16))) uint8_t ks0[kTeams * kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t ks1[kTeams * kSlotBytes];
@@ -781,10 +805,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float* kscale = p.ks + sc_off;
   const float* vscale = KEQV ? kscale : p.vs + sc_off;
 
-  // Copy this wave's share of tile ti into a slot; member 0 also copies the
-  // tile's key scales and the last member its value scales (64 lanes, key
-  // lane & 31, so the upper half repeats the lower).  Rows past s_hi repeat
-  // row s_hi - 1.
+  // Copy this wave's share of tile ti into a slot, and the tile's key (and
+  // value) scales (64 lanes, key lane & 31, so the upper half repeats the
+  // lower).  Every member of a team copies the scales, the same bytes to the
+  // same place: with the copy under a branch on the member, the compiler lost
+  // track of which LDS array it writes and waited for every copy in flight
+  // before the next LDS read.  Rows past s_hi repeat row s_hi - 1.
   auto copy_tile = [&](int32_t ti, uint8_t* kdst, uint8_t* vdst, float* kscd, float* vscd) __attribute__((always_inline)) {
     const int32_t k0 = s_lo + ti * kTK8;
     const int32_t last = s_hi - 1 - k0;
@@ -802,8 +828,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (!KEQV) copy_to_lds<16, kStreamAux>(vrs, off, vdst + op * 1024);
     }
     const uint32_t koff = static_cast<uint32_t>(min(ln & 31, last)) * 4u;
-    if (member == 0) copy_to_lds<4, kStreamAux>(raw_rsrc(kscale + k0, kTK8 * 4), koff, kscd);
-    if (!KEQV && member == kTeam - 1) copy_to_lds<4, kStreamAux>(raw_rsrc(vscale + k0, kTK8 * 4), koff, vscd);
+    copy_to_lds<4, kStreamAux>(raw_rsrc(kscale + k0, kTK8 * 4), koff, kscd);
+    if (!KEQV) copy_to_lds<4, kStreamAux>(raw_rsrc(vscale + k0, kTK8 * 4), koff, vscd);
   };
 
   auto compute = [&](int32_t ti, const uint8_t* kb, const uint8_t* vb, const float* kscs, const float* vscs) __attribute__((always_inline)) {
@@ -833,7 +859,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // only after the next tile's team barrier, which follows this read.
       sx[(member * 2 + 0) * 64 + ln] = sacc[0];
       sx[(member * 2 + 1) * 64 + ln] = sacc[1];
-      __syncthreads();
+      lds_barrier();   // the next tile's copies stay in flight
       sacc[0] += sx[((1 - member) * 2 + 0) * 64 + ln];
       sacc[1] += sx[((1 - member) * 2 + 1) * 64 + ln];
     }
@@ -936,12 +962,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     else return vsc3 + team * 64;
   };
   auto team_sync = [&]() {
-    if constexpr (kTeam > 1) __syncthreads();
+    if constexpr (kTeam > 1) lds_barrier();
   };
   // The team's tiles are ti = team, team + kTeams, ...; tile k of the team
   // sits in slot k % kSlots, and up to kSlots - 1 tiles are copied ahead.
   // Before computing a tile its copies must have landed; the newer tiles'
-  // copies (kOpsMember0 or kOpsMember1 per wave each) may stay in flight.
+  // copies (kOpsPerTile per wave each) may stay in flight.
   int32_t ti = team;
   static_for([&](auto I) __attribute__((always_inline)) {
     constexpr int i = decltype(I)::value;
@@ -952,8 +978,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     using Next = std::integral_constant<int, (kCur + kSlots - 1) % kSlots>;
     const int32_t after = (n_t - 1 - ti) / kTeams;          // team tiles issued after this one, capped below
     const int32_t newer = after < kSlots - 2 ? after : kSlots - 2;
-    if (member == 0) wait_tiles<kSlots - 2, kOpsMember0>(newer);
-    else wait_tiles<kSlots - 2, kOpsMember1>(newer);
+    wait_tiles<kSlots - 2, kOpsPerTile>(newer);
     team_sync();
     const int32_t ta = ti + (kSlots - 1) * kTeams;
     if (ta < n_t) copy_tile(ta, kslot(Next{}), vslot(Next{}), kscl(Next{}), vscl(Next{}));
@@ -1221,7 +1246,7 @@ void decode_tile_kernel(DecodeParams p) {
       const f32x4* other = sx + (wave ^ 1) * 256 + ln;
 #pragma unroll
       for (int r = 0; r < 16; r += 4) mine[(r / 4) * 64] = f32x4{sacc[r], sacc[r + 1], sacc[r + 2], sacc[r + 3]};
-      __syncthreads();
+      lds_barrier();   // the next tile's copies stay in flight
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
         const f32x4 t4 = other[(r / 4) * 64];
@@ -1402,7 +1427,13 @@ hipError_t launch_t(const DecodeArgs& a, const DecodeParams& prm, hipStream_t st
                         stream, pp);
     }
   } else {
-    e = launch_kernel(decode_split_kernel<D, G, KEQV, CAP, 1>, grid, dim3(DecodeShape<D, 1>::kWaves * 64), stream, pp);
+    // Keys as values at width 512: the two-slot ring holds 32 KB, so four
+    // workgroups would share a CU; 16 KB more of LDS per workgroup makes it
+    // three, the round the plan sizes the grid for (Gemma-4 global layer:
+    // 393 us at four per CU, 388 at three, 387 at two, 525 at one).
+    constexpr uint32_t kReserve = (KEQV && D == 512) ? 16384u : 0u;
+    e = launch_kernel(decode_split_kernel<D, G, KEQV, CAP, 1>, grid, dim3(DecodeShape<D, 1>::kWaves * 64), stream, pp,
+                      kReserve);
   }
   if (e != hipSuccess) return e;
   if (a.per_seq && kFinalInKernel<D>) return hipSuccess;   // each sequence's only workgroup wrote its output

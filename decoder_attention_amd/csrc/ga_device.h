@@ -64,6 +64,23 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_
   else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, voff, 0, 0, 2);
 }
 
+// Workgroup barrier for LDS traffic that leaves direct-to-LDS copies in
+// flight.  __syncthreads() carries a workgroup fence, and a direct-to-LDS copy
+// counts as an LDS write on the vector-memory counter, so the compiler puts
+// s_waitcnt vmcnt(0) before every such barrier: each barrier inside a
+// copy-ahead loop would wait for the tiles still meant to be in flight.  Here
+// the wave waits only for its own LDS reads and writes (lgkmcnt(0)), so after
+// the barrier every wave's LDS stores are visible and every wave's reads of
+// the previous contents are done.  Callers wait for the copies they need
+// (vmcnt) before it.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // gfx9 encoding: lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // Buffer resource over nbytes from base (raw addressing, 32-bit offsets).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int32_t>(nbytes), 0x00020000);

@@ -8,11 +8,13 @@ namespace ga {
 
 // Launch a kernel that takes one parameter struct and return the launch's own
 // status (hipLaunchKernel reports it directly, so no stale error from an
-// earlier, unrelated call is picked up).
+// earlier, unrelated call is picked up).  `lds_reserve` bytes of dynamic LDS
+// that the kernel does not use limit how many of its workgroups share a CU.
 template <class P>
-inline hipError_t launch_kernel(void (*fn)(P), dim3 grid, dim3 block, hipStream_t stream, P p) {
+inline hipError_t launch_kernel(void (*fn)(P), dim3 grid, dim3 block, hipStream_t stream, P p,
+                                uint32_t lds_reserve = 0) {
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, lds_reserve, stream);
 }
 
 // Launchers return hipErrorNotSupported for a shape with no kernel

@@ -99,10 +99,11 @@ DecodePlan decode_plan(const gemma_attn_layer& L, int32_t num_heads, int32_t bat
     per_cu = 2;
   } else {
     // One round of workgroups on the device: the split kernel's workgroups
-    // per CU follow from its LDS ring (two waves per workgroup, two waves per
-    // SIMD): slots of 16 bf16 rows (or 32 int8 rows, the same bytes) per team,
-    // two of them, or three for bf16 caches with keys as values at width 512
-    // (three workgroups per CU, more tiles in flight).
+    // per CU follow from its LDS (two waves per workgroup, two waves per
+    // SIMD): two slots of 16 bf16 rows (or 32 int8 rows, the same bytes) per
+    // team, plus, for bf16 caches with keys as values at width 512, a third
+    // slot's worth that the launch reserves so that three workgroups share a
+    // CU.
     const long long team = L.head_dim > 256 ? 2 : 1;
     const long long slots = (!int8 && L.k_eq_v && L.head_dim == 512) ? 3 : 2;
     const long long lds = (2 / team) * slots * 16LL * L.head_dim * 2 * (L.k_eq_v ? 1 : 2);

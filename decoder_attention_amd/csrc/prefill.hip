@@ -451,7 +451,7 @@ void prefill_kernel(PrefillParams p) {
       const f32x4* other = reinterpret_cast<const f32x4*>(sx_lds) + (wave ^ 1) * 256 + ln;
 #pragma unroll
       for (int r = 0; r < 16; r += 4) mine[(r / 4) * 64] = f32x4{sacc[r], sacc[r + 1], sacc[r + 2], sacc[r + 3]};
-      __syncthreads();
+      lds_barrier();   // the copies issued for later tiles stay in flight
       if (need) {
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
@@ -589,7 +589,7 @@ void prefill_kernel(PrefillParams p) {
     // The next tile's copies must have landed before anyone reads them; the
     // copies of the tile after it may stay in flight.
     if (kAhead > 1 && it + 2 < n_tiles) wait_vmcnt<(kAhead > 1 ? kLoadsPerTile : 0)>(); else wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();
     ++it;
   };
   while (it < n_tiles) {
