@@ -7,7 +7,10 @@ One step = one pass of the hot path over the Gemma-2-2B-shaped layer pair
 query_pre_attn_scalar 256, RoPE base 1e4): QK prologue + prefill attention of
 the local layer (window 4096) and of the global layer.  ``value`` is the
 step's unmasked attention FLOPs (4*D per allowed query-key pair) divided by
-the step time, in TFLOP/s, with every input already resident in HBM.
+the step time, in TFLOP/s, with every input already resident in HBM.  The K
+timed steps run back to back with events only before the first and after the
+last; the per-kernel launch times below come from a second pass of K steps
+with an event pair around every launch.
 
 The same JSON line also carries
   * ``roofline``: the prefill kernel's algorithmic FLOPs per launch over its
@@ -29,8 +32,8 @@ The same JSON line also carries
     step (``configs``), with the CPU model and the threads used.
 Every ``roofline`` block (the pair's, one per layer in ``prefill_configs``,
 and the decode one) divides the kernel's algorithmic work per launch by its
-mean launch time from HIP events recorded on the launch stream around the
-timed launches (``timing`` says so); ``traffic`` is the HBM bytes per launch
+mean launch time from HIP events recorded on the launch stream around its
+launches (``timing`` says which); ``traffic`` is the HBM bytes per launch
 from the committed rocprofv3 counter summary under ``profiles/`` while the
 kernel source still hashes to the value recorded there, else null.
 ``measured_ceiling`` holds what library code reaches on the same GPU in the
@@ -230,18 +233,25 @@ def bench_pair(ga, steps, warmup):
         for layer in (0, 1):
             run_layer_step(ga, kw, layer, layers[layer])
     torch.cuda.synchronize()
-    timer = Timer()
+    # The timed steps carry no events between their launches (an event record
+    # between two kernels idles the GPU for a few microseconds); the launch
+    # times per kernel come from a second, instrumented pass of as many steps.
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(steps):
         for layer in (0, 1):
-            run_layer_step(ga, kw, layer, layers[layer], timer, tag=str(layer))
+            run_layer_step(ga, kw, layer, layers[layer])
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = start.elapsed_time(end) / steps
+    timer = Timer()
+    for _ in range(steps):
+        for layer in (0, 1):
+            run_layer_step(ga, kw, layer, layers[layer], timer, tag=str(layer))
+    torch.cuda.synchronize()
     pre = {layer: float(np.mean(timer.ms(f"prefill{layer}"))) for layer in (0, 1)}
     pro = {layer: float(np.mean(timer.ms(f"prologue{layer}"))) for layer in (0, 1)}
     total_flops = flops[0] + flops[1]
@@ -259,7 +269,9 @@ def bench_pair(ga, steps, warmup):
                       kernel="prefill_kernel<256,2,false,true,WIDE>: local WIDE=false (4 waves), global WIDE=true (8)",
                       flops_per_launch={"local_w4096": flops[0], "global": flops[1]},
                       avg_launch_ms={"local_w4096": round(pre[0], 4), "global": round(pre[1], 4)},
-                      timing=TIMING + "; achieved = both layers' FLOPs over their summed mean launch times"),
+                      timing="HIP events on the launch stream around each launch of an instrumented pass of as many "
+                             "steps, run after the timed ones; mean over those launches; achieved = both layers' FLOPs "
+                             "over their summed mean launch times"),
         layers=layers,
     )
 
