@@ -154,6 +154,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                            _VP, ctypes.c_size_t, _VP]
     lib.gemma_attn_prefill_ragged.argtypes = [cfgp, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
     lib.gemma_attn_prefill_ragged.restype = ctypes.c_int
+    lib.gemma_attn_prefill_qrope.argtypes = [cfgp, i32, i32, i32, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.gemma_attn_prefill_qrope.restype = ctypes.c_int
     lib.gemma_attn_decode_int8.restype = ctypes.c_int
     lib.gemma_qk_prologue_cache_int8.argtypes = [cfgp, i32, i32, i32, i32] + [_VP] * 12
     lib.gemma_qk_prologue_cache_int8.restype = ctypes.c_int
@@ -217,18 +219,25 @@ def _expect(t, shape, name):
 # ----------------------------------------------------------------------------- entry points
 def qk_prologue(cfg, layer_idx, q, k=None, q_out=None, k_out=None, q_norm_w=None, k_norm_w=None,
                 pos0=None, stream=None):
-    """gemma_qk_prologue; returns (q_out, k_out).  Pass q_out=q for in place."""
+    """gemma_qk_prologue; returns (q_out, k_out).  Pass q_out=q for in place; q=None processes the keys
+    only (q_out is then None)."""
     import torch
 
     cfg = Config.from_any(cfg)
     L = resolve_layer(cfg, layer_idx)
-    B, S = q.shape[0], q.shape[1]
-    _expect(q, (B, S, cfg.num_heads, L["head_dim"]), "q")
+    if q is None and k is None:
+        raise ValueError("qk_prologue needs q or k")
+    B, S = (q if q is not None else k).shape[:2]
+    if q is not None:
+        _expect(q, (B, S, cfg.num_heads, L["head_dim"]), "q")
     if k is not None:
         _expect(k, (B, S, L["num_kv_heads"], L["head_dim"]), "k")
-    if q_out is None:
+    if q is None:
+        q_out = None
+    elif q_out is None:
         q_out = torch.empty_like(q)
-    _expect(q_out, tuple(q.shape), "q_out")
+    if q is not None:
+        _expect(q_out, tuple(q.shape), "q_out")
     if k is not None and k_out is None:
         k_out = torch.empty_like(k)
     if k is not None:
@@ -241,7 +250,7 @@ def qk_prologue(cfg, layer_idx, q, k=None, q_out=None, k_out=None, q_norm_w=None
     bf = torch.bfloat16
     rc = load().gemma_qk_prologue(
         ctypes.byref(cfg.to_c()), int(layer_idx), B, S, _ptr(q, bf, "q"), _ptr(k, bf, "k"),
-        _ptr(q_out, bf, "q_out"), _ptr(k_out, bf, "k_out") if k is not None else None,
+        _ptr(q_out, bf, "q_out") if q is not None else None, _ptr(k_out, bf, "k_out") if k is not None else None,
         _ptr(q_norm_w, torch.float32, "q_norm_w"), _ptr(k_norm_w, torch.float32, "k_norm_w"),
         _ptr(pos0, torch.int32, "pos0"), _stream(stream))
     _check(rc, "gemma_qk_prologue")
@@ -280,6 +289,37 @@ def attn_prefill(cfg, layer_idx, q, k, v=None, out=None, lse=None, want_lse=Fals
         rc = load().gemma_attn_prefill_ragged(*args, _ptr(seq_start, torch.int32, "seq_start"),
                                               _ptr(seq_end, torch.int32, "seq_end"), _stream(stream))
         _check(rc, "gemma_attn_prefill_ragged")
+    return (out, lse) if lse is not None else out
+
+
+def attn_prefill_qrope(cfg, layer_idx, q_raw, k, v=None, pos0=None, out=None, lse=None, want_lse=False,
+                       stream=None):
+    """gemma_attn_prefill_qrope: q_raw [B,S,Hq,D] before rotary (rotated inside the attention kernel), k already
+    processed (qk_prologue with q=None); returns out, or (out, lse) when an lse buffer is asked for."""
+    import torch
+
+    cfg = Config.from_any(cfg)
+    L = resolve_layer(cfg, layer_idx)
+    B, S = q_raw.shape[0], q_raw.shape[1]
+    _expect(q_raw, (B, S, cfg.num_heads, L["head_dim"]), "q_raw")
+    _expect(k, (B, S, L["num_kv_heads"], L["head_dim"]), "k")
+    if v is not None and not L["k_eq_v"]:
+        _expect(v, (B, S, L["num_kv_heads"], L["head_dim"]), "v")
+    if pos0 is not None:
+        _expect(pos0, (B,), "pos0")
+    if out is None:
+        out = torch.empty_like(q_raw)
+    _expect(out, tuple(q_raw.shape), "out")
+    if want_lse and lse is None:
+        lse = torch.empty((B, cfg.num_heads, S), dtype=torch.float32, device=q_raw.device)
+    if lse is not None:
+        _expect(lse, (B, cfg.num_heads, S), "lse")
+    bf = torch.bfloat16
+    rc = load().gemma_attn_prefill_qrope(
+        ctypes.byref(cfg.to_c()), int(layer_idx), B, S, _ptr(q_raw, bf, "q_raw"), _ptr(k, bf, "k"),
+        None if L["k_eq_v"] else _ptr(v, bf, "v"), _ptr(pos0, torch.int32, "pos0"), _ptr(out, bf, "out"),
+        _ptr(lse, torch.float32, "lse"), _stream(stream))
+    _check(rc, "gemma_attn_prefill_qrope")
     return (out, lse) if lse is not None else out
 
 

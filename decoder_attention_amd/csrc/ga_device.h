@@ -64,6 +64,36 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_
   else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, voff, 0, 0, 2);
 }
 
+// Rotary helpers shared by the QK prologue (its per-token tables) and the
+// attention kernel's in-register query rotation, so that both turn a query
+// by exactly the same arithmetic.
+//
+// Frequency of rotate-half pair i in revolutions per position:
+// c0 * w1^i with w1 = theta^(-2/r) and c0 = 1 / (2 pi pos_div), by one fixed
+// chain of fp64 products: i = 16a + 8b + e gives ((c0 * w8^b) * w16^a) * w1^e,
+// multiplied out in that order (w2 = w1 w1, w4 = w2 w2, w8 = w4 w4,
+// w16 = w8 w8).  A few fp64 ulps from the exact power.
+__device__ __forceinline__ double rotary_rev_freq(int32_t i, double w1, double c0) {
+  const double w2 = w1 * w1, w4 = w2 * w2, w8 = w4 * w4, w16 = w8 * w8;
+  double f = ((i >> 3) & 1) ? c0 * w8 : c0;
+  for (int32_t a = 0; a < (i >> 4); ++a) f *= w16;
+  for (int32_t e = 0; e < (i & 7); ++e) f *= w1;
+  return f;
+}
+// (cos, sin) at position p for frequency f (revolutions per position): the
+// fractional part of p * f taken in fp64, then the hardware fp32 cosine and
+// sine, which take revolutions (measured on gfx950 against fp64: within
+// 1.3e-7).
+__device__ __forceinline__ float2 rotary_cos_sin(double p, double f) {
+  const float r = static_cast<float>(__builtin_amdgcn_fract(p * f));
+  return make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
+}
+// One rotated element: x cos + partner * s, with s = -sin for the lower half
+// of a pair (partner = upper) and +sin for the upper half (partner = lower).
+__device__ __forceinline__ float rotary_turn(float x, float partner, float c, float s) {
+  return __builtin_fmaf(x, c, partner * s);
+}
+
 // Workgroup barrier for LDS traffic that leaves direct-to-LDS copies in
 // flight.  __syncthreads() carries a workgroup fence, and a direct-to-LDS copy
 // counts as an LDS write on the vector-memory counter, so the compiler puts

@@ -4,7 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 namespace ga {
+
+// Host side of the shared rotary arithmetic (rotary_rev_freq in ga_device.h):
+// w1 = theta^(-2/r) and c0 = 1 / (2 pi pos_div), formed once per launch by the
+// prologue's and the attention kernel's launchers alike.
+inline double rotary_w1(double theta, int32_t rotary_dim) { return std::pow(theta, -2.0 / rotary_dim); }
+inline double rotary_c0(double pos_div) {
+  return 1.0 / (2.0 * 3.14159265358979323846 * (pos_div > 0.0 ? pos_div : 1.0));
+}
 
 // Launch a kernel that takes one parameter struct and return the launch's own
 // status (hipLaunchKernel reports it directly, so no stale error from an
@@ -61,6 +71,12 @@ struct PrefillArgs {
   const int32_t* seq_end;
   double scale, softcap;
   int32_t xcds;               // L2 domains (XCDs) the dispatcher deals workgroups over, round-robin
+  // Fused query rotary (q_rope = 1): q holds the queries before rotary; the
+  // kernel turns them by the layer's full-width rotary at positions
+  // pos0[b] + s (pos0 device [B] or null), divided by rope_pos_div.
+  int32_t q_rope;
+  const int32_t* pos0;
+  double rope_theta, rope_pos_div;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -68,12 +68,13 @@ void* device_scratch() {
 
 int prefill_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq, const void* q,
                    const void* k, const void* v, void* out, float* lse, const int32_t* seq_start,
-                   const int32_t* seq_end, void* stream) {
+                   const int32_t* seq_end, void* stream, bool q_rope = false, const int32_t* pos0 = nullptr) {
   gemma_attn_layer L;
   const int rc = ga::resolve_layer(cfg, layer_idx, &L);
   if (rc != GA_OK) return rc;
   if (batch < 0 || seq < 0) return GA_ERR_INVALID_ARG;
   if (!ga::attn_dim_supported(L.head_dim) || !ga::attn_group_supported(L.group)) return GA_ERR_UNSUPPORTED;
+  if (q_rope && (L.head_dim != 256 || L.k_eq_v || L.rotary_dim != L.head_dim)) return GA_ERR_UNSUPPORTED;
   if (batch > 65535 || L.num_kv_heads > 65535) return GA_ERR_UNSUPPORTED;
   if (batch == 0 || seq == 0) return GA_OK;
   if (!dev_ok(q) || !dev_ok(k) || !dev_ok(out)) return GA_ERR_INVALID_ARG;
@@ -98,6 +99,10 @@ int prefill_common(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batc
   a.scale = L.scale;
   a.softcap = L.softcap;
   a.xcds = current_device_shape().xcds;
+  a.q_rope = q_rope ? 1 : 0;
+  a.pos0 = pos0;
+  a.rope_theta = L.theta;
+  a.rope_pos_div = L.pos_div;
   return hip_rc(ga::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -191,20 +196,21 @@ int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
   if (static_cast<long long>(batch) * seq > INT_MAX) return GA_ERR_UNSUPPORTED;
   if (!ga::prologue_dim_supported(L.head_dim)) return GA_ERR_UNSUPPORTED;
   if (batch == 0 || seq == 0) return GA_OK;
-  if (!dev_ok(q_in) || !dev_ok(q_out)) return GA_ERR_INVALID_ARG;
+  if (!q_in && !k_in) return GA_ERR_INVALID_ARG;
+  if (q_in && (!dev_ok(q_in) || !dev_ok(q_out))) return GA_ERR_INVALID_ARG;
   if (k_in && !dev_ok(k_out)) return GA_ERR_INVALID_ARG;
   if (k_in && !ga::aligned16(k_in)) return GA_ERR_INVALID_ARG;
   if ((q_norm_w && !ga::aligned16(q_norm_w)) || (k_norm_w && !ga::aligned16(k_norm_w))) return GA_ERR_INVALID_ARG;
   ga::PrologueArgs a{};
   a.batch = batch;
   a.seq = seq;
-  a.hq = cfg->num_heads;
+  a.hq = q_in ? cfg->num_heads : 0;      // keys only: no query rows
   a.hkv = L.num_kv_heads;
   a.dim = L.head_dim;
   a.rotary_dim = L.rotary_dim;
   a.q_in = q_in;
   a.k_in = k_in;
-  a.q_out = q_out;
+  a.q_out = q_in ? q_out : nullptr;
   a.k_out = k_in ? k_out : nullptr;
   a.q_norm_w = q_norm_w;
   a.k_norm_w = k_norm_w;
@@ -223,6 +229,12 @@ int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
 int gemma_attn_prefill(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
                        const void* q, const void* k, const void* v, void* out, float* lse, void* stream) {
   return prefill_common(cfg, layer_idx, batch, seq, q, k, v, out, lse, nullptr, nullptr, stream);
+}
+
+int gemma_attn_prefill_qrope(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
+                             const void* q_raw, const void* k, const void* v, const int32_t* pos0, void* out,
+                             float* lse, void* stream) {
+  return prefill_common(cfg, layer_idx, batch, seq, q_raw, k, v, out, lse, nullptr, nullptr, stream, true, pos0);
 }
 
 int gemma_attn_prefill_ragged(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,

@@ -96,6 +96,11 @@ struct PrefillParams {
   float scale_log2;   // scale * log2(e)            (no cap)
   float cap_in2;      // 2 * scale * log2(e) / cap  (cap: exp2 argument of tanh)
   float cap_log2;     // cap * log2(e)
+  // Query rotary inside the kernel (the fused form): position pos0[b] + s
+  // (pos0 null: s); pair i turns by (pos0[b] + s) * rot_c0 * rot_w1^i
+  // revolutions, rot_w1 = theta^(-2/D), rot_c0 = 1 / (2 pi pos_div).
+  const int32_t* pos0;
+  double rot_w1, rot_c0;
 };
 
 template <int D>
@@ -197,7 +202,7 @@ constexpr int positions_per_block() {
   return (pf_waves<D, KEQV, WIDE>() / DSplit<D>::value) * kCols / G;
 }
 
-template <int D, int G, bool KEQV, bool CAP, bool WIDE>
+template <int D, int G, bool KEQV, bool CAP, bool WIDE, bool QROPE>
 __global__ __launch_bounds__((pf_waves<D, KEQV, WIDE>() * 64)) __attribute__((amdgpu_waves_per_eu(waves_per_simd<D, KEQV>(), 2)))
 void prefill_kernel(PrefillParams p) {
   constexpr int kWaves = pf_waves<D, KEQV, WIDE>();
@@ -343,8 +348,10 @@ void prefill_kernel(PrefillParams p) {
     const int32_t lc = (pc % kRowChunks) ^ swz<D>(row);       // logical chunk held at pc
     doff[i] = static_cast<uint32_t>(row) * row_pitch + static_cast<uint32_t>(lc) * 16u;
   }
-  auto issue = [&](int32_t kt, auto B) {
-    const int64_t tile_off = (static_cast<int64_t>(kt) * p.hkv + kvh) * D * 2;
+  // A dead tile (live = false) gets a zero-byte resource: its copies read no
+  // memory and write zeros into the slot.
+  auto issue = [&](int32_t kt, auto B, bool live = true) {
+    const int64_t tile_off = live ? (static_cast<int64_t>(kt) * p.hkv + kvh) * D * 2 : 0;
     const char* kt_base = kbase + tile_off;
     const char* vt_base = vbase + tile_off;
     // Rows outside the kept range repeat its first or last row (masked), so
@@ -352,8 +359,9 @@ void prefill_kernel(PrefillParams p) {
     const bool tail = kt < r_lo || kt + kKeys > r_hi;
     uint16_t* kdst = kslot(B);
     uint16_t* vdst = vslot(B);
-    const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kt_base, kKeys * row_pitch);
-    const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vt_base, kKeys * row_pitch);
+    const uint32_t nbytes = live ? kKeys * row_pitch : 0u;
+    const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kt_base, nbytes);
+    const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vt_base, nbytes);
 #pragma unroll
     for (int i = 0; i < kWaveLoads; ++i) {
       if (kOps % kWaves != 0 && wave * kWaveLoads + i >= kOps) break;   // uniform per wave
@@ -375,15 +383,27 @@ void prefill_kernel(PrefillParams p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  if (0 < n_tiles) issue(tile_key(0), I0{});
-  if (kAhead > 1 && 1 < n_tiles) issue(tile_key(1), I1{});
+  const int32_t pos_base = (QROPE && p.pos0) ? p.pos0[b] : 0;   // first position of sequence b
 
-  // Q^T operand: lane holds d = ds*16 + h*8 + [0, 8) of its column.
+  // Q^T operand: lane holds d = ds*16 + h*8 + [0, 8) of its column.  With the
+  // fused query rotary q is loaded before the first tiles' copies, so that the
+  // rotation can start while those are in flight.
   bf16x8 qf[kDS];
-  {
+  auto load_q = [&]() {
     const uint16_t* qrow = p.q + ((static_cast<int64_t>(b) * S + pos_m) * p.hq + head) * D + dlo + h * 8;
 #pragma unroll
     for (int ds = 0; ds < kDS; ++ds) qf[ds] = *reinterpret_cast<const bf16x8*>(qrow + ds * 16);
+  };
+  if constexpr (QROPE) {
+    // Every first-tile copy is issued (dead ones copy nothing), so the wait
+    // for q below is one constant count.
+    load_q();
+    issue(tile_key(0), I0{}, 0 < n_tiles);
+    if constexpr (kAhead > 1) issue(tile_key(1), I1{}, 1 < n_tiles);
+  } else {
+    if (0 < n_tiles) issue(tile_key(0), I0{});
+    if (kAhead > 1 && 1 < n_tiles) issue(tile_key(1), I1{});
+    load_q();
   }
 
   f32x16 o[kDB];
@@ -392,7 +412,52 @@ void prefill_kernel(PrefillParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  wait_vmcnt<0>();   // Q^T and the first tiles
+  if constexpr (!QROPE) wait_vmcnt<0>();   // Q^T and the first tiles
+  if constexpr (QROPE) {
+    // Wait for q only: the copies of the first tiles, issued after it, stay
+    // in flight during the rotation.
+    static_assert(kOps % kWaves == 0, "every wave issues kLoadsPerTile copies per tile");
+    wait_vmcnt<(kAhead > 1 ? 2 : 1) * kLoadsPerTile>();
+    // The fused form: q arrives before rotary, and each lane turns its own
+    // column in registers.  Rotate-half pairs (i, i + D/2): the lane holds
+    // i = ds*16 + h*8 + [0, 8) at step ds < kDS/2 and its partner at step
+    // ds + kDS/2.  The frequencies follow rotary_rev_freq's chain of products
+    // (c0, times w8 for h = 1, times w16 per step, times w1 per element) and
+    // the angle, cosine, sine and turn are rotary_cos_sin and rotary_turn, the
+    // prologue's own arithmetic, so the rotated query rounds to the same bf16
+    // values as the prologue's output.
+    static_assert(kSplit == 1, "the rotary partner of a dim must sit in the same lane");
+    const double pd = static_cast<double>(pos_base) + static_cast<double>(pos_m);
+    const double w1 = p.rot_w1;
+    const double w2 = w1 * w1, w4 = w2 * w2, w8 = w4 * w4, w16 = w8 * w8;
+    double f_ds = h ? p.rot_c0 * w8 : p.rot_c0;
+#pragma unroll
+    for (int ds = 0; ds < kDS / 2; ++ds) {
+      u32x4 lo = __builtin_bit_cast(u32x4, qf[ds]);
+      u32x4 hi = __builtin_bit_cast(u32x4, qf[ds + kDS / 2]);
+      double f = f_ds;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 cs0 = rotary_cos_sin(pd, f);
+        f *= w1;
+        const float2 cs1 = rotary_cos_sin(pd, f);
+        f *= w1;
+        const float a0 = lo_bf16(lo[e]), a1 = hi_bf16(lo[e]);
+        const float b0 = lo_bf16(hi[e]), b1 = hi_bf16(hi[e]);
+        lo[e] = pack_bf16x2(rotary_turn(a0, b0, cs0.x, -cs0.y), rotary_turn(a1, b1, cs1.x, -cs1.y));
+        hi[e] = pack_bf16x2(rotary_turn(b0, a0, cs0.x, cs0.y), rotary_turn(b1, a1, cs1.x, cs1.y));
+      }
+      qf[ds] = __builtin_bit_cast(bf16x8, lo);
+      qf[ds + kDS / 2] = __builtin_bit_cast(bf16x8, hi);
+      f_ds *= w16;
+    }
+    // Pin the rotated values here, before the wait for the tiles: left alone,
+    // the compiler moved the whole rotation (register-only work) past that
+    // wait and the barrier, next to its first use.
+#pragma unroll
+    for (int ds = 0; ds < kDS; ++ds) asm volatile("" : "+v"(qf[ds]));
+    wait_vmcnt<0>();   // the first tiles
+  }
   __syncthreads();
 
   int32_t it = 0;
@@ -667,7 +732,7 @@ void prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int D, int G, bool KEQV, bool CAP, bool WIDE = false>
+template <int D, int G, bool KEQV, bool CAP, bool WIDE = false, bool QROPE = false>
 hipError_t launch_t(const PrefillArgs& a, const PrefillParams& prm, hipStream_t stream) {
   constexpr int kP = positions_per_block<D, G, KEQV, WIDE>();
   PrefillParams pp = prm;
@@ -685,13 +750,23 @@ hipError_t launch_t(const PrefillArgs& a, const PrefillParams& prm, hipStream_t 
   pp.xcd_runs = a.window > 0 && static_cast<int64_t>(a.window) * 8 <= a.seq;
   const int64_t blocks = static_cast<int64_t>(npairs) * pad;
   if (blocks > 0x7fffffff) return hipErrorNotSupported;
-  return launch_kernel(prefill_kernel<D, G, KEQV, CAP, WIDE>, dim3(static_cast<uint32_t>(blocks)),
+  return launch_kernel(prefill_kernel<D, G, KEQV, CAP, WIDE, QROPE>, dim3(static_cast<uint32_t>(blocks)),
                        dim3(pf_waves<D, KEQV, WIDE>() * 64), stream, pp);
 }
 
 template <int D, int G>
 hipError_t dispatch_flags(const PrefillArgs& a, const PrefillParams& prm, hipStream_t s) {
   const bool cap = a.softcap > 0.0;
+  if (a.q_rope) {
+    // The fused query rotary: width 256, keys and values separate.
+    if constexpr (D == 256) {
+      if (a.k_eq_v) return hipErrorNotSupported;
+      const bool global = a.window <= 0 || a.window >= a.seq;
+      if (cap && global) return launch_t<D, G, false, true, true, true>(a, prm, s);
+      return cap ? launch_t<D, G, false, true, false, true>(a, prm, s) : launch_t<D, G, false, false, false, true>(a, prm, s);
+    }
+    return hipErrorNotSupported;
+  }
   if (a.k_eq_v) return cap ? launch_t<D, G, true, true>(a, prm, s) : launch_t<D, G, true, false>(a, prm, s);
   if constexpr (D == 256) {
     const bool global = a.window <= 0 || a.window >= a.seq;
@@ -740,6 +815,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   prm.scale_log2 = static_cast<float>(a.scale * log2e);
   prm.cap_in2 = a.softcap > 0.0 ? static_cast<float>(2.0 * a.scale * log2e / a.softcap) : 0.f;
   prm.cap_log2 = static_cast<float>(a.softcap * log2e);
+  prm.pos0 = a.pos0;
+  prm.rot_w1 = a.q_rope ? rotary_w1(a.rope_theta, a.dim) : 0.0;
+  prm.rot_c0 = a.q_rope ? rotary_c0(a.rope_pos_div) : 0.0;
   switch (a.dim) {
     case 64: return dispatch_group<64>(a, prm, stream);
     case 256: return dispatch_group<256>(a, prm, stream);

@@ -16,11 +16,13 @@
 //    rows; the next item's 16-byte row loads are issued before the current
 //    item is worked on, so they stay in flight under its table build and row
 //    math;
-//  - the rotary frequencies w_i = theta^(-2i/r) (fp64) and the norm weights
-//    are formed once per workgroup; per item, each token's cos/sin(p * w_i)
-//    (angle reduced to [-pi, pi] in fp64 with a two-term 2*pi, fp32 sincos)
-//    goes to an LDS table laid out per element, with the rotate-half sign
-//    folded in, so every element is one multiply and one FMA;
+//  - the rotary frequencies theta^(-2i/r) / (2 pi pos_div), in revolutions
+//    per position (fp64, rotary_rev_freq), and the norm weights are formed
+//    once per workgroup; per item, each token's cos/sin (the fractional part
+//    of p times the frequency in fp64, then the hardware fp32 cosine and sine,
+//    rotary_cos_sin) goes to an LDS table laid out per element, with the
+//    rotate-half sign folded in, so every element is one multiply and one FMA
+//    (rotary_turn);
 //  - each head row of width D is handled by D/8 lanes holding 8 contiguous
 //    bf16; the RMS (and int8 absmax) reductions run inside those lanes with
 //    DPP and lane swaps, and only on rows that have a norm weight.
@@ -50,9 +52,6 @@ constexpr int kLoads = 7;               // 16-byte row loads per lane per item
 constexpr int32_t tab_tokens(int32_t dim) {
   return dim <= 256 ? (4096 / dim < 64 ? 4096 / dim : 64) : 3584 / dim;
 }
-constexpr double kInv2Pi = 0.15915494309189533577;
-constexpr double kTwoPiHi = 6.283185307179586232;          // 2*pi rounded to double
-constexpr double kTwoPiLo = 2.4492935982947064e-16;        // 2*pi - kTwoPiHi
 
 struct ProParams {
   const uint16_t* q_in;
@@ -71,8 +70,8 @@ struct ProParams {
   float* v_scales;
   int32_t tokens, rows_per_item;
   int32_t seq, hq, hkv, rotary_dim, max_ctx;   // max_ctx > 0: cache mode
-  double theta;
-  double pos_div;
+  double rot_w1;    // theta^(-2/r)
+  double rot_c0;    // 1 / (2 pi pos_div)
   float eps, offset;
 };
 
@@ -218,9 +217,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SHFL ?
   u32x4 cur[kLoads];
   TokInfo nt_cur = fetch_tok(j);
   load_item(j, cur);
-  // Once per workgroup: (p / pos_div) * w_i, formed as p * (w_i / pos_div);
+  // Once per workgroup: the frequencies in revolutions per position;
   // the norm weights; the pass-through entries.
-  for (int32_t i = tid; i < half; i += kThreads) omega[i] = pow(p.theta, -2.0 * i / p.rotary_dim) / p.pos_div;
+  for (int32_t i = tid; i < half; i += kThreads) omega[i] = rotary_rev_freq(i, p.rot_w1, p.rot_c0);
   for (int32_t d = tid; d < dim; d += kThreads) {
     wtab[0][d] = p.qw ? p.qw[d] + p.offset : 1.0f;
     wtab[1][d] = p.kw ? p.kw[d] + p.offset : 1.0f;
@@ -245,13 +244,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SHFL ?
     for (int32_t e = tid; e < ntok * half; e += kThreads) {
       const int32_t tt = e / half;
       const int32_t i = e - tt * half;
-      const double ang = static_cast<double>(tok_pos[it][tt]) * omega[i];
-      const double k = rint(ang * kInv2Pi);
-      const double red = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
-      float sn, cn;
-      sincosf(static_cast<float>(red), &sn, &cn);
-      cs_tab[tt * dim + i] = make_float2(cn, -sn);
-      cs_tab[tt * dim + half + i] = make_float2(cn, sn);
+      const float2 cs = rotary_cos_sin(static_cast<double>(tok_pos[it][tt]), omega[i]);
+      cs_tab[tt * dim + i] = make_float2(cs.x, -cs.y);
+      cs_tab[tt * dim + half + i] = make_float2(cs.x, cs.y);
     }
     __syncthreads();
 
@@ -336,7 +331,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SHFL ?
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int e = 2 * e2 + h;
-          const float rot = x[e] * c2[2 * h] + partner[e] * c2[2 * h + 1];
+          const float rot = rotary_turn(x[e], partner[e], c2[2 * h], c2[2 * h + 1]);
           y[e] = any_keep && (is_v || d0 + e >= p.rotary_dim) ? x[e] : rot;   // v rows, pass-through part
         }
       }
@@ -444,8 +439,8 @@ hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream) {
   p.hq = a.hq;
   p.hkv = a.hkv;
   p.rotary_dim = a.rotary_dim;
-  p.theta = a.theta;
-  p.pos_div = a.pos_div > 0.0 ? a.pos_div : 1.0;
+  p.rot_w1 = a.rotary_dim > 0 ? rotary_w1(a.theta, a.rotary_dim) : 0.0;
+  p.rot_c0 = rotary_c0(a.pos_div);
   p.eps = a.eps;
   p.offset = a.offset;
   // Rows per item: kLoads passes of the block, fewer when the tokens an item

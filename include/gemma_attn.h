@@ -124,10 +124,14 @@ int gemma_attn_resolve_layer(const gemma_attn_config* cfg, int32_t layer_idx, ge
  * q_in [B,S,Hq,D] -> q_out, k_in [B,S,Hkv,D] -> k_out; bf16.  Outputs may alias
  * their inputs exactly (in place) but must not partially overlap them.
  * k_in may be NULL (then k_out is ignored): queries only, as in decode.
+ * q_in may be NULL (then q_out is ignored): keys only, for
+ * gemma_attn_prefill_qrope, which rotates the queries itself.  Not both.
  * q_norm_w / k_norm_w: fp32 [D] device arrays, or NULL for no norm on that side.
  * pos0: device int32 [B] first position of each sequence, or NULL for zeros.
  * Values are never normed or rotated.  Accumulation is fp32; the angle is
- * formed and reduced modulo 2*pi in fp64; outputs round to nearest even.
+ * formed in fp64 in revolutions (p * theta^(-2i/r) / (2 pi pos_div)), reduced
+ * to its fractional part there, and evaluated by the hardware fp32 cosine and
+ * sine; outputs round to nearest even.
  */
 int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
                       const void* q_in, const void* k_in, void* q_out, void* k_out,
@@ -152,6 +156,26 @@ int gemma_qk_prologue(const gemma_attn_config* cfg, int32_t layer_idx, int32_t b
 int gemma_attn_prefill(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
                        const void* q, const void* k, const void* v, void* out, float* lse,
                        void* stream);
+
+/*
+ * gemma_attn_prefill with the query rotary done inside the attention kernel:
+ * the prologue's step 2 for q (no query norm) without its write and re-read
+ * of q.  q_raw [B,S,Hq,D] bf16 holds the queries before rotary; each
+ * workgroup turns the columns it loads in registers, in the prologue's pairs
+ * (i, i + D/2) by the angle (p / pos_div) * theta^(-2i/D), p = pos0[b] + s,
+ * and rounds them to bf16 as the prologue does before the products.  k must
+ * already be processed (gemma_qk_prologue with q_in = NULL); v and the rest as
+ * for gemma_attn_prefill.  pos0: device int32 [B], or NULL for zeros.
+ * The rotation is the prologue's own arithmetic (the same fp64 angles,
+ * hardware cosine and sine, and fused multiply-add), so without a query norm
+ * the result equals gemma_qk_prologue + gemma_attn_prefill bit for bit.
+ * For layers with no query norm and a full-width rotary (r = D), at head width
+ * 256 with separate keys and values (the Gemma 2 layers); other layers return
+ * GA_ERR_UNSUPPORTED and take gemma_qk_prologue + gemma_attn_prefill.
+ */
+int gemma_attn_prefill_qrope(const gemma_attn_config* cfg, int32_t layer_idx, int32_t batch, int32_t seq,
+                             const void* q_raw, const void* k, const void* v, const int32_t* pos0, void* out,
+                             float* lse, void* stream);
 
 /*
  * gemma_attn_prefill over a padded batch.  generate() on the Gemma, Gemma 2

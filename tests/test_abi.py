@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(ga):
                           "gemma_attn_decode_workspace_size", "gemma_attn_decode", "gemma_attn_strerror",
                           "gemma_attn_decode_multi", "gemma_attn_decode_multi_workspace_size",
                           "gemma_qk_prologue_cache", "gemma_attn_decode_int8", "gemma_qk_prologue_cache_int8",
-                          "gemma_kv_quantize_int8", "gemma_attn_prefill_ragged", "gemma_attn_decode_multi_noalloc"}
+                          "gemma_kv_quantize_int8", "gemma_attn_prefill_ragged", "gemma_attn_decode_multi_noalloc",
+                          "gemma_attn_prefill_qrope"}
     lib = ctypes.CDLL(ga.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -128,6 +129,18 @@ def test_argument_errors_before_any_launch(ga):
     pro = ga.Config(num_heads=8, num_kv_heads=4, head_dim=96).to_c()
     assert lib.gemma_qk_prologue(ref(pro), 0, 1, 8, fake, fake, fake, fake, None, None, None, None) == ga.GA_ERR_UNSUPPORTED
     assert lib.gemma_qk_prologue(ref(good), 0, 1, 8, fake, fake, fake, None, None, None, None, None) == ga.GA_ERR_INVALID_ARG
+    # keys only needs k; neither q nor k is an error
+    assert lib.gemma_qk_prologue(ref(good), 0, 1, 8, None, None, None, None, None, None, None, None) == ga.GA_ERR_INVALID_ARG
+    assert lib.gemma_qk_prologue(ref(good), 0, 1, 8, None, fake, None, None, None, None, None, None) == ga.GA_ERR_INVALID_ARG
+    # the fused query rotary: width 256, separate values, full-width rotary only
+    QR = lib.gemma_attn_prefill_qrope
+    assert QR(ref(good), 0, 1, 8, None, fake, fake, None, fake, None, None) == ga.GA_ERR_INVALID_ARG
+    assert QR(ref(good), 0, 0, 8, None, None, None, None, None, None, None) == ga.GA_OK
+    for bad in (ga.Config(num_heads=4, num_kv_heads=1, head_dim=64),
+                ga.Config(num_heads=8, num_kv_heads=1, head_dim=512, k_eq_v=True),
+                ga.Config(num_heads=8, num_kv_heads=4, head_dim=256, k_eq_v=True),
+                ga.Config(num_heads=8, num_kv_heads=4, head_dim=256, partial_rotary_factor=0.5)):
+        assert QR(ref(bad.to_c()), 0, 1, 8, fake, fake, fake, None, fake, None, None) == ga.GA_ERR_UNSUPPORTED
     keqv = ga.Config(num_heads=8, num_kv_heads=1, head_dim=512, k_eq_v=True).to_c()
     need = lib.gemma_attn_decode_workspace_size(ref(keqv), 0, 4, 1000)
     assert need > 0
