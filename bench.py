@@ -4,13 +4,17 @@
 
 One step = one pass of the hot path over the Gemma-2-2B-shaped layer pair
 (B=2, S=8192, 8 query heads, 4 KV heads, head width 256, logit soft cap 50,
-query_pre_attn_scalar 256, RoPE base 1e4): QK prologue + prefill attention of
-the local layer (window 4096) and of the global layer.  ``value`` is the
-step's unmasked attention FLOPs (4*D per allowed query-key pair) divided by
-the step time, in TFLOP/s, with every input already resident in HBM.  The K
-timed steps run back to back with events only before the first and after the
-last; the per-kernel launch times below come from a second pass of K steps
-with an event pair around every launch.
+query_pre_attn_scalar 256, RoPE base 1e4): QK-norm/rotary and prefill
+attention of the local layer (window 4096) and of the global layer.  The
+Gemma 2 layers have no query norm, so the step takes the fused form: the
+prologue processes the keys and the prefill kernel rotates the queries as it
+loads them (gemma_attn_prefill_qrope, bit-identical to prologue + prefill).
+``value`` is the step's unmasked attention FLOPs (4*D per allowed query-key
+pair) divided by the step time, in TFLOP/s, with every input already resident
+in HBM.  The K timed steps run back to back with events only before the first
+and after the last; the per-kernel launch times below come from a second pass
+of K steps with an event pair around every launch.  ``step_forms`` also times
+the prologue-then-prefill form over K steps.
 
 The same JSON line also carries
   * ``roofline``: the prefill kernel's algorithmic FLOPs per launch over its
@@ -24,8 +28,8 @@ The same JSON line also carries
   * ``prefill_configs``: the Gemma-3-1B-shaped 6-layer stack and the
     Gemma-4-12B-shaped global layer (TFLOP/s per layer);
   * ``prologue_ms`` / ``prologue_gbs`` (and the same per prefill config): the
-    QK prologue's time and its rate over the bytes it must move (q and k read
-    and written once), as it is HBM-bound;
+    QK prologue's time and its rate over the bytes it must move (k, and q
+    outside the fused pair, read and written once), as it is HBM-bound;
   * ``cpu_baseline``: the fp64 oracle timed on the host's cores over a
     bounded sample of the same workload (``value``), and beside it over
     samples of the Gemma-3 stack, the Gemma-4 global layer and the decode
@@ -197,24 +201,33 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
 
 
-def run_layer_step(ga, kw, layer, t, timer=None, tag=""):
+def run_layer_step(ga, kw, layer, t, timer=None, tag="", fused=False):
+    """One layer of the hot path.  fused: the prologue processes the keys only and the prefill kernel rotates
+    the queries as it loads them (gemma_attn_prefill_qrope; layers without a query norm)."""
     if timer:
         timer.start(f"prologue{tag}")
-    ga.qk_prologue(kw, layer, t["q"], t["k"], q_out=t["qt"], k_out=t["kt"], q_norm_w=t["qw"], k_norm_w=t["kw"])
+    if fused:
+        ga.qk_prologue(kw, layer, None, t["k"], k_out=t["kt"], k_norm_w=t["kw"])
+    else:
+        ga.qk_prologue(kw, layer, t["q"], t["k"], q_out=t["qt"], k_out=t["kt"], q_norm_w=t["qw"], k_norm_w=t["kw"])
     if timer:
         timer.stop(f"prologue{tag}")
         timer.start(f"prefill{tag}")
-    ga.attn_prefill(kw, layer, t["qt"], t["kt"], t["v"], out=t["out"])
+    if fused:
+        ga.attn_prefill_qrope(kw, layer, t["q"], t["kt"], t["v"], out=t["out"])
+    else:
+        ga.attn_prefill(kw, layer, t["qt"], t["kt"], t["v"], out=t["out"])
     if timer:
         timer.stop(f"prefill{tag}")
 
 
-def _prologue_bytes(kw, layer, B, S) -> int:
-    """Bytes the QK prologue must move: q and k read once and written once (bf16)."""
+def _prologue_bytes(kw, layer, B, S, keys_only=False) -> int:
+    """Bytes the QK prologue must move: q (unless keys only) and k read once and written once (bf16)."""
     import decoder_attention_amd as ga
 
     L = ga.resolve_layer(kw, layer)
-    return 2 * 2 * B * S * (kw["num_heads"] + L["num_kv_heads"]) * L["head_dim"]
+    heads = (0 if keys_only else kw["num_heads"]) + L["num_kv_heads"]
+    return 2 * 2 * B * S * heads * L["head_dim"]
 
 
 def _pair_traffic():
@@ -230,27 +243,36 @@ def bench_pair(ga, steps, warmup):
     layers = {layer: layer_tensors(cfg_id, kw, layer, B, S, norm) for layer in (0, 1)}
     flops = {layer: _flops(kw, layer, B, S) for layer in (0, 1)}
     for _ in range(warmup):
-        for layer in (0, 1):
-            run_layer_step(ga, kw, layer, layers[layer])
+        for fused in (True, False):
+            for layer in (0, 1):
+                run_layer_step(ga, kw, layer, layers[layer], fused=fused)
     torch.cuda.synchronize()
+
+    def timed(fused):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            for layer in (0, 1):
+                run_layer_step(ga, kw, layer, layers[layer], fused=fused)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
     # The timed steps carry no events between their launches (an event record
     # between two kernels idles the GPU for a few microseconds); the launch
     # times per kernel come from a second, instrumented pass of as many steps.
+    # The step is the fused form (keys-only prologue, query rotary in the
+    # prefill kernel); the prologue-then-prefill form is timed after it for
+    # comparison.
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
-        for layer in (0, 1):
-            run_layer_step(ga, kw, layer, layers[layer])
-    end.record()
-    torch.cuda.synchronize()
+    step_ms = timed(True)
     wall = time.perf_counter() - t0
-    step_ms = start.elapsed_time(end) / steps
+    unfused_ms = timed(False)
     timer = Timer()
     for _ in range(steps):
         for layer in (0, 1):
-            run_layer_step(ga, kw, layer, layers[layer], timer, tag=str(layer))
+            run_layer_step(ga, kw, layer, layers[layer], timer, tag=str(layer), fused=True)
     torch.cuda.synchronize()
     pre = {layer: float(np.mean(timer.ms(f"prefill{layer}"))) for layer in (0, 1)}
     pro = {layer: float(np.mean(timer.ms(f"prologue{layer}"))) for layer in (0, 1)}
@@ -259,14 +281,19 @@ def bench_pair(ga, steps, warmup):
     return dict(
         step_ms=step_ms, wall_s=wall, total_flops=total_flops,
         value=total_flops / (step_ms * 1e-3) / 1e12,
+        step_forms={
+            "fused_query_rotary": dict(ms=round(step_ms, 4), tflops=round(total_flops / (step_ms * 1e-3) / 1e12, 2)),
+            "prologue_then_prefill": dict(ms=round(unfused_ms, 4),
+                                          tflops=round(total_flops / (unfused_ms * 1e-3) / 1e12, 2))},
         prefill_ms={"local_w4096": pre[0], "global": pre[1]},
         prologue_ms={"local_w4096": pro[0], "global": pro[1]},
-        prologue_gbs={name: round(_prologue_bytes(kw, layer, B, S) / (pro[layer] * 1e-3) / 1e9, 1)
+        prologue_gbs={name: round(_prologue_bytes(kw, layer, B, S, keys_only=True) / (pro[layer] * 1e-3) / 1e9, 1)
                       for layer, name in ((0, "local_w4096"), (1, "global"))},
         prefill_tflops={"local_w4096": flops[0] / (pre[0] * 1e-3) / 1e12, "global": flops[1] / (pre[1] * 1e-3) / 1e12},
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=_pair_traffic(),
-                      kernel="prefill_kernel<256,2,false,true,WIDE>: local WIDE=false (4 waves), global WIDE=true (8)",
+                      kernel="prefill_kernel<256,2,false,true,WIDE,true> (query rotary in the kernel): local "
+                             "WIDE=false (4 waves), global WIDE=true (8)",
                       flops_per_launch={"local_w4096": flops[0], "global": flops[1]},
                       avg_launch_ms={"local_w4096": round(pre[0], 4), "global": round(pre[1], 4)},
                       timing="HIP events on the launch stream around each launch of an instrumented pass of as many "
@@ -734,9 +761,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) fp32 rounded to bf16; no weights)",
-        "config": {"workload": "Gemma-2-2B-shaped layer pair: QK prologue + prefill attention of one local "
-                               "(window 4096) and one global layer; B2 S8192 Hq8 Hkv4 D256, softcap 50, qpas 256, "
-                               "RoPE 1e4",
+        "config": {"workload": "Gemma-2-2B-shaped layer pair: QK prologue (keys) + prefill attention with the "
+                               "query rotary in the kernel, of one local (window 4096) and one global layer; "
+                               "B2 S8192 Hq8 Hkv4 D256, softcap 50, qpas 256, RoPE 1e4",
                    "batch": 2, "seq_len": 8192, "num_heads": 8, "num_kv_heads": 4, "head_dim": 256,
                    "flops_per_step": pair["total_flops"]},
         "roofline": pair["roofline"],
@@ -744,6 +771,7 @@ def main():
         "prologue_ms": pair["prologue_ms"],
         "prologue_gbs": pair["prologue_gbs"],
         "prefill_tflops": {k: round(v, 2) for k, v in pair["prefill_tflops"].items()},
+        "step_forms": pair["step_forms"],
     }
     if not a.no_extra and a.workload == "all":
         log("[bench] gemma3 stack / gemma4 global prefill")
