@@ -9,6 +9,8 @@ checked here:
   * decode: the Gemma-4-12B-shaped step over 64 ragged contexts of up to
     65536 rows (local layer window 1024, global layer D512), one new token,
     four new tokens, and the int8 cache.
+The pair's timed form (keys-only prologue, query rotary in the prefill
+kernel) must equal prologue + prefill bit for bit.
 The oracle recomputes every output: the prologue of the whole q and k
 tensors, then the attention of every query row (prefill) or of every
 sequence (decode).  Outputs and lse are held to the attention tolerance
@@ -104,11 +106,19 @@ def test_prefill_full_size_every_row(gpu, case, workload, layer):
     print(f"[fullsize] {case}: B={B} S={S} D={L['head_dim']} window={W}", flush=True)
     h = bench.layer_inputs(cfg_id, kw, layer, B, S, norm)
     t = bench.layer_tensors(cfg_id, kw, layer, B, S, norm, host=h)
-    bench.run_layer_step(ga, kw, layer, t)                 # the timed launch: prologue, then prefill
+    bench.run_layer_step(ga, kw, layer, t)                 # prologue, then prefill
     out2, lse = ga.attn_prefill(kw, layer, t["qt"], t["kt"], t["v"], want_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), t["out"].view(torch.int16)), "lse request changed the output"
     del out2
+    if workload == "gemma2_pair":
+        # the timed form of this workload: keys-only prologue, query rotary in the prefill kernel
+        _, k_only = ga.qk_prologue(kw, layer, None, t["k"])
+        fused = ga.attn_prefill_qrope(kw, layer, t["q"], k_only, t["v"])
+        torch.cuda.synchronize()
+        assert torch.equal(k_only.view(torch.int16), t["kt"].view(torch.int16)), "keys-only prologue differs"
+        assert torch.equal(fused.view(torch.int16), t["out"].view(torch.int16)), "fused form differs"
+        del k_only, fused
     got_q = from_dev_f64(t["qt"])
     got_k = from_dev_f64(t["kt"])
     got_o = from_dev_f64(t["out"])
