@@ -9,7 +9,7 @@ turns the query with the prologue's own arithmetic.  A keys-only prologue
 must equal the keys of the full prologue bit for bit.
 Cases cover g = 1, 2, 4, 8 and 16, the soft-capped local (four-wave) and
 global (eight-wave) forms and an uncapped one, ragged tails, first positions
-up to 10^5 and rope scaling.
+up to 2^30, a single token and rope scaling.
 """
 import numpy as np
 import pytest
@@ -36,6 +36,9 @@ CASES = [
                            rope_theta=1e4, attn_logit_softcapping=50.0), 0, 1, 257, [3], 1.0),
     ("g16_window_large_pos", dict(num_heads=16, num_kv_heads=1, head_dim=256, sliding_window=64,
                                   sliding_window_pattern=0, rope_theta=1e6), 0, 1, 200, [123456], 1.0),
+    # one token; one block with a ragged tail; positions near 2^30 (the fp64 angle's fraction)
+    ("g2_one_token", GEMMA2, 1, 3, 1, [0, 7, 1 << 20], 1.0),
+    ("g2_one_block_ragged", GEMMA2, 0, 2, 33, [1 << 30, 5], 1.0),
 ]
 
 
