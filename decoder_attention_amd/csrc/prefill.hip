@@ -615,18 +615,22 @@ void prefill_kernel(PrefillParams p) {
       const int32_t cl = 2 * (lgrp & 1) + ((li16 & 3) >> 1);
       const char* vbc = reinterpret_cast<const char*>(vb);
       const uint32_t rest = static_cast<uint32_t>(dlo * 2 + (li16 & 1) * 8);
+      // Rows r0 = 16*t + rb and r0 + 8 of half t, rb = 4*(ln>>5) + (li16>>2).
+      // The swizzle reads only row bits 0-3 and t moves bit 4, so the two
+      // per-lane bases below serve both halves: half t is the immediate
+      // offset t * 16 rows.
+      const int32_t rb = 4 * (ln >> 5) + (li16 >> 2);
+      const uint32_t vb0 = static_cast<uint32_t>(rb * D * 2 + ((cl ^ swz<D>(rb)) << 4)) + rest;
+      const uint32_t vb1 = static_cast<uint32_t>((rb + 8) * D * 2 + ((cl ^ swz<D>(rb + 8)) << 4)) + rest;
       auto vread = [&](int v) -> bf16x8 {
         const int t = v / kDB;
         const int db = v % kDB;
-        const int32_t r0 = 16 * t + 4 * (ln >> 5) + (li16 >> 2);
-        const int32_t r1 = r0 + 8;
-        const uint32_t va0 = static_cast<uint32_t>(r0 * D * 2 + ((cl ^ swz<D>(r0)) << 4)) + rest;
-        const uint32_t va1 = static_cast<uint32_t>(r1 * D * 2 + ((cl ^ swz<D>(r1)) << 4)) + rest;
-        // as for K: bit 8 of va0/va1 is clear from D = 256 up, so db's top bit
-        // is an offset addition (at D = 64, db < 2 never reaches it)
+        // as for K: bit 8 of the bases is clear from D = 256 up, so db's top
+        // bit is an offset addition (at D = 64, db < 2 never reaches it)
         const uint32_t x = static_cast<uint32_t>((db & 3) * 64);
-        const i16x4 a0 = lds_read_tr16(vbc + (va0 ^ x) + (db >> 2) * 256);
-        const i16x4 a1 = lds_read_tr16(vbc + (va1 ^ x) + (db >> 2) * 256);
+        const int32_t imm = t * 16 * D * 2 + (db >> 2) * 256;
+        const i16x4 a0 = lds_read_tr16(vbc + (vb0 ^ x) + imm);
+        const i16x4 a1 = lds_read_tr16(vbc + (vb1 ^ x) + imm);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       constexpr int kV = 2 * kDB;
