@@ -616,21 +616,23 @@ void prefill_kernel(PrefillParams p) {
       const char* vbc = reinterpret_cast<const char*>(vb);
       const uint32_t rest = static_cast<uint32_t>(dlo * 2 + (li16 & 1) * 8);
       // Rows r0 = 16*t + rb and r0 + 8 of half t, rb = 4*(ln>>5) + (li16>>2).
-      // The swizzle reads only row bits 0-3 and t moves bit 4, so the two
-      // per-lane bases below serve both halves: half t is the immediate
-      // offset t * 16 rows.
+      // The swizzle reads only row bits 0-3 and t moves bit 4, so one
+      // per-lane base serves both halves (half t is the immediate offset t *
+      // 16 rows).  Row r0 + 8 differs from r0 in swizzle bit 1 alone (rb's
+      // bits 2-3 are 0 or 1, and 8 adds 2 to them), and the row, chunk and
+      // slice fields of the base do not overlap, so its address is the base
+      // XOR 32 plus the immediate offset 8 rows.
       const int32_t rb = 4 * (ln >> 5) + (li16 >> 2);
       const uint32_t vb0 = static_cast<uint32_t>(rb * D * 2 + ((cl ^ swz<D>(rb)) << 4)) + rest;
-      const uint32_t vb1 = static_cast<uint32_t>((rb + 8) * D * 2 + ((cl ^ swz<D>(rb + 8)) << 4)) + rest;
       auto vread = [&](int v) -> bf16x8 {
         const int t = v / kDB;
         const int db = v % kDB;
-        // as for K: bit 8 of the bases is clear from D = 256 up, so db's top
+        // as for K: bit 8 of the base is clear from D = 256 up, so db's top
         // bit is an offset addition (at D = 64, db < 2 never reaches it)
         const uint32_t x = static_cast<uint32_t>((db & 3) * 64);
         const int32_t imm = t * 16 * D * 2 + (db >> 2) * 256;
         const i16x4 a0 = lds_read_tr16(vbc + (vb0 ^ x) + imm);
-        const i16x4 a1 = lds_read_tr16(vbc + (vb1 ^ x) + imm);
+        const i16x4 a1 = lds_read_tr16(vbc + (vb0 ^ (x ^ 32u)) + imm + 8 * D * 2);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       constexpr int kV = 2 * kDB;
