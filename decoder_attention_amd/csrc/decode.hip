@@ -1329,17 +1329,19 @@ void decode_tile_kernel(DecodeParams p) {
       const int32_t cl = 2 * (lgrp & 1) + ((li16 & 3) >> 1);
       const char* vbc = reinterpret_cast<const char*>(cur);
       const uint32_t rest = static_cast<uint32_t>(dlo * 2 + (li16 & 1) * 8);
+      // One per-lane base for every read (as in the prefill kernel): the
+      // swizzle reads only row bits 0-3, so half t is the immediate offset
+      // t * 16 rows, and row r0 + 8 is the base XOR 32 plus 8 rows.
+      const int32_t rb = 4 * (ln >> 5) + (li16 >> 2);
+      const uint32_t vb0 = static_cast<uint32_t>(rb * kD * 2 + ((cl ^ swz(rb)) << 4)) + rest;
       auto vread = [&](int v) -> bf16x8 {
         const int t = v / kDB;
         const int db = v % kDB;
-        const int32_t r0 = 16 * t + 4 * (ln >> 5) + (li16 >> 2);
-        const int32_t r1 = r0 + 8;
-        const uint32_t va0 = static_cast<uint32_t>(r0 * kD * 2 + ((cl ^ swz(r0)) << 4)) + rest;
-        const uint32_t va1 = static_cast<uint32_t>(r1 * kD * 2 + ((cl ^ swz(r1)) << 4)) + rest;
-        // bit 8 of va0/va1 is clear: db's top bit is an offset addition
+        // bit 8 of the base is clear: db's top bit is an offset addition
         const uint32_t x = static_cast<uint32_t>((db & 3) * 64);
-        const i16x4 a0 = lds_read_tr16(vbc + (va0 ^ x) + (db >> 2) * 256);
-        const i16x4 a1 = lds_read_tr16(vbc + (va1 ^ x) + (db >> 2) * 256);
+        const int32_t imm = t * 16 * kD * 2 + (db >> 2) * 256;
+        const i16x4 a0 = lds_read_tr16(vbc + (vb0 ^ x) + imm);
+        const i16x4 a1 = lds_read_tr16(vbc + (vb0 ^ (x ^ 32u)) + imm + 8 * kD * 2);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       constexpr int kV = 2 * kDB;
