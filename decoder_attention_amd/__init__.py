@@ -17,7 +17,9 @@ import os
 from dataclasses import dataclass
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgemma_attn.so")
+# GEMMA_ATTN_LIBRARY selects another build of the same library by path (the
+# tests use it for the LDS-poisoning debug build, libgemma_attn_ldsnan.so).
+LIB_PATH = os.environ.get("GEMMA_ATTN_LIBRARY") or os.path.join(_HERE, "libgemma_attn.so")
 
 GA_OK, GA_ERR_INVALID_ARG, GA_ERR_UNSUPPORTED, GA_ERR_WORKSPACE, GA_ERR_HIP, GA_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4, 5
 
@@ -126,6 +128,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m decoder_attention_amd.build`")
+    # torch ships its own HIP runtime under the soname the library links
+    # against.  Loaded first, the library would pull in the system runtime and
+    # torch would then load its own beside it: two runtimes in one process,
+    # and the library's launches on torch's streams fail.  With torch loaded
+    # first, the library binds to torch's runtime.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(p)
     i32, cfgp = ctypes.c_int32, ctypes.POINTER(CConfig)
     lib.gemma_attn_resolve_layer.argtypes = [cfgp, i32, ctypes.POINTER(CLayer)]

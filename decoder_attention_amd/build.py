@@ -2,8 +2,13 @@
 
     python -m decoder_attention_amd.build          # compile every source, link
 
-Objects go to decoder_attention_amd/_build/; the shared library is written next
-to this file.  Every call recompiles.
+Two builds of the same sources, both written next to this file:
+  libgemma_attn.so         the library;
+  libgemma_attn_ldsnan.so  the debug build (GA_LDS_POISON=1): every kernel
+                           fills its LDS with NaN bytes before use, so a read
+                           of LDS it never wrote shows in the outputs.
+Objects go to decoder_attention_amd/_build/ (the debug build's to
+_build/ldsnan/).  Every call recompiles.
 """
 from __future__ import annotations
 
@@ -20,6 +25,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgemma_attn.so")
+LIB_LDSNAN = os.path.join(PKG, "libgemma_attn_ldsnan.so")
 
 HIP_SOURCES = ["prologue.hip", "prefill.hip", "decode.hip", "gemma_attn_api.hip"]
 CXX_SOURCES = ["host_logic.cpp"]
@@ -50,19 +56,32 @@ def _run(cmd: list[str]) -> None:
 
 
 def build(jobs: int | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+    """Compile both builds (the library and its LDS-poisoning debug build) and
+    link them; returns the library's path."""
     hipcc = _hipcc()
-    cmds, objs = [], []
+    dbg_dir = os.path.join(BUILD, "ldsnan")
+    os.makedirs(dbg_dir, exist_ok=True)
+    cmds, objs, dbg_objs = [], [], []
     for src in HIP_SOURCES + CXX_SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        stem = os.path.splitext(src)[0]
+        obj = os.path.join(BUILD, stem + ".o")
         objs.append(obj)
         lang = [] if src.endswith(".hip") else ["-x", "c++"]
         cmds.append([hipcc, *_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        if src.endswith(".hip"):
+            dobj = os.path.join(dbg_dir, stem + ".o")
+            dbg_objs.append(dobj)
+            cmds.append([hipcc, *_flags(), "-DGA_LDS_POISON=1", "-c", os.path.join(CSRC, src), "-o", dobj])
+        else:
+            dbg_objs.append(obj)   # host code has no LDS
+    # the longest compiles (decode.hip) first
+    cmds.sort(key=lambda c: "decode.hip" not in " ".join(c))
     with ThreadPoolExecutor(jobs or min(8, os.cpu_count() or 1)) as ex:
         list(ex.map(_run, cmds))
-    tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    for target, parts in ((LIB, objs), (LIB_LDSNAN, dbg_objs)):
+        tmp = target + ".tmp"
+        _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *parts, "-o", tmp])
+        os.replace(tmp, target)
     return LIB
 
 

@@ -88,6 +88,7 @@ __device__ __forceinline__ void seq_range(const DecodeParams& p, int32_t b, int3
 constexpr int kPlanThreads = 256;
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeParams p) {
   __shared__ int64_t wsum[kPlanThreads / 64];
+  lds_poison(wsum);
   const int32_t t = threadIdx.x;
   const int32_t per = (p.batch + kPlanThreads - 1) / kPlanThreads;
   const int32_t b0 = min(p.batch, t * per), b1 = min(p.batch, b0 + per);
@@ -405,6 +406,7 @@ void decode_split_kernel(DecodeParams p) {
   __shared__ float m_w[2][16];
   __shared__ float l_w[2][16];
   static_assert(kTeams == 1 || kSlotElems * kTeams * 2 >= 16 * D * 4, "merge buffer reuses slot 0");
+  lds_poison(ks0, ks1, ks2, ks3, ks4, ks5, vs0, vs1, vs2, vs3, vs4, vs5, m_w, l_w);
 
   const DecodeBlock blk = decode_block(p);
   if (!blk.valid) return;                                        // padding block (uniform)
@@ -713,6 +715,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float l_w[2][16];
   // Partial scores of a two-wave team: [member][half][lane].
   __shared__ f32x4 sx[kTeam > 1 ? 2 * 2 * 64 : 1];
+  lds_poison(ks0, ks1, ks2, ks3, vs0, vs1, vs2, vs3, ksc0, ksc1, ksc2, ksc3, vsc0, vsc1, vsc2, vsc3, m_w, l_w, sx);
 
   const DecodeBlock blk = decode_block(p);
   if (!blk.valid) return;                                        // padding block (uniform)
@@ -1146,6 +1149,7 @@ void decode_tile_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ts0[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t ts1[kTileElems];
   __shared__ __attribute__((aligned(16))) f32x4 sx[4 * 4 * 64];   // [wave][r/4][lane] partial scores
+  lds_poison(ts0, ts1, sx);
 
   const DecodeBlock blk = decode_block(p);
   if (!blk.valid) return;                                        // padding block (uniform)

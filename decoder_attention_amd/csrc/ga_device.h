@@ -111,6 +111,27 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
+// Debug build (compiled with GA_LDS_POISON=1): every LDS array of a kernel
+// starts filled with all-ones bytes, which is a NaN in bf16, fp16, fp32 and
+// fp64, so reading a location the kernel has not written turns an output
+// non-finite.  (For int8 codes the byte 0xFF is the valid code -1; those
+// tiles are covered through their fp32 scales, copied alongside.)  Called
+// by every thread of the workgroup before anything else touches the LDS.
+#ifndef GA_LDS_POISON
+#define GA_LDS_POISON 0
+#endif
+template <typename... A>
+__device__ __forceinline__ void lds_poison(A&... arrs) {
+  if constexpr (GA_LDS_POISON != 0) {
+    auto fill = [](void* base, uint32_t bytes) {
+      uint32_t* w = static_cast<uint32_t*>(base);
+      for (uint32_t i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0xffffffffu;
+    };
+    (fill(static_cast<void*>(&arrs), static_cast<uint32_t>(sizeof(arrs))), ...);
+    __syncthreads();
+  }
+}
+
 // Buffer resource over nbytes from base (raw addressing, 32-bit offsets).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int32_t>(nbytes), 0x00020000);

@@ -242,6 +242,7 @@ void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t v_lds1[KEQV ? 8 : kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds2[(KEQV || kBufs < 3) ? 8 : kTileElems];
   __shared__ __attribute__((aligned(16))) float sx_lds[kSplit > 1 ? kWaves * 64 * 16 : 4];
+  lds_poison(k_lds0, k_lds1, k_lds2, v_lds0, v_lds1, v_lds2, sx_lds);
   auto kslot = [&](auto B) -> uint16_t* {
     if constexpr (decltype(B)::value == 0) return k_lds0;
     else if constexpr (decltype(B)::value == 1) return k_lds1;

@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SHFL ?
   __shared__ int64_t tok_pos[2][kTabTok];      // double-buffered: one item ahead
   __shared__ int32_t tok_b[2][kTabTok];
   __shared__ float rowbuf[SHFL ? 1 : kThreads * 8];
+  lds_poison(omega, cs_tab, wtab, tok_pos, tok_b, rowbuf);
 
   const int32_t tid = threadIdx.x;
   const int32_t half = p.rotary_dim >> 1;

@@ -43,6 +43,31 @@ def test_exports_every_declared_symbol(ga):
         assert hasattr(lib, n), n
 
 
+def test_load_before_torch_keeps_one_hip_runtime(ga):
+    """torch bundles a HIP runtime under the soname the library links against.
+    load() called before anything imported torch must still leave a single
+    runtime in the process (two runtimes make the library's launches on
+    torch's streams fail)."""
+    import sys
+
+    code = ("import decoder_attention_amd as ga; ga.load(); "
+            "print(len(set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l)))")
+    out = subprocess.check_output([sys.executable, "-c", code], cwd=ROOT, text=True)
+    assert out.strip().splitlines()[-1] == "1"
+
+
+def test_lds_poisoning_debug_build_exports_the_same_symbols():
+    """The debug build (every kernel's LDS filled with NaN bytes before use)
+    is the same library: the same entry points, loadable on the CPU."""
+    from decoder_attention_amd import build as b
+
+    if not os.path.exists(b.LIB_LDSNAN):
+        pytest.skip("debug build not built (python -m decoder_attention_amd.build)")
+    lib = ctypes.CDLL(b.LIB_LDSNAN)
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+
+
 def test_struct_layout_matches_c(tmp_path):
     src = tmp_path / "sz.c"
     src.write_text('#include "gemma_attn.h"\n#include <stdio.h>\n#include <stddef.h>\n'
