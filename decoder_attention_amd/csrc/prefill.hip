@@ -476,6 +476,41 @@ void prefill_kernel(PrefillParams p) {
     const bool need = w_lo <= w_hi && kt <= w_hi && kt + kKeys - 1 >= max(r_lo, W > 0 ? w_lo - W + 1 : 0);
     const bool full = kt >= r_lo && kt + kKeys - 1 <= w_lo && (W == 0 || kt >= w_hi - W + 1);
 
+    // V^T operand addressing (used after the softmax; set up here so that the
+    // first operand can be read while the softmax runs).  Lane (lgrp, li16)
+    // reads chunk dlo/8 + 4*db + 2*(lgrp&1) + (li16&3)/2 of rows r0 and
+    // r0 + 8; as for K, the chunk bits are clear of the row, slice and
+    // half-chunk bits, so block db's address is one XOR: base ^ (64 * db).
+    const int32_t ln = lane_id_here();
+    const int32_t lgrp = ln >> 4;
+    const int32_t li16 = ln & 15;
+    const int32_t cl = 2 * (lgrp & 1) + ((li16 & 3) >> 1);
+    const char* vbc = reinterpret_cast<const char*>(vb);
+    const uint32_t rest = static_cast<uint32_t>(dlo * 2 + (li16 & 1) * 8);
+    // Rows r0 = 16*t + rb and r0 + 8 of half t, rb = 4*(ln>>5) + (li16>>2).
+    // The swizzle reads only row bits 0-3 and t moves bit 4, so one
+    // per-lane base serves both halves (half t is the immediate offset t *
+    // 16 rows).  Row r0 + 8 differs from r0 in swizzle bit 1 alone (rb's
+    // bits 2-3 are 0 or 1, and 8 adds 2 to them), and the row, chunk and
+    // slice fields of the base do not overlap, so its address is the base
+    // XOR 32 plus the immediate offset 8 rows.
+    const int32_t rb = 4 * (ln >> 5) + (li16 >> 2);
+    const uint32_t vb0 = static_cast<uint32_t>(rb * D * 2 + ((cl ^ swz<D>(rb)) << 4)) + rest;
+    auto vread = [&](int v) -> bf16x8 {
+      const int t = v / kDB;
+      const int db = v % kDB;
+      // as for K: bit 8 of the base is clear from D = 256 up, so db's top
+      // bit is an offset addition (at D = 64, db < 2 never reaches it)
+      const uint32_t x = static_cast<uint32_t>((db & 3) * 64);
+      const int32_t imm = t * 16 * D * 2 + (db >> 2) * 256;
+      const i16x4 a0 = lds_read_tr16(vbc + (vb0 ^ x) + imm);
+      const i16x4 a1 = lds_read_tr16(vbc + (vb0 ^ (x ^ 32u)) + imm + 8 * D * 2);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int kV = 2 * kDB;
+    constexpr int kLV = 3;
+    bf16x8 va[kLV];
+
     // S^T = K . Q^T (partial over this wave's D slice when split).  Lane
     // (jj, hh) reads chunk dlo/8 + 2*ds + hh of key row jj.  The chunk's bits
     // (ds, hh, swizzle) sit in address bits 4-8, clear of the row and slice
@@ -509,6 +544,11 @@ void prefill_kernel(PrefillParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (kMatPrio > 0) __builtin_amdgcn_s_setprio(0);
+      // The first value operand is read now, so that its LDS latency passes
+      // under the softmax instead of stalling the first PV product
+      // (measured: global layers 0.6-1.9% faster, windows unchanged).
+      va[0] = vread(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (kSplit > 1) {
       // [wave][r/4][lane] float4 layout: consecutive lanes, consecutive 16 bytes.
@@ -604,43 +644,12 @@ void prefill_kernel(PrefillParams p) {
       for (int r = 0; r < 4; ++r) prob_pair(r);   // keys 0-15: the first half's operand
 
       // O^T += V^T . P^T, two 16-key halves per tile (product v: half
-      // v / kDB, 32-row block v % kDB).  Lane (lgrp, li16) reads chunk
-      // dlo/8 + 4*db + 2*(lgrp&1) + (li16&3)/2 of rows r0 and r0 + 8; as for
-      // K, the chunk bits are clear of the row, slice and half-chunk bits, so
-      // block db's address is one XOR: base ^ (64 * db).  The operands of
-      // kLV products are read ahead (fenced), and the second half's
-      // probabilities are computed during the first half's products.
-      const int32_t ln = lane_id_here();
-      const int32_t lgrp = ln >> 4;
-      const int32_t li16 = ln & 15;
-      const int32_t cl = 2 * (lgrp & 1) + ((li16 & 3) >> 1);
-      const char* vbc = reinterpret_cast<const char*>(vb);
-      const uint32_t rest = static_cast<uint32_t>(dlo * 2 + (li16 & 1) * 8);
-      // Rows r0 = 16*t + rb and r0 + 8 of half t, rb = 4*(ln>>5) + (li16>>2).
-      // The swizzle reads only row bits 0-3 and t moves bit 4, so one
-      // per-lane base serves both halves (half t is the immediate offset t *
-      // 16 rows).  Row r0 + 8 differs from r0 in swizzle bit 1 alone (rb's
-      // bits 2-3 are 0 or 1, and 8 adds 2 to them), and the row, chunk and
-      // slice fields of the base do not overlap, so its address is the base
-      // XOR 32 plus the immediate offset 8 rows.
-      const int32_t rb = 4 * (ln >> 5) + (li16 >> 2);
-      const uint32_t vb0 = static_cast<uint32_t>(rb * D * 2 + ((cl ^ swz<D>(rb)) << 4)) + rest;
-      auto vread = [&](int v) -> bf16x8 {
-        const int t = v / kDB;
-        const int db = v % kDB;
-        // as for K: bit 8 of the base is clear from D = 256 up, so db's top
-        // bit is an offset addition (at D = 64, db < 2 never reaches it)
-        const uint32_t x = static_cast<uint32_t>((db & 3) * 64);
-        const int32_t imm = t * 16 * D * 2 + (db >> 2) * 256;
-        const i16x4 a0 = lds_read_tr16(vbc + (vb0 ^ x) + imm);
-        const i16x4 a1 = lds_read_tr16(vbc + (vb0 ^ (x ^ 32u)) + imm + 8 * D * 2);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      constexpr int kV = 2 * kDB;
-      constexpr int kLV = 3;
-      bf16x8 va[kLV];
+      // v / kDB, 32-row block v % kDB).  The operands of kLV products are
+      // read ahead (fenced; the first one before the softmax), and the
+      // second half's probabilities are computed during the first half's
+      // products.
 #pragma unroll
-      for (int v = 0; v < kLV; ++v) va[v] = vread(v);
+      for (int v = 1; v < kLV; ++v) va[v] = vread(v);
       if constexpr (kMatPrio > 0) __builtin_amdgcn_s_setprio(kMatPrio);
 #pragma unroll
       for (int v = 0; v < kV; ++v) {
