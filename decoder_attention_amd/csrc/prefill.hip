@@ -340,15 +340,33 @@ void prefill_kernel(PrefillParams p) {
   const char* vbase = reinterpret_cast<const char*>(KEQV ? p.k : p.v) + static_cast<int64_t>(b) * S * p.hkv * D * 2;
   const uint32_t row_pitch = static_cast<uint32_t>(p.hkv) * D * 2;
   // Per-lane byte offsets of this wave's copy ops inside a tile (rows not
-  // clamped); loop-invariant, so the copies of a full tile cost no VALU.
-  uint32_t doff[kWaveLoads];
+  // clamped).  Where one wave covers all of D (kHold), only op 0's offset is
+  // kept: op i's is (doff[0] ^ dx) + drow with wave-uniform dx and drow (the
+  // swizzle of op i's rows differs from op 0's by a pattern that does not
+  // depend on the lane, and the row term, a multiple of the row pitch, has no
+  // bits in the chunk field), one instruction per op instead of a register
+  // per op; the registers go to the LDS read bases held across the loop
+  // (below).  At D = 512 every op keeps its register and the read bases are
+  // recomputed each tile: holding them there spilled and ran slower.
+  constexpr bool kHold = kSplit == 1;
+  uint32_t doff[kHold ? 1 : kWaveLoads];
 #pragma unroll
-  for (int i = 0; i < kWaveLoads; ++i) {
+  for (int i = 0; i < (kHold ? 1 : kWaveLoads); ++i) {
     const int32_t pc = (wave * kWaveLoads + i) * 64 + lane;
     const int32_t row = pc / kRowChunks;
     const int32_t lc = (pc % kRowChunks) ^ swz<D>(row);       // logical chunk held at pc
     doff[i] = static_cast<uint32_t>(row) * row_pitch + static_cast<uint32_t>(lc) * 16u;
   }
+  auto op_dx = [&](int i) -> uint32_t {
+    const int32_t r0 = (wave * kWaveLoads * 64) / kRowChunks;
+    const int32_t ri = ((wave * kWaveLoads + i) * 64) / kRowChunks;
+    return static_cast<uint32_t>(swz<D>(ri) ^ swz<D>(r0)) << 4;
+  };
+  auto op_drow = [&](int i) -> uint32_t {
+    const int32_t r0 = (wave * kWaveLoads * 64) / kRowChunks;
+    const int32_t ri = ((wave * kWaveLoads + i) * 64) / kRowChunks;
+    return static_cast<uint32_t>(ri - r0) * row_pitch;
+  };
   // A dead tile (live = false) gets a zero-byte resource: its copies read no
   // memory and write zeros into the slot.
   auto issue = [&](int32_t kt, auto B, bool live = true) {
@@ -363,11 +381,17 @@ void prefill_kernel(PrefillParams p) {
     const uint32_t nbytes = live ? kKeys * row_pitch : 0u;
     const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kt_base, nbytes);
     const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vt_base, nbytes);
+    // (the pinned base keeps the compiler from hoisting every op's offset
+    // out of the loop into a register of its own)
+    uint32_t dbase = doff[0];
+    if constexpr (kHold) asm volatile("" : "+v"(dbase));
 #pragma unroll
     for (int i = 0; i < kWaveLoads; ++i) {
       if (kOps % kWaves != 0 && wave * kWaveLoads + i >= kOps) break;   // uniform per wave
       const int32_t base = (wave * kWaveLoads + i) * 64;     // first physical chunk of this op
-      uint32_t off = doff[i];
+      uint32_t off;
+      if constexpr (kHold) off = (dbase ^ op_dx(i)) + op_drow(i);
+      else off = doff[i];
       if (tail) {
         const int32_t ln = lane_id_here();
         const int32_t pc = base + ln;
@@ -461,6 +485,13 @@ void prefill_kernel(PrefillParams p) {
   }
   __syncthreads();
 
+  // Per-lane LDS read bases of the K and V^T operands (the addressing is
+  // described at their reads).  kHold: computed once and held across the
+  // tile loop; at D = 512 they are recomputed from the lane index each tile.
+  const uint32_t kaddr_h = static_cast<uint32_t>((lane & 31) * D * 2 + dlo * 2 + (((lane >> 5) ^ swz<D>(lane & 31)) << 4));
+  const uint32_t vb0_h = static_cast<uint32_t>((4 * (lane >> 5) + ((lane & 15) >> 2)) * D * 2 +
+      (((2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) ^ swz<D>(4 * (lane >> 5) + ((lane & 15) >> 2))) << 4)) +
+      static_cast<uint32_t>(dlo * 2 + (lane & 1) * 8);
   int32_t it = 0;
   // One tile: compute from ring slot B while the copies for slot
   // (B + kAhead) % kBufs are issued.
@@ -495,7 +526,7 @@ void prefill_kernel(PrefillParams p) {
     // slice fields of the base do not overlap, so its address is the base
     // XOR 32 plus the immediate offset 8 rows.
     const int32_t rb = 4 * (ln >> 5) + (li16 >> 2);
-    const uint32_t vb0 = static_cast<uint32_t>(rb * D * 2 + ((cl ^ swz<D>(rb)) << 4)) + rest;
+    const uint32_t vb0 = kHold ? vb0_h : static_cast<uint32_t>(rb * D * 2 + ((cl ^ swz<D>(rb)) << 4)) + rest;
     auto vread = [&](int v) -> bf16x8 {
       const int t = v / kDB;
       const int db = v % kDB;
@@ -520,7 +551,7 @@ void prefill_kernel(PrefillParams p) {
       const int32_t ln = lane_id_here();
       const int32_t jj = ln & 31;
       const int32_t hh = ln >> 5;
-      const uint32_t kaddr = static_cast<uint32_t>(jj * D * 2 + dlo * 2 + ((hh ^ swz<D>(jj)) << 4));
+      const uint32_t kaddr = kHold ? kaddr_h : static_cast<uint32_t>(jj * D * 2 + dlo * 2 + ((hh ^ swz<D>(jj)) << 4));
       const char* kbc = reinterpret_cast<const char*>(kb);
       // kLA operand reads in flight ahead of the matrix instruction that
       // consumes them (fenced, so the order holds): the LDS latency is several
