@@ -434,7 +434,18 @@ void prefill_kernel(PrefillParams p) {
   f32x16 o[kDB];
 #pragma unroll
   for (int db = 0; db < kDB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;
+  // Capped layers at one wave per D first run with a fixed maximum: every
+  // capped logit is below the cap, so cap (log2 units) bounds the row max
+  // and probabilities 2^(logit - cap) need neither a running max nor a
+  // rescale.  A row whose logits all lie far below the cap would push its
+  // probabilities toward the bottom of the fp32/bf16 range; the workgroup
+  // then recomputes with a tracked maximum (below).
+  // The fixed maximum is the cap rounded up to an integer, so that the lse
+  // can be formed exactly from the sum's exponent (at the end).
+  constexpr bool kFixedMax = CAP && kSplit == 1;
+  const float m_fix = kFixedMax ? ceilf(p.cap_log2) : 0.f;
+  float m_run = kFixedMax ? m_fix : -INFINITY;
+  bool tracked = !kFixedMax;   // uniform: the running maximum is in use
   float l_run = 0.f;
 
   if constexpr (!QROPE) wait_vmcnt<0>();   // Q^T and the first tiles
@@ -495,8 +506,9 @@ void prefill_kernel(PrefillParams p) {
   int32_t it = 0;
   // One tile: compute from ring slot B while the copies for slot
   // (B + kAhead) % kBufs are issued.
-  auto step = [&](auto B) {
+  auto step = [&](auto B, auto TRACK) {
     constexpr int kB = decltype(B)::value;
+    constexpr bool kTrack = decltype(TRACK)::value;   // running maximum (else the cap)
     const int32_t kt = tile_key(it);
     if (it + kAhead < n_tiles) issue(tile_key(it + kAhead), std::integral_constant<int, (kB + kAhead) % kBufs>{});
     const uint16_t* kb = kslot(B);
@@ -626,32 +638,35 @@ void prefill_kernel(PrefillParams p) {
           x[r] = ok ? x[r] : (CAP ? INFINITY : -INFINITY);
         }
       }
-      float mx;
-      if (CAP) {
-        float mr = x[0];
+      float m_use = m_fix;
+      if constexpr (kTrack) {
+        float mx;
+        if (CAP) {
+          float mr = x[0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mr = fminf(mr, x[r]);
-        mr = xhalf_min(mr);
-        mx = fmaf(-2.f * p.cap_log2, mr, p.cap_log2);     // -inf when every key is masked
-      } else {
-        mx = x[0];
+          for (int r = 1; r < 16; ++r) mr = fminf(mr, x[r]);
+          mr = xhalf_min(mr);
+          mx = fmaf(-2.f * p.cap_log2, mr, p.cap_log2);     // -inf when every key is masked
+        } else {
+          mx = x[0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-        mx = xhalf_max(mx) * p.scale_log2;
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+          mx = xhalf_max(mx) * p.scale_log2;
+        }
+        // The running max only moves when the tile exceeds it by more than
+        // kTau (log2 units): probabilities then stay <= 2^kTau and the output
+        // rescale, a pass over every accumulator, is rare.
+        const bool grow = mx > m_run + kTau;
+        const float m_next = grow ? mx : m_run;
+        m_use = m_next == -INFINITY ? 0.f : m_next;
+        if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) o[db] *= alpha;
+        }
+        m_run = m_next;
       }
-      // The running max only moves when the tile exceeds it by more than
-      // kTau (log2 units): probabilities then stay <= 2^kTau and the output
-      // rescale, a pass over every accumulator, is rare.
-      const bool grow = mx > m_run + kTau;
-      const float m_next = grow ? mx : m_run;
-      const float m_use = m_next == -INFINITY ? 0.f : m_next;
-      if (__builtin_amdgcn_ballot_w64(grow && m_run != -INFINITY) != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) o[db] *= alpha;
-      }
-      m_run = m_next;
 
       // Probabilities rounded to bf16; the row sum adds the same rounded
       // values (v_dot2_f32_bf16 against (1, 1)), in key order.
@@ -704,14 +719,51 @@ void prefill_kernel(PrefillParams p) {
     lds_barrier();
     ++it;
   };
-  while (it < n_tiles) {
-    step(I0{});
-    if (it >= n_tiles) break;
-    step(I1{});
-    if constexpr (kBufs > 2) {
+  auto run_tiles = [&](auto TRACK) {
+    while (it < n_tiles) {
+      step(I0{}, TRACK);
       if (it >= n_tiles) break;
-      step(I2{});
+      step(I1{}, TRACK);
+      if constexpr (kBufs > 2) {
+        if (it >= n_tiles) break;
+        step(I2{}, TRACK);
+      }
     }
+  };
+  if constexpr (kFixedMax) {
+    run_tiles(std::false_type{});
+    // A kept row always sees its own key, so its sum holds 2^(max logit -
+    // cap) or more; below 2^-100 every logit of the row is within about 28
+    // (log2 units) of -cap, where the terms near the bottom of the fp32 and
+    // bf16 range would lose precision or flush to zero.  Then the whole
+    // workgroup (it shares the K/V tiles) recomputes with a running maximum.
+    // The decision goes through the idle ring: every copy has landed and
+    // every wave has passed the last tile's barrier.
+    const float l_chk = xhalf_sum(l_run);
+    const bool low = kept && !(l_chk >= 0x1p-100f);
+    uint32_t* flag = reinterpret_cast<uint32_t*>(k_lds0);
+    const bool wave_low = __builtin_amdgcn_ballot_w64(low) != 0;
+    if (lane == 0) flag[wave] = wave_low ? 1u : 0u;
+    __syncthreads();
+    uint32_t any_low = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any_low |= flag[w];
+    __syncthreads();   // every wave has read the flags before the ring is written again
+    if (any_low != 0) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) o[db] = f32x16{};
+      l_run = 0.f;
+      m_run = -INFINITY;
+      tracked = true;
+      it = 0;
+      if (0 < n_tiles) issue(tile_key(0), I0{});
+      if (kAhead > 1 && 1 < n_tiles) issue(tile_key(1), I1{});
+      wait_vmcnt<0>();
+      __syncthreads();
+      run_tiles(std::true_type{});
+    }
+  } else {
+    run_tiles(std::true_type{});
   }
 
   const float l_tot = xhalf_sum(l_run);
@@ -775,7 +827,17 @@ void prefill_kernel(PrefillParams p) {
     }
   }
   if (col_valid && p.lse && h == 0 && dlo == 0) {
-    p.lse[(static_cast<int64_t>(b) * p.hq + head) * S + pos] = live ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    // With the fixed (integer) maximum, m + log2(l) is formed as the integer
+    // m + exponent(l) plus log2 of l's mantissa, which keeps the precision a
+    // large offset would cost.
+    float lse2;
+    if (!tracked) {
+      const int32_t e = __builtin_amdgcn_frexp_expf(l_tot);     // l_tot = mant * 2^e, mant in [0.5, 1)
+      lse2 = static_cast<float>(static_cast<int32_t>(m_fix) + e) + __log2f(__builtin_amdgcn_frexp_mantf(l_tot));
+    } else {
+      lse2 = m_run + __log2f(l_tot);
+    }
+    p.lse[(static_cast<int64_t>(b) * p.hq + head) * S + pos] = live ? lse2 * kLn2 : -INFINITY;
   }
 }
 

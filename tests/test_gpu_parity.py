@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import gemma_ref as R
-from synth import BF16_NAN, bf16_bits_to_f64, ctx_lengths, normal_bf16, norm_weight
+from synth import BF16_NAN, bf16_bits_to_f64, ctx_lengths, f32_to_bf16_bits, normal_bf16, norm_weight
 from tests.gpu_util import (assert_close, assert_within_one_ulp, from_dev_bf16_bits, from_dev_f64, to_dev,
                             to_dev_bf16)
 
@@ -222,6 +222,48 @@ def test_prefill_peaked(gpu, kw, layer, scale):
     out = ga.attn_prefill(kw, layer, to_dev_bf16(q), to_dev_bf16(k), None if L["k_eq_v"] else to_dev_bf16(v))
     ro, _ = R.prefill(cfg, layer, bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v))
     assert_close(from_dev_f64(out), ro, what=f"peaked x{scale}")
+
+
+# Soft-capped layers first run with the cap as a fixed softmax maximum (every
+# capped logit lies below it).  A row whose logits all lie far below the cap
+# would put its probabilities near the bottom of the fp32/bf16 range, so the
+# workgroup holding it recomputes with a running maximum.  These rows sit next
+# to ordinary ones, in the same workgroups and in others.
+FAR = [("gemma2_local_4wave", GEMMA2, 0, 2), ("gemma2_global_8wave", GEMMA2, 1, 1), ("tiny_d64", TINY, 0, 1)]
+
+
+@pytest.mark.parametrize("name,kw,layer,B", FAR, ids=[f[0] for f in FAR])
+def test_prefill_capped_rows_far_below_cap(gpu, name, kw, layer, B):
+    ga = gpu
+    cfg = R.GemmaAttnConfig(**kw)
+    L = R.resolve_layer(cfg, layer)
+    D, Hkv, Hq = L["head_dim"], L["num_kv_heads"], cfg.num_heads
+    S = 700
+    # keys close to one direction k0; far rows ask for -c k0, which puts
+    # score * scale / cap near -1.3 (capped logits near -0.86 cap) for every key
+    k0 = bf16_bits_to_f64(normal_bf16(910, (1, D)))[0]
+    noise = bf16_bits_to_f64(normal_bf16(911, (B, S, Hkv, D)))
+    k = R.round_bf16(k0[None, None, None, :] + 0.05 * noise)
+    v = bf16_bits_to_f64(normal_bf16(912, (B, S, Hkv, D)))
+    q = bf16_bits_to_f64(normal_bf16(913, (B, S, Hq, D)))
+    c = 1.3 * kw["attn_logit_softcapping"] / (float(k0 @ k0) * L["scale"])
+    far = np.zeros((B, S), dtype=bool)
+    far[0, 100:164] = True          # a whole query block
+    far[:, 5::37] = True            # scattered rows beside ordinary ones
+    q = np.where(far[:, :, None, None], R.round_bf16(-c * k0)[None, None, None, :], q)
+    print(f"[far] {name} layer={layer} D={D} g={L['group']} far rows {int(far.sum())}", flush=True)
+    ro, rl = R.prefill(cfg, layer, q, k, v)
+    for b in range(B):   # the rows are far below the cap
+        assert np.all(rl[b][:, far[b]] < -0.7 * kw["attn_logit_softcapping"] + np.log(S))
+    out, lse = ga.attn_prefill(kw, layer, to_dev_bf16(_bits(q)), to_dev_bf16(_bits(k)),
+                               None if L["k_eq_v"] else to_dev_bf16(_bits(v)), want_lse=True)
+    assert_close(from_dev_f64(out), ro, what=name)
+    assert_close(from_dev_f64(lse), rl, max_abs=2e-2, mean_abs=2e-3, what=name + " lse")
+
+
+def _bits(x):
+    """bf16 bit patterns of values that are already bf16-exact."""
+    return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
 
 
 # ----------------------------------------------------------------------------- integer facts, bit-exact
