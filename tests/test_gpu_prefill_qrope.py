@@ -9,13 +9,14 @@ turns the query with the prologue's own arithmetic.  A keys-only prologue
 must equal the keys of the full prologue bit for bit.
 Cases cover g = 1, 2, 4, 8 and 16, the soft-capped local (four-wave) and
 global (eight-wave) forms and an uncapped one, ragged tails, first positions
-up to 2^30, a single token and rope scaling.
+up to 2^30, a single token, rope scaling, and rows whose capped logits all lie
+far below the cap (the fixed-maximum pass and its workgroup recompute).
 """
 import numpy as np
 import pytest
 
 from oracle import gemma_ref as R
-from synth import bf16_bits_to_f64, normal_bf16
+from synth import bf16_bits_to_f64, f32_to_bf16_bits, normal_bf16
 from tests.gpu_util import assert_close, from_dev_bf16_bits, from_dev_f64, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -108,3 +109,47 @@ def test_fused_query_rotary_refuses_other_layers(gpu, kw, layer, why):
     with pytest.raises(ga.GemmaAttnError) as e:
         ga.attn_prefill_qrope(kw, layer, q, k, k)
     assert e.value.code == ga.GA_ERR_UNSUPPORTED, why
+
+
+@pytest.mark.parametrize("layer", [0, 1], ids=["local_4wave", "global_8wave"])
+def test_fused_query_rotary_capped_rows_far_below_cap(gpu, layer):
+    """The fused kernels' fixed-maximum pass and its workgroup recompute: rows
+    whose every capped logit lies near -cap sit beside ordinary rows.  Keys
+    and the far rows' queries live on the slowest-turning rotary pairs, so the
+    rotation keeps the far scores near -1.3 cap / scale over the sequence."""
+    ga = gpu
+    import torch
+
+    kw = GEMMA2
+    cfg = R.GemmaAttnConfig(**kw)
+    L = R.resolve_layer(cfg, layer)
+    D, Hkv, Hq = L["head_dim"], L["num_kv_heads"], cfg.num_heads
+    B, S = 1, 700
+    slow = np.zeros(D)
+    slow[D // 2 - 16:D // 2] = 1.0
+    slow[D - 16:] = 1.0
+    k0 = bf16_bits_to_f64(normal_bf16(920, (1, D)))[0] * slow
+    noise = bf16_bits_to_f64(normal_bf16(921, (B, S, Hkv, D)))
+    k = R.round_bf16(k0[None, None, None, :] + 0.02 * noise * slow)
+    v = bf16_bits_to_f64(normal_bf16(922, (B, S, Hkv, D)))
+    q = bf16_bits_to_f64(normal_bf16(923, (B, S, Hq, D)))
+    c = 1.3 * kw["attn_logit_softcapping"] / (float(k0 @ k0) * L["scale"])
+    far = np.zeros((B, S), dtype=bool)
+    far[0, 200:264] = True
+    far[0, 3::41] = True
+    q = np.where(far[:, :, None, None], R.round_bf16(-c * k0)[None, None, None, :], q)
+    bits = lambda x: f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+    qd, kd, vd = to_dev_bf16(bits(q)), to_dev_bf16(bits(k)), to_dev_bf16(bits(v))
+    print(f"[qrope-far] layer={layer} far rows {int(far.sum())}", flush=True)
+    _, k_only = ga.qk_prologue(kw, layer, None, kd)
+    qt, kt = ga.qk_prologue(kw, layer, qd, kd)
+    out_f, lse_f = ga.attn_prefill_qrope(kw, layer, qd, k_only, vd, want_lse=True)
+    out_u, lse_u = ga.attn_prefill(kw, layer, qt, kt, vd, want_lse=True)
+    torch.cuda.synchronize()
+    rq, rk = R.prologue(cfg, layer, q, k)
+    ro, rl = R.prefill(cfg, layer, R.round_bf16(rq), R.round_bf16(rk), v)
+    assert np.all(rl[0][:, far[0]] < -0.7 * kw["attn_logit_softcapping"] + np.log(S))   # the rows are far
+    assert_close(from_dev_f64(out_f), ro, what="fused far out")
+    assert_close(from_dev_f64(lse_f), rl, what="fused far lse")
+    assert np.array_equal(from_dev_bf16_bits(out_f), from_dev_bf16_bits(out_u)), "fused and unfused outputs differ"
+    assert np.array_equal(from_dev_f64(lse_f), from_dev_f64(lse_u)), "fused and unfused lse differ"
