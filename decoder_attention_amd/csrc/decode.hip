@@ -819,7 +819,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int32_t last = s_hi - 1 - k0;
     const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kseq + static_cast<int64_t>(k0) * row_pitch, kTK8 * row_pitch);
     const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vseq + static_cast<int64_t>(k0) * row_pitch, kTK8 * row_pitch);
-    const int32_t ln = lane_here();
+    // The lane index is visible to loop-invariant code motion here (not
+    // lane_here()): the lane-derived copy offsets and LDS addresses are held
+    // across the tile loop, which fits the int8 kernel's registers (keys as
+    // values: 216 VGPRs) and saves their per-tile arithmetic.
+    const int32_t ln = static_cast<int32_t>(threadIdx.x) & 63;
 #pragma unroll
     for (int i = 0; i < kWaveOps; ++i) {
       const int32_t op = member * kWaveOps + i;
@@ -837,7 +841,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   auto compute = [&](int32_t ti, const uint8_t* kb, const uint8_t* vb, const float* kscs, const float* vscs) __attribute__((always_inline)) {
     const int32_t k0 = s_lo + ti * kTK8;
-    const int32_t ln = lane_here();
+    const int32_t ln = static_cast<int32_t>(threadIdx.x) & 63;   // hoistable, as in copy_tile
     const int32_t li16 = ln & 15;
     const int32_t lgrp = ln >> 4;
     // S^T[32 keys x 16 columns] in two 16-key halves (this wave's share of D).
