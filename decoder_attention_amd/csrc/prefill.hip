@@ -442,10 +442,14 @@ void prefill_kernel(PrefillParams p) {
   // then recomputes with a tracked maximum (below).
   // The fixed maximum is the cap rounded up to an integer, so that the lse
   // can be formed exactly from the sum's exponent (at the end).
+  // Caps above 96 log2 units (about 66.5) keep the running maximum from the
+  // start: there an ordinary row's probabilities relative to the cap would
+  // already sit below the recompute threshold (2^-100).
   constexpr bool kFixedMax = CAP && kSplit == 1;
+  const bool fixed = kFixedMax && p.cap_log2 <= 96.f;   // uniform
   const float m_fix = kFixedMax ? ceilf(p.cap_log2) : 0.f;
-  float m_run = kFixedMax ? m_fix : -INFINITY;
-  bool tracked = !kFixedMax;   // uniform: the running maximum is in use
+  float m_run = fixed ? m_fix : -INFINITY;
+  bool tracked = !fixed;   // uniform: the running maximum is in use
   float l_run = 0.f;
 
   if constexpr (!QROPE) wait_vmcnt<0>();   // Q^T and the first tiles
@@ -730,7 +734,9 @@ void prefill_kernel(PrefillParams p) {
       }
     }
   };
-  if constexpr (kFixedMax) {
+  if (!fixed) {
+    run_tiles(std::true_type{});
+  } else if constexpr (kFixedMax) {
     run_tiles(std::false_type{});
     // A kept row always sees its own key, so its sum holds 2^(max logit -
     // cap) or more; below 2^-100 every logit of the row is within about 28
@@ -762,8 +768,6 @@ void prefill_kernel(PrefillParams p) {
       __syncthreads();
       run_tiles(std::true_type{});
     }
-  } else {
-    run_tiles(std::true_type{});
   }
 
   const float l_tot = xhalf_sum(l_run);

@@ -229,7 +229,9 @@ def test_prefill_peaked(gpu, kw, layer, scale):
 # would put its probabilities near the bottom of the fp32/bf16 range, so the
 # workgroup holding it recomputes with a running maximum.  These rows sit next
 # to ordinary ones, in the same workgroups and in others.
-FAR = [("gemma2_local_4wave", GEMMA2, 0, 2), ("gemma2_global_8wave", GEMMA2, 1, 1), ("tiny_d64", TINY, 0, 1)]
+FAR = [("gemma2_local_4wave", GEMMA2, 0, 2), ("gemma2_global_8wave", GEMMA2, 1, 1), ("tiny_d64", TINY, 0, 1),
+       # a cap above 96 log2 units keeps the running maximum from the start
+       ("gemma2_local_cap120", GEMMA2 | dict(attn_logit_softcapping=120.0), 0, 1)]
 
 
 @pytest.mark.parametrize("name,kw,layer,B", FAR, ids=[f[0] for f in FAR])
