@@ -45,9 +45,10 @@
 //   v_permlane32_swap with the other half of the wave.
 //   Scale, tanh soft cap, causal/window mask (boundary tiles only), online
 //   softmax in the exp2 domain with a lazily updated running max (the
-//   accumulators are rescaled only when a row's max grows by more than 2^8);
-//   probabilities rounded to bf16 and the row sum taken over the same
-//   rounded values.
+//   accumulators are rescaled only when a row's max grows by more than 2^8)
+//   -- or, on soft-capped layers, the cap itself as a fixed maximum, with a
+//   recompute for workgroups whose rows lie far below it; probabilities
+//   rounded to bf16 and the row sum taken over the same rounded values.
 //   O^T[D x 32 cols] += V^T . P^T           (same MFMA)
 //     A = V^T read straight from the row-major tile with the transpose read,
 //     B = P^T from the score registers.  With keys-as-values the same LDS
